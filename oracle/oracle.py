@@ -1,0 +1,189 @@
+"""CPU oracle for the fused Indexer-TopK -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import or call anything in this package.  The GPU library never does, and
+this package imports nothing from the GPU library.
+
+What it computes is the plain definition that the LiteTopK method claims to
+reach exactly (LiteTopK pages: arXiv abstract, "preserving exact top-k
+correctness"; summary, "Selection": exact top-k).  No sampling, no bins:
+
+  valid keys   V_t = { s : 0 <= s <= pos[t], s < L }           (causal, inclusive)
+  indexer      I[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[s, :])
+  retrieval    I[t, s] = q[t, :] . x[s, :]                      (no heads, no ReLU)
+  output       the first min(k, |V_t|) keys of V_t ordered by (I descending,
+               index ascending), padded with -1 to length k.
+
+The indexer score is the DSA-style indexer score (the pages call it the
+relevance score of every candidate token, "Problem statement"); the
+retrieval score is the inner product of the pages' vector-retrieval use.
+
+Inputs are the raw storage bits handed to the GPU (fp32 values, bf16 bit
+patterns, OCP e4m3fn bit patterns with fp32 per-token scales) and are decoded
+exactly to fp64; all arithmetic is fp64.  Ties are broken towards the lower
+index by a full lexicographic sort.
+
+Parity status: every function here is pinned by the tests in
+tests/test_oracle.py (brute-force ranks, exhaustive subsets, hand-derived
+golden values, algebraic identities, library special cases).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# exact decoding of the storage formats
+# ---------------------------------------------------------------------------
+
+
+def e4m3fn_table() -> np.ndarray:
+    """fp64 value of each of the 256 OCP FP8 E4M3 ("fn") codes.
+
+    From the OCP 8-bit floating point specification: 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+    (m/8) * 2^-6; S.1111.111 is NaN; there are no infinities, so the largest
+    finite magnitude is 1.75 * 2^8 = 448.
+    """
+    vals = np.empty(256, dtype=np.float64)
+    for b in range(256):
+        sign = -1.0 if b & 0x80 else 1.0
+        e = (b >> 3) & 0xF
+        m = b & 0x7
+        if e == 0xF and m == 0x7:
+            vals[b] = np.nan
+        elif e == 0:
+            vals[b] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            vals[b] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+_E4M3 = e4m3fn_table()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64: a bf16 is the top half of an fp32."""
+    b = np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def decode(raw: np.ndarray, dtype: str, scale: np.ndarray | None = None) -> np.ndarray:
+    """Exact fp64 values of a storage array.
+
+    For fp8, ``scale`` holds one fp32 factor per leading index (per token);
+    the product of an e4m3fn value and an fp32 scale is exact in fp64.
+    """
+    if dtype == "f32":
+        return np.asarray(raw, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return bf16_to_f64(raw)
+    if dtype == "fp8":
+        v = _E4M3[np.asarray(raw, dtype=np.uint8)]
+        if scale is not None:
+            s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+            v = v * s.reshape((-1,) + (1,) * (v.ndim - 1))
+        return v
+    raise ValueError(dtype)
+
+
+# ---------------------------------------------------------------------------
+# scores
+# ---------------------------------------------------------------------------
+
+
+def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Indexer scores of one query against a block of keys, in fp64.
+
+    q: [H, D] decoded query heads; w: [H] head weights; keys: [n, D] decoded
+    keys.  Returns [n] with I[s] = sum_h w[h] * max(0, q[h] . keys[s]).
+    """
+    x = keys @ q.T                      # [n, H]: per-head dot products
+    return np.maximum(x, 0.0) @ w       # ReLU, then the weighted sum over heads
+
+
+def retrieval_scores(q: np.ndarray, db: np.ndarray) -> np.ndarray:
+    """Inner products q . x[s] of one query against a block of rows, in fp64."""
+    return db @ q
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+
+def topk_row(scores: np.ndarray, idx: np.ndarray, k: int):
+    """The k best (score desc, index asc) of one row, padded with -1 / NaN."""
+    order = np.lexsort((idx, -scores))[:k]
+    out_i = np.full(k, -1, dtype=np.int32)
+    out_s = np.full(k, np.nan, dtype=np.float64)
+    out_i[: len(order)] = idx[order]
+    out_s[: len(order)] = scores[order]
+    return out_i, out_s
+
+
+def valid_keys(pos_t: int, L: int) -> np.ndarray:
+    """Causal key set of a query at position pos_t: 0..min(pos_t, L-1)."""
+    hi = min(int(pos_t), L - 1)
+    return np.arange(0, hi + 1, dtype=np.int64) if hi >= 0 else np.zeros(0, dtype=np.int64)
+
+
+def indexer_row_scores(inp: dict, t: int, kd: np.ndarray | None = None):
+    """(valid key indices, fp64 scores) of query t of an indexer input dict."""
+    dt = inp["dtype"]
+    if kd is None:
+        kd = decode(inp["k"], dt, inp.get("k_scale"))
+    qs = inp.get("q_scale")
+    qd = decode(inp["q"][t : t + 1], dt, None if qs is None else qs[t : t + 1])[0]
+    w = np.asarray(inp["w"][t], dtype=np.float32).astype(np.float64)
+    v = valid_keys(inp["pos"][t], inp["L"])
+    return v, indexer_scores(qd, w, kd[: len(v)])   # V_t is the prefix 0..pos[t]
+
+
+def oracle_indexer(inp: dict, rows=None, with_scores: bool = True):
+    """Exact top-k of the indexer input ``inp`` for the query rows ``rows``.
+
+    Returns (idx int32 [R, k], scores fp64 [R, k]); padded entries are -1/NaN.
+    """
+    T, k = inp["T"], inp["topk"]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    kd = decode(inp["k"], inp["dtype"], inp.get("k_scale"))
+    out_i = np.full((len(rows), k), -1, dtype=np.int32)
+    out_s = np.full((len(rows), k), np.nan, dtype=np.float64)
+    for r, t in enumerate(rows):
+        v, s = indexer_row_scores(inp, int(t), kd)
+        out_i[r], out_s[r] = topk_row(s, v, k)
+    return (out_i, out_s) if with_scores else out_i
+
+
+def oracle_retrieval(q_raw: np.ndarray, db_raw: np.ndarray, k: int, rows=None, dtype: str = "bf16",
+                     block: int = 1 << 18):
+    """Exact top-k inner-product retrieval for the query rows ``rows``.
+
+    db_raw is the raw [N, D] storage; it is decoded in blocks of ``block``
+    rows so that an 8M x 768 database never exists in fp64 at once.
+    """
+    T = q_raw.shape[0]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    qd = decode(q_raw[rows], dtype)                      # [R, D]
+    N = db_raw.shape[0]
+    scores = np.empty((len(rows), N), dtype=np.float64)
+    for s0 in range(0, N, block):
+        xd = decode(db_raw[s0 : s0 + block], dtype)      # [n, D]
+        scores[:, s0 : s0 + len(xd)] = (xd @ qd.T).T
+    idx = np.arange(N, dtype=np.int64)
+    out_i = np.full((len(rows), k), -1, dtype=np.int32)
+    out_s = np.full((len(rows), k), np.nan, dtype=np.float64)
+    for r in range(len(rows)):
+        out_i[r], out_s[r] = topk_row(scores[r], idx, k)
+    return out_i, out_s
+
+
+def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t: int, dtype: str = "bf16",
+                         block: int = 1 << 18) -> np.ndarray:
+    """fp64 scores of query t against every database row."""
+    qd = decode(q_raw[t : t + 1], dtype)[0]
+    N = db_raw.shape[0]
+    out = np.empty(N, dtype=np.float64)
+    for s0 in range(0, N, block):
+        out[s0 : s0 + block] = retrieval_scores(qd, decode(db_raw[s0 : s0 + block], dtype))
+    return out

@@ -1,0 +1,265 @@
+"""Pins of the CPU oracle against facts other than itself.
+
+Each ``check_*`` takes the oracle module (so that the mutation tests can hand
+in a copy with a planted mistake) and raises AssertionError on a mismatch.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _row_input(q, w, keys, pos, k):
+    """A one-query fp32 indexer input dict around explicit values."""
+    q = np.asarray(q, np.float32)[None]
+    keys = np.asarray(keys, np.float32)
+    return dict(kind="indexer", T=1, L=len(keys), H=q.shape[1], D=q.shape[2], dtype="f32", topk=k,
+                q=q, k=keys, q_scale=None, k_scale=None, w=np.asarray(w, np.float32)[None],
+                pos=np.array([pos], np.int32))
+
+
+# --------------------------------------------------------------------------- scores
+
+
+def check_hand_example(O):
+    """Hand-derived scores and top-k sets (tests/golden/indexer_hand.json)."""
+    g = _load("indexer_hand.json")
+    q, w, keys = (np.array(g[x], np.float64) for x in ("q", "w", "keys"))
+    s = O.indexer_scores(q, w, keys)
+    assert np.array_equal(s, np.array(g["scores"])), (s, g["scores"])
+    for c in g["cases"]:
+        inp = _row_input(g["q"], g["w"], g["keys"], c["pos"], c["k"])
+        idx, _ = O.oracle_indexer(inp)
+        assert idx[0].tolist() == c["idx"], (c, idx[0].tolist())
+
+
+def check_relu_identities(O, seed=1):
+    """ReLU(x) - ReLU(-x) = x and ReLU(x) + ReLU(-x) = |x|, summed over heads.
+
+    I(q) - I(-q) = (sum_h w_h q_h) . k is a single mat-vec that never applies a
+    ReLU, and I(q) + I(-q) = sum_h w_h |q_h . k|; together they fix I(q).
+    """
+    g = np.random.default_rng(seed)
+    H, D, n = 5, 7, 33
+    q = g.standard_normal((H, D))
+    w = g.uniform(0.1, 1.0, H)
+    keys = g.standard_normal((n, D))
+    a, b = O.indexer_scores(q, w, keys), O.indexer_scores(-q, w, keys)
+    lin = keys @ (w @ q)
+    absum = np.abs(np.einsum("nd,hd->nh", keys, q)) @ w
+    assert np.allclose(a - b, lin, rtol=1e-12, atol=1e-12)
+    assert np.allclose(a + b, absum, rtol=1e-12, atol=1e-12)
+    assert np.all(a >= 0)
+
+
+def check_homogeneity(O, seed=2):
+    """Positive homogeneity in q and k, linearity in w, permutation of heads."""
+    g = np.random.default_rng(seed)
+    H, D, n = 4, 6, 20
+    q, keys = g.standard_normal((H, D)), g.standard_normal((n, D))
+    w1, w2 = g.uniform(0, 1, H), g.uniform(0, 1, H)
+    s = O.indexer_scores(q, w1, keys)
+    assert np.allclose(O.indexer_scores(2.5 * q, w1, keys), 2.5 * s, rtol=1e-12)
+    assert np.allclose(O.indexer_scores(q, w1, 0.25 * keys), 0.25 * s, rtol=1e-12)
+    assert np.allclose(O.indexer_scores(q, w1 + w2, keys), s + O.indexer_scores(q, w2, keys), rtol=1e-12)
+    p = g.permutation(H)
+    assert np.allclose(O.indexer_scores(q[p], w1[p], keys), s, rtol=1e-12)
+
+
+def check_gemm_special_case(O, seed=3):
+    """H = 1, w = 1 and non-negative q, k: the ReLU never fires and I = K q."""
+    g = np.random.default_rng(seed)
+    D, n = 16, 50
+    q = np.abs(g.standard_normal((1, D)))
+    keys = np.abs(g.standard_normal((n, D)))
+    s = O.indexer_scores(q, np.ones(1), keys)
+    assert np.allclose(s, np.matmul(keys, q[0]), rtol=1e-13)
+
+
+def check_fp8_scale_factorisation(O, seed=4):
+    """fp8 with per-token scales: I = sigma_q * sigma_k-weighted unscaled score.
+
+    For one key, scaling that key by sigma_k scales its score by sigma_k (the
+    decode of a scaled e4m3fn tensor must apply the scale per token, not per
+    element or per tensor).
+    """
+    g = np.random.default_rng(seed)
+    T, H, D, L = 3, 4, 8, 12
+    q8 = g.integers(0, 0x7E, size=(T, H, D), dtype=np.uint8) | (g.integers(0, 2, size=(T, H, D), dtype=np.uint8) << 7)
+    k8 = g.integers(0, 0x7E, size=(L, D), dtype=np.uint8) | (g.integers(0, 2, size=(L, D), dtype=np.uint8) << 7)
+    sq = g.uniform(0.5, 2, T).astype(np.float32)
+    sk = g.uniform(0.5, 2, L).astype(np.float32)
+    w = g.uniform(0, 1, (T, H)).astype(np.float32)
+    inp = dict(kind="indexer", T=T, L=L, H=H, D=D, dtype="fp8", topk=4, q=q8, k=k8, q_scale=sq, k_scale=sk,
+               w=w, pos=np.full(T, L - 1, np.int32))
+    tab = O.e4m3fn_table()
+    for t in range(T):
+        _, s = O.indexer_row_scores(inp, t)
+        ref = np.array([float(sq[t]) * float(sk[j]) * O.indexer_scores(tab[q8[t]], w[t].astype(np.float64), tab[k8[j]][None])[0]
+                        for j in range(L)])
+        assert np.allclose(s, ref, rtol=1e-12), (s, ref)
+
+
+# --------------------------------------------------------------------------- decoding
+
+
+def check_e4m3fn_points(O):
+    """Code points fixed by the OCP FP8 E4M3 definition (tests/golden/e4m3fn_points.json)."""
+    tab = O.e4m3fn_table()
+    for code, val in _load("e4m3fn_points.json")["points"].items():
+        c = int(code, 16)
+        if val is None:
+            assert np.isnan(tab[c]), code
+        else:
+            assert tab[c] == float(val) and np.signbit(tab[c]) == (c >= 0x80), (code, tab[c], val)
+
+
+def check_e4m3fn_vs_torch(O):
+    """All 256 codes against torch's float8_e4m3fn -> float32 conversion."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    tab = O.e4m3fn_table()
+    both_nan = np.isnan(ref) & np.isnan(tab)
+    assert np.array_equal(tab[~both_nan], ref[~both_nan]) and np.array_equal(np.isnan(ref), np.isnan(tab))
+
+
+def check_bf16_vs_torch(O, seed=5):
+    import torch
+    g = np.random.default_rng(seed)
+    x = torch.from_numpy((g.standard_normal(1000) * 10 ** g.uniform(-30, 30, 1000)).astype(np.float32))
+    b = x.to(torch.bfloat16)
+    bits = b.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_to_f64(bits), b.to(torch.float32).numpy().astype(np.float64))
+
+
+# --------------------------------------------------------------------------- selection
+
+
+def _brute_rank_select(scores, k):
+    """Key i is selected iff fewer than k keys beat it under (score desc, index asc)."""
+    n = len(scores)
+    sel = []
+    for i in range(n):
+        beats = sum(1 for j in range(n) if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+        if beats < k:
+            sel.append(i)
+    return sel
+
+
+def check_brute_force_ranks(O, seed=6, trials=60):
+    g = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(g.integers(1, 40))
+        k = int(g.integers(1, 45))
+        s = g.integers(-3, 4, n).astype(np.float64)           # many ties on purpose
+        idx, sc = O.topk_row(s, np.arange(n), k)
+        got = sorted(int(i) for i in idx if i >= 0)
+        assert got == _brute_rank_select(s, k), (s, k, got)
+        m = min(k, n)
+        assert np.all(idx[m:] == -1) and np.all(idx[:m] >= 0)
+        # returned in rank order
+        assert list(idx[:m]) == sorted(idx[:m], key=lambda i: (-s[i], i))
+
+
+def check_exhaustive_subsets(O, seed=7, trials=25):
+    """For n <= 10, exactly one k-subset dominates its complement; it is the oracle's."""
+    g = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(g.integers(1, 11))
+        k = int(g.integers(1, n + 1))
+        s = g.integers(0, 3, n).astype(np.float64)
+        winners = []
+        for S in itertools.combinations(range(n), k):
+            out = [j for j in range(n) if j not in S]
+            if all(s[i] > s[j] or (s[i] == s[j] and i < j) for i in S for j in out):
+                winners.append(set(S))
+        assert len(winners) == 1
+        idx, _ = O.topk_row(s, np.arange(n), k)
+        assert set(int(i) for i in idx) == winners[0]
+
+
+def check_selection_special_cases(O, seed=8):
+    g = np.random.default_rng(seed)
+    s = g.integers(0, 5, 100).astype(np.float64)
+    idx, _ = O.topk_row(s, np.arange(100), 1)
+    assert idx[0] == np.argmax(s)                             # argmax returns the first maximum
+    idx, _ = O.topk_row(np.full(50, 7.0), np.arange(50), 10)
+    assert idx.tolist() == list(range(10))                    # all equal -> lowest indices
+    s = g.standard_normal(30)
+    idx, _ = O.topk_row(s, np.arange(30), 40)
+    assert sorted(idx[:30].tolist()) == list(range(30)) and np.all(idx[30:] == -1)
+    s = g.standard_normal(200)                                # no ties: agrees with argpartition
+    idx, _ = O.topk_row(s, np.arange(200), 17)
+    assert set(idx.tolist()) == set(np.argpartition(-s, 17)[:17].tolist())
+
+
+def check_invariant_on_workload(O, inp, rows):
+    """Every selected score >= every unselected one; ties go to the lower index."""
+    for t in rows:
+        v, s = O.indexer_row_scores(inp, int(t))
+        idx, sc = O.topk_row(s, v, inp["topk"])
+        chosen = idx[idx >= 0]
+        mask = np.zeros(len(v), bool)
+        mask[chosen] = True
+        if mask.all() or len(chosen) == 0:
+            continue
+        lo = s[mask].min()
+        hi = s[~mask].max()
+        assert lo >= hi
+        if lo == hi:
+            assert v[mask][s[mask] == lo].max() < v[~mask][s[~mask] == hi].min()
+
+
+def check_causal(O, seed=9):
+    """Keys after the query position never appear; positions clamp to the context."""
+    g = np.random.default_rng(seed)
+    H, D, L = 2, 4, 30
+    q = g.standard_normal((H, D))
+    keys = g.standard_normal((L, D))
+    w = np.ones(H)
+    for pos in (-1, 0, 5, 29, 100):
+        inp = _row_input(q, w, keys, pos, 8)
+        idx, _ = O.oracle_indexer(inp)
+        nvalid = max(0, min(pos, L - 1) + 1)
+        chosen = idx[0][idx[0] >= 0]
+        assert len(chosen) == min(8, nvalid) and np.all(chosen <= min(pos, L - 1))
+
+
+# --------------------------------------------------------------------------- retrieval
+
+
+def check_retrieval_self_match(O, seed=10):
+    """A database holding each query itself returns it first (Cauchy-Schwarz on unit rows)."""
+    g = np.random.default_rng(seed)
+    import torch
+    N, D, T = 300, 24, 6
+    x = g.standard_normal((N, D))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    rows = g.choice(N, T, replace=False)
+    idx, sc = O.oracle_retrieval(bits[rows], bits, 5, block=37)
+    assert idx[:, 0].tolist() == rows.tolist()
+    xd = O.bf16_to_f64(bits)
+    assert np.allclose(sc[:, 0], (xd[rows] ** 2).sum(1), rtol=1e-12)
+    # block size does not change anything
+    idx2, sc2 = O.oracle_retrieval(bits[rows], bits, 5, block=1 << 18)
+    assert np.array_equal(idx, idx2) and np.array_equal(sc, sc2)
+
+
+ALL_CHECKS = [
+    check_hand_example, check_relu_identities, check_homogeneity, check_gemm_special_case,
+    check_fp8_scale_factorisation, check_e4m3fn_points, check_e4m3fn_vs_torch, check_bf16_vs_torch,
+    check_brute_force_ranks, check_exhaustive_subsets, check_selection_special_cases, check_causal,
+    check_retrieval_self_match,
+]

@@ -1,0 +1,137 @@
+"""The CPU oracle against facts other than itself, plus planted-mistake checks."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests import oracle_pins as P
+from workloads import indexer_config, indexer_inputs
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check(O)
+
+
+def test_invariant_config0():
+    inp = indexer_config(0)
+    P.check_invariant_on_workload(O, inp, range(inp["T"]))
+
+
+def test_invariant_small_bf16_fp8():
+    for dt in ("bf16", "fp8"):
+        inp = indexer_inputs(16, 700, 8, 32, dt, 50, 40, drift=True, tag=11)
+        P.check_invariant_on_workload(O, inp, range(16))
+
+
+def test_oracle_rows_subset_consistent():
+    inp = indexer_config(0)
+    full, _ = O.oracle_indexer(inp)
+    rows = [3, 17, 63]
+    part, _ = O.oracle_indexer(inp, rows=rows)
+    assert np.array_equal(full[rows], part)
+
+
+# --------------------------------------------------------------------------- planted mistakes
+
+ORACLE_PY = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.py")
+
+
+def _fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant", ORACLE_PY)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _no_relu(m):
+    m.indexer_scores = lambda q, w, keys: (keys @ q.T) @ w
+
+
+def _ties_high(m):
+    orig = m.topk_row
+
+    def topk_row(scores, idx, k):
+        order = np.lexsort((-np.asarray(idx), -scores))[:k]
+        oi = np.full(k, -1, np.int32)
+        os_ = np.full(k, np.nan)
+        oi[: len(order)] = np.asarray(idx)[order]
+        os_[: len(order)] = scores[order]
+        return oi, os_
+    m.topk_row = topk_row
+    assert orig is not topk_row
+
+
+def _causal_exclusive(m):
+    m.valid_keys = lambda pos_t, L: np.arange(0, max(0, min(int(pos_t), L)), dtype=np.int64)
+
+
+def _fp8_bias8(m):
+    orig = m.e4m3fn_table
+
+    def tab():
+        t = orig()
+        return t / 2.0
+    m.e4m3fn_table = tab
+
+
+def _fp8_scale_per_tensor(m):
+    orig = m.decode
+
+    def decode(raw, dtype, scale=None):
+        if dtype == "fp8" and scale is not None:
+            return orig(raw, dtype, None) * float(np.asarray(scale).reshape(-1)[0])
+        return orig(raw, dtype, scale)
+    m.decode = decode
+
+
+def _weights_reversed(m):
+    m.indexer_scores = lambda q, w, keys: np.maximum(keys @ q.T, 0.0) @ w[::-1]
+
+
+def _bf16_shift15(m):
+    m.bf16_to_f64 = lambda bits: (np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+
+
+def _transposed_keys(m):
+    m.retrieval_scores = lambda q, db: db[:, ::-1] @ q
+    m.oracle_retrieval.__globals__["retrieval_scores"] = m.retrieval_scores
+
+    def oracle_retrieval(q_raw, db_raw, k, rows=None, dtype="bf16", block=1 << 18):
+        T = q_raw.shape[0]
+        rows = np.arange(T) if rows is None else np.asarray(rows)
+        qd = m.decode(q_raw[rows], dtype)
+        xd = m.decode(db_raw, dtype)
+        scores = (xd[:, ::-1] @ qd.T).T
+        idx = np.arange(len(xd))
+        oi = np.full((len(rows), k), -1, np.int32)
+        os_ = np.full((len(rows), k), np.nan)
+        for r in range(len(rows)):
+            oi[r], os_[r] = m.topk_row(scores[r], idx, k)
+        return oi, os_
+    m.oracle_retrieval = oracle_retrieval
+
+
+MUTANTS = {
+    "no_relu": (_no_relu, [P.check_hand_example, P.check_relu_identities]),
+    "ties_to_higher_index": (_ties_high, [P.check_brute_force_ranks, P.check_hand_example,
+                                           P.check_selection_special_cases]),
+    "causal_exclusive": (_causal_exclusive, [P.check_hand_example, P.check_causal]),
+    "fp8_wrong_bias": (_fp8_bias8, [P.check_e4m3fn_points, P.check_e4m3fn_vs_torch]),
+    "fp8_scale_per_tensor": (_fp8_scale_per_tensor, [P.check_fp8_scale_factorisation]),
+    "head_weights_reversed": (_weights_reversed, [P.check_hand_example, P.check_relu_identities]),
+    "bf16_wrong_shift": (_bf16_shift15, [P.check_bf16_vs_torch, P.check_retrieval_self_match]),
+    "retrieval_transposed": (_transposed_keys, [P.check_retrieval_self_match]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    plant, checks = MUTANTS[name]
+    for check in checks:
+        m = _fresh_oracle()
+        plant(m)
+        with pytest.raises(AssertionError):
+            check(m)

@@ -1,0 +1,214 @@
+"""Seeded input generators for the Indexer-TopK workloads.
+
+The workloads stand in for the activations of a DSA-style sparse-attention
+indexer in long-context prefill (LiteTopK pages, "Problem statement" and
+"Experimental results": 1M-token context, 8,192-token chunks, k = 2,048) and
+for a dense vector-retrieval workload (same pages, "Large-scale retrieval":
+k from 1,024 up).  The pages print neither the data nor the generator; the
+recipe below is synthetic and is stated in full in the design notes.
+
+Score concentration, the property the method relies on (pages, "Methodology":
+in high dimension, scores crowd into a narrow band with a long tail), is
+built in: most keys are isotropic Gaussian noise and a minority of "hot" keys
+carry a component along a shared direction that the queries also lean on.
+
+The module holds no scoring, binning or selection arithmetic.  It returns raw
+storage arrays (fp32 values, bf16 bit patterns as uint16, OCP fp8 e4m3fn bit
+patterns as uint8 with fp32 per-token scales), exactly the bits handed to the
+GPU, so that the oracle can decode the very same values.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+SEED_BASE = 20260713
+
+# stream ids inside one workload's SeedSequence
+_S_KEYS, _S_HOT, _S_QUERIES, _S_WEIGHTS, _S_SAMPLE, _S_PREV_QUERIES, _S_DB = 0, 1, 2, 3, 4, 5, 6
+_S_DIR = 7
+
+# The five workloads.  Index 0 is small enough for the oracle to finish in
+# seconds; 1-3 are the indexer prefill chunks at 64K / 256K / 1M context;
+# 4 is the retrieval workload.
+CONFIGS = {
+    0: dict(kind="indexer", name="tiny-4k-fp32", T=64, L=4096, H=4, D=64, dtype="f32",
+            topk=256, n_hot=128, drift=False, w_range=(0.5, 1.0), n_sample=768),
+    1: dict(kind="indexer", name="prefill-64k-bf16", T=2048, L=65536, H=64, D=128, dtype="bf16",
+            topk=2048, n_hot=4096, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    2: dict(kind="indexer", name="prefill-256k-bf16", T=8192, L=262144, H=64, D=128, dtype="bf16",
+            topk=2048, n_hot=16384, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    3: dict(kind="indexer", name="prefill-1m-fp8", T=8192, L=1048576, H=64, D=128, dtype="fp8",
+            topk=2048, n_hot=65536, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    4: dict(kind="retrieval", name="retrieval-8m-d768-bf16", T=1024, N=8_000_000, D=768,
+            dtype="bf16", topk=1024, n_centres=1000, sigma=0.3, n_sample=3072),
+}
+
+FP8_MAX = 448.0  # largest finite OCP e4m3fn value
+
+
+def _rng(tag: int, stream: int, seed: int = SEED_BASE) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, tag, stream]))
+
+
+def _unit(v: np.ndarray, axis: int = -1) -> np.ndarray:
+    return v / np.linalg.norm(v, axis=axis, keepdims=True)
+
+
+def to_storage(x: np.ndarray, dtype: str, axes=None):
+    """Round fp32 values to the storage format ``dtype``.
+
+    Returns ``(raw, scale)``: ``raw`` holds fp32 values, bf16 bit patterns
+    (uint16) or e4m3fn bit patterns (uint8); ``scale`` is None except for fp8,
+    where it is the fp32 per-token scale amax/448 over ``axes`` (so that no
+    value saturates) and ``raw`` encodes ``x / scale``.
+    """
+    import torch
+
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x, None
+    if dtype == "bf16":
+        t = torch.from_numpy(x).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16).copy(), None
+    if dtype == "fp8":
+        amax = np.abs(x).max(axis=axes, keepdims=True).astype(np.float32)
+        scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+        scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+        y = (x / scale).astype(np.float32)
+        t = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
+        raw = t.view(torch.uint8).numpy().copy()
+        return raw, scale.reshape(-1).astype(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _direction(tag: int, D: int, seed: int):
+    """Shared unit direction(s): u0 and an orthogonal u1 for the drifting case."""
+    g = _rng(tag, _S_DIR, seed)
+    u0 = _unit(g.standard_normal(D))
+    v = g.standard_normal(D)
+    v = v - (v @ u0) * u0
+    u1 = _unit(v)
+    return u0, u1
+
+
+def _u_at(p: np.ndarray, L: int, u0: np.ndarray, u1: np.ndarray, drift: bool) -> np.ndarray:
+    """Unit direction at positions p: a quarter turn from u0 to u1 over the context."""
+    if not drift:
+        return np.broadcast_to(u0, (len(p), len(u0)))
+    phi = (math.pi / 2.0) * (np.asarray(p, dtype=np.float64) / float(L))
+    v = np.cos(phi)[:, None] * u0[None, :] + np.sin(phi)[:, None] * u1[None, :]
+    return _unit(v)
+
+
+def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot: int,
+                   drift: bool = False, w_range=(0.0, 1.0), tag: int = 100,
+                   seed: int = SEED_BASE, chunk: int = 0, pos=None, n_sample: int | None = None,
+                   hot_gain: float = 3.0, q_gain: float = 0.5):
+    """Inputs for one indexer chunk.
+
+    Keys: k[s] = N(0, I_D) + hot_gain * u(s) for s in a hot set of n_hot keys
+    drawn without replacement.  Queries: q[t, h] = q_gain * u(pos[t]) +
+    N(0, I_D) / sqrt(D).  Head weights: U(w_range).  Positions: the last T
+    positions of the context for chunk 0, the T before them for chunk -1 (the
+    previous chunk, whose queries come from their own stream), unless ``pos``
+    is given.
+
+    Returns a dict of raw storage arrays and sizes.  ``sample`` holds
+    ``n_sample`` distinct seeded-random causal key indices (a bootstrap sample;
+    the previous-chunk sample is built by the caller from a previous run).
+    """
+    u0, u1 = _direction(tag, D, seed)
+    gk = _rng(tag, _S_KEYS, seed)
+    k = gk.standard_normal((L, D), dtype=np.float32)
+    gh = _rng(tag, _S_HOT, seed)
+    n_hot = min(n_hot, L)
+    hot = np.sort(gh.choice(L, size=n_hot, replace=False)) if n_hot > 0 else np.zeros(0, np.int64)
+    if n_hot:
+        k[hot] += (hot_gain * _u_at(hot, L, u0, u1, drift)).astype(np.float32)
+
+    if pos is None:
+        end = L + chunk * T
+        pos = np.arange(end - T, end, dtype=np.int64)
+    pos = np.asarray(pos, dtype=np.int64)
+    assert pos.shape == (T,)
+    gq = _rng(tag, _S_QUERIES if chunk == 0 else _S_PREV_QUERIES + 16 * (-chunk - 1), seed)
+    q = gq.standard_normal((T, H, D), dtype=np.float32) / np.float32(math.sqrt(D))
+    q += (q_gain * _u_at(np.clip(pos, 0, L - 1), L, u0, u1, drift)).astype(np.float32)[:, None, :]
+    gw = _rng(tag, _S_WEIGHTS + 16 * (-chunk), seed)
+    w = gw.uniform(w_range[0], w_range[1], size=(T, H)).astype(np.float32)
+
+    q_raw, q_scale = to_storage(q, dtype, axes=(1, 2))
+    k_raw, k_scale = to_storage(k, dtype, axes=(1,))
+    out = dict(kind="indexer", T=T, L=L, H=H, D=D, dtype=dtype, topk=topk,
+               q=q_raw, k=k_raw, q_scale=q_scale, k_scale=k_scale, w=w,
+               pos=pos.astype(np.int32), hot=hot.astype(np.int64))
+    if n_sample is not None:
+        out["sample"] = random_sample(n_sample, int(pos.max()) + 1 if T else L, tag, seed, stream=_S_SAMPLE + 16 * (-chunk))
+    return out
+
+
+def random_sample(n: int, upto: int, tag: int = 0, seed: int = SEED_BASE, stream: int = _S_SAMPLE) -> np.ndarray:
+    """n distinct uniform indices in [0, upto), as int32 (fewer if upto < n)."""
+    g = _rng(tag, stream, seed)
+    n = min(n, upto)
+    return np.sort(g.choice(upto, size=n, replace=False)).astype(np.int32)
+
+
+def indexer_config(i: int, chunk: int = 0, seed: int = SEED_BASE):
+    """The seeded inputs of indexer workload ``i`` (0-3); chunk -1 is the previous chunk."""
+    c = CONFIGS[i]
+    assert c["kind"] == "indexer"
+    return indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
+                          drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk,
+                          n_sample=c["n_sample"])
+
+
+def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, sigma: float = 0.3,
+                     n_sample: int = 3072, tag: int = 4, seed: int = SEED_BASE, device: str = "cpu",
+                     block: int = 1 << 20, db_dtype: str = "bf16"):
+    """Gaussian-mixture retrieval workload.
+
+    Centres c_j ~ N(0, I_D); database row i = unit(c_{a_i} + sigma * N(0, I_D))
+    with a_i uniform; query = unit(c_j + sigma * N(0, I_D)) with j uniform.
+    The database is drawn with torch's generator on ``device`` (so that 8M
+    rows of 768 dims can be drawn on the GPU in milliseconds) in blocks of
+    ``block`` rows, then rounded to bf16; queries and the sample come from
+    numpy.  Returns numpy queries (uint16 bf16 bits) and a torch bf16 database
+    tensor on ``device``.
+    """
+    import torch
+
+    gc = _rng(tag, _S_HOT, seed)
+    centres = gc.standard_normal((n_centres, D)).astype(np.float32)
+    gq = _rng(tag, _S_QUERIES, seed)
+    cq = gq.integers(0, n_centres, size=T)
+    q = _unit(centres[cq] + sigma * gq.standard_normal((T, D)).astype(np.float32)).astype(np.float32)
+    q_raw, _ = to_storage(q, db_dtype)
+
+    dev = torch.device(device)
+    seed_db = int(np.random.SeedSequence([seed, tag, _S_DB]).generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed_db)
+    cen = torch.from_numpy(centres).to(dev)
+    tdt = torch.bfloat16 if db_dtype == "bf16" else torch.float32
+    db = torch.empty((N, D), dtype=tdt, device=dev)
+    for s0 in range(0, N, block):
+        n = min(block, N - s0)
+        a = torch.randint(0, n_centres, (n,), generator=g, device=dev)
+        x = cen[a] + sigma * torch.randn((n, D), generator=g, device=dev, dtype=torch.float32)
+        x = x / torch.linalg.vector_norm(x, dim=1, keepdim=True)
+        db[s0:s0 + n] = x.to(tdt)
+        del a, x
+    sample = random_sample(n_sample, N, tag, seed, stream=_S_SAMPLE)
+    return dict(kind="retrieval", T=T, N=N, D=D, dtype=db_dtype, topk=topk, q=q_raw, db=db,
+                sample=sample, centre_of_query=cq)
+
+
+def retrieval_config(i: int = 4, device: str = "cpu", seed: int = SEED_BASE, N: int | None = None,
+                     T: int | None = None):
+    c = CONFIGS[i]
+    assert c["kind"] == "retrieval"
+    return retrieval_inputs(T or c["T"], N or c["N"], c["D"], c["topk"], c["n_centres"], c["sigma"],
+                            c["n_sample"], tag=i, seed=seed, device=device)
