@@ -1,0 +1,154 @@
+/*
+ * litetopk.h -- C ABI of the MI355X (gfx950) fused Indexer-TopK library.
+ *
+ * The operation (LiteTopK pages, "Problem statement" and "Methodology"):
+ * for every query of a prefill chunk, score every causal key and return the
+ * exact top-k key indices, without writing the full score matrix to device
+ * memory.  The method runs in three phases -- Sample, Filter, Select -- and
+ * is exact: the returned set is the plain top-k of the scores (arXiv
+ * abstract: "preserving exact top-k correctness").
+ *
+ * Scores (the pages name "relevance scores for all candidate tokens"; the
+ * indexer form is the DSA-style indexer score):
+ *   indexer    I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:])   s <= pos[t]
+ *   retrieval  I[t,s] = q[t,:] . x[s,:]                              all s
+ * Ties at the k-th score go to the lower key index.
+ *
+ * Conventions for every entry point below:
+ *  - All pointers are DEVICE pointers unless noted; the caller owns every
+ *    buffer, including the workspace.  The library allocates nothing and
+ *    keeps no state between calls except a cached per-device architecture
+ *    check.
+ *  - Arrays are row-major and contiguous.  q/k/db rows must start on a
+ *    16-byte boundary (q, k and db themselves 16-byte aligned).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream), never synchronises the host, and returns an ltk_status.  No
+ *    C++ exception crosses the ABI.  Calls on different streams must use
+ *    different workspaces.
+ *  - Host-side argument errors are reported before anything is enqueued.
+ *    Data conditions are NOT errors: duplicate, out-of-range or non-causal
+ *    sample entries are ignored; an empty sample is allowed; a candidate
+ *    buffer that overflows is recovered exactly on the device; rows with
+ *    fewer than k valid keys are padded with -1 (score NaN).
+ *  - Inputs must be finite (no NaN/Inf in q, k, w, scales).
+ */
+#ifndef LITETOPK_H
+#define LITETOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LTK_OK = 0,
+    LTK_EINVAL = -1,        /* bad argument (null pointer, size, alignment, option) */
+    LTK_EUNSUPPORTED = -2,  /* unsupported (H, D, dtype) or device is not gfx950 */
+    LTK_EWORKSPACE = -3,    /* ws_bytes smaller than litetopk_workspace_bytes() */
+    LTK_EHIP = -4           /* a HIP runtime call or launch failed */
+} ltk_status;
+
+typedef enum {
+    LTK_F32 = 0,            /* fp32 q/k */
+    LTK_BF16 = 1,           /* bf16 q/k (bit patterns, round-to-nearest-even) */
+    LTK_FP8_E4M3FN = 2      /* OCP e4m3fn q/k with fp32 per-token scales */
+} ltk_dtype;
+
+typedef enum {
+    LTK_KIND_SCORE_SELECT = 0,   /* litetopk_score_select */
+    LTK_KIND_RETRIEVE = 1,       /* litetopk_retrieve */
+    LTK_KIND_UNFUSED = 2         /* litetopk_unfused_score_select */
+} ltk_kind;
+
+/* Tuning options (HOST struct).  Pass NULL for the defaults; a zero field
+ * also means "default".  None of them changes the result, only the work. */
+typedef struct {
+    int32_t nbins;          /* equal-width bins over the sample's score range; 1..4096, default 256 */
+    int32_t refresh_every;  /* threshold refresh after every N candidate batches; default 1; <0 = never */
+    int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
+    int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
+    int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072) */
+} ltk_opts;
+
+/* Optional counters (DEVICE struct, written by the call; pass NULL to skip). */
+typedef struct {
+    uint64_t cand_written;        /* candidates appended over all queries (incl. dropped ones) */
+    uint32_t max_cand_per_query;  /* largest per-query candidate count */
+    uint32_t overflow_rows;       /* rows recovered by the exact overflow fallback */
+} ltk_stats;
+
+/* Bytes of workspace a call of `kind` needs.  For LTK_KIND_RETRIEVE, H is
+ * ignored and L is the database size N; for LTK_KIND_UNFUSED, topk, n_sample
+ * and opts are ignored (it holds the full T x L fp32 score matrix).
+ * Returns 0 for invalid sizes. */
+size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, int64_t L,
+                                int32_t topk, int32_t n_sample, int32_t dtype, const ltk_opts* opts);
+
+/* Fused indexer top-k of one prefill chunk (LiteTopK pages, "Methodology":
+ * Sample -> Filter -> Select).
+ *
+ *  q        [T, H, D] queries (dtype); k [L, D] keys (dtype)
+ *  q_scale  [T] fp32 per-query scales (fp8 only; NULL otherwise)
+ *  k_scale  [L] fp32 per-key scales (fp8 only; NULL otherwise)
+ *  w        [T, H] fp32 head weights (>= 0)
+ *  pos      [T] int32 query positions; keys 0..pos[t] (and < L) are valid
+ *  T >= 0, 1 <= H <= 64, D in {64, 128}, 1 <= L < 2^31, 1 <= topk <= 65536
+ *  sample   [n_sample] int32 key indices reused from the previous chunk's
+ *           result (the pages reuse its top-3k); may be NULL if n_sample == 0
+ *  out_idx  [T, topk] int32 result; -1 padded
+ *  out_score[T, topk] fp32 scores of out_idx (NaN where padded), or NULL
+ *  ws       workspace of ws_bytes >= litetopk_workspace_bytes(LTK_KIND_SCORE_SELECT, ...)
+ *  stats    optional device counters, or NULL
+ */
+int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                          const float* w, const int32_t* pos, int32_t T, int32_t H, int32_t D,
+                          int64_t L, int32_t dtype, int32_t topk, const int32_t* sample,
+                          int32_t n_sample, int32_t* out_idx, float* out_score, void* ws,
+                          size_t ws_bytes, const ltk_opts* opts, ltk_stats* stats, void* stream);
+
+/* Fused inner-product retrieval top-k (LiteTopK pages: the same primitive
+ * serves vector retrieval; "Large-scale retrieval", k from 1,024).
+ *
+ *  q [T, D] queries, db [N, D] database rows, both dtype (LTK_BF16 only),
+ *  D a multiple of 64 up to 1024, 1 <= N < 2^31; sample [n_sample] database
+ *  rows used to estimate the score range.  Other arguments as above.
+ */
+int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype,
+                      int32_t topk, const int32_t* sample, int32_t n_sample, int32_t* out_idx,
+                      float* out_score, void* ws, size_t ws_bytes, const ltk_opts* opts,
+                      ltk_stats* stats, void* stream);
+
+/* Unfused comparison path (LiteTopK pages, "Problem statement": the
+ * decoupled pipeline writes the full score matrix to device memory, then
+ * radix-selects each row, reading the matrix several times).  Same
+ * arguments and result as litetopk_score_select without the sample; the
+ * workspace holds the T x L fp32 score matrix. */
+int litetopk_unfused_score_select(const void* q, const float* q_scale, const void* k,
+                                  const float* k_scale, const float* w, const int32_t* pos,
+                                  int32_t T, int32_t H, int32_t D, int64_t L, int32_t dtype,
+                                  int32_t topk, int32_t* out_idx, float* out_score, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* Sample for the next chunk (LiteTopK pages, "Sampling": the previous
+ * chunk's top-3k tokens are reused as the next chunk's sample).  Ranks the
+ * keys 0..L-1 by how many rows of prev_idx [T, topk] (int32, -1 entries
+ * ignored) selected them, ties to the lower index, and writes the first
+ * n_sample of them to out_sample [n_sample] (int32).  The workspace holds
+ * L 32-bit counters: ws_bytes >= 4 * L. */
+int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64_t L, int32_t n_sample,
+                         int32_t* out_sample, void* ws, size_t ws_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* litetopk_strerror(int status);
+
+/* LTK_OK if the current HIP device is a gfx950, LTK_EUNSUPPORTED otherwise,
+ * LTK_EHIP if there is no usable device. */
+int litetopk_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LITETOPK_H */

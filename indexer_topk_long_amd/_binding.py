@@ -1,0 +1,248 @@
+"""ctypes binding of liblitetopk.so (same names as the C ABI, minus the prefix)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+from .build import INCLUDE, lib_path
+
+KIND_SCORE_SELECT, KIND_RETRIEVE, KIND_UNFUSED = 0, 1, 2
+_STATUS = {0: "LTK_OK", -1: "LTK_EINVAL", -2: "LTK_EUNSUPPORTED", -3: "LTK_EWORKSPACE", -4: "LTK_EHIP"}
+
+_c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+
+class _COpts(ctypes.Structure):
+    _fields_ = [("nbins", _c_i32), ("refresh_every", _c_i32), ("l_splits", _c_i32),
+                ("sorted_output", _c_i32), ("cand_capacity", _c_i64)]
+
+
+@dataclass
+class Opts:
+    """Tuning options (none changes the result): see ltk_opts in litetopk.h."""
+    nbins: int = 0
+    refresh_every: int = 0
+    l_splits: int = 0
+    sorted_output: bool = False
+    cand_capacity: int = 0
+
+    def c(self) -> _COpts:
+        return _COpts(self.nbins, self.refresh_every, self.l_splits, int(bool(self.sorted_output)),
+                      self.cand_capacity)
+
+
+@dataclass
+class Stats:
+    cand_written: int
+    max_cand_per_query: int
+    overflow_rows: int
+
+
+class LtkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({strerror(status)})")
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _LIB
+    if _LIB is None:
+        # torch ships its own HIP runtime with the same SONAME as the system one;
+        # importing torch first makes the library bind to that already-loaded copy,
+        # so one process never holds two HIP runtimes.
+        import torch  # noqa: F401
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m indexer_topk_long_amd.build`")
+        lib = ctypes.CDLL(path)
+        lib.litetopk_workspace_bytes.restype = _c_sz
+        lib.litetopk_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_i32, _c_p]
+        lib.litetopk_score_select.restype = ctypes.c_int
+        lib.litetopk_score_select.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i64,
+                                              _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p, _c_p, _c_p]
+        lib.litetopk_unfused_score_select.restype = ctypes.c_int
+        lib.litetopk_unfused_score_select.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                                      _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]
+        lib.litetopk_retrieve.restype = ctypes.c_int
+        lib.litetopk_retrieve.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_p, _c_i32, _c_p,
+                                          _c_p, _c_p, _c_sz, _c_p, _c_p, _c_p]
+        lib.litetopk_strerror.restype = ctypes.c_char_p
+        lib.litetopk_strerror.argtypes = [ctypes.c_int]
+        lib.litetopk_device_check.restype = ctypes.c_int
+        lib.litetopk_device_check.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def exported_symbols() -> list[str]:
+    """Function names declared in include/litetopk.h."""
+    with open(os.path.join(INCLUDE, "litetopk.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(litetopk_\w+)\s*\(", src, flags=re.M)))
+
+
+def strerror(status: int) -> str:
+    return library().litetopk_strerror(int(status)).decode()
+
+
+def device_check() -> int:
+    return int(library().litetopk_device_check())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float8_e4m3fn")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if t is None:
+        return None
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_bytes(kind: int, T: int, H: int, D: int, L: int, topk: int, n_sample: int, dtype_code: int,
+                    opts: Opts | None = None) -> int:
+    o = opts.c() if opts is not None else None
+    return int(library().litetopk_workspace_bytes(kind, T, H, D, L, topk, n_sample, dtype_code,
+                                                  ctypes.byref(o) if o is not None else None))
+
+
+def _workspace(nbytes: int, device, ws=None):
+    import torch
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _stats_buf(device):
+    import torch
+    return torch.zeros(2, dtype=torch.int64, device=device)
+
+
+def _read_stats(buf) -> Stats:
+    v = buf.cpu()
+    return Stats(int(v[0]), int(v[1]) & 0xFFFFFFFF, (int(v[1]) >> 32) & 0xFFFFFFFF)
+
+
+def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=None, opts: Opts | None = None,
+                 return_scores: bool = False, return_stats: bool = False, workspace=None):
+    """Fused indexer top-k (litetopk_score_select).
+
+    q [T, H, D] and k [L, D] in float32 / bfloat16 / float8_e4m3fn (fp8 needs
+    q_scale [T] and k_scale [L] fp32); w [T, H] fp32; pos [T] int32; sample
+    int32 key indices (the previous chunk's top-3k).  Returns int32 [T, topk]
+    (-1 padded), plus fp32 scores and/or Stats when asked.
+    """
+    import torch
+    _dev(q, "q"), _dev(k, "k"), _dev(w, "w", torch.float32), _dev(pos, "pos", torch.int32)
+    _dev(q_scale, "q_scale", torch.float32), _dev(k_scale, "k_scale", torch.float32)
+    if sample is not None:
+        _dev(sample, "sample", torch.int32)
+    if q.dim() != 3 or k.dim() != 2 or q.dtype != k.dtype:
+        raise ValueError("q must be [T, H, D] and k [L, D] of the same dtype")
+    T, H, D = q.shape
+    L = k.shape[0]
+    dt = _dtype_code(q)
+    ns = 0 if sample is None else sample.numel()
+    lib = library()
+    o = opts.c() if opts is not None else None
+    nbytes = lib.litetopk_workspace_bytes(KIND_SCORE_SELECT, T, H, D, L, topk, ns, dt,
+                                          ctypes.byref(o) if o is not None else None)
+    if nbytes == 0:
+        raise LtkError(-1, "litetopk_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    osc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    st = _stats_buf(q.device) if return_stats else None
+    rc = lib.litetopk_score_select(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(pos), T, H, D, L,
+                                   dt, topk, _ptr(sample), ns, _ptr(out), _ptr(osc), _ptr(ws),
+                                   ws.numel() * ws.element_size(), ctypes.byref(o) if o is not None else None,
+                                   _ptr(st), _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_score_select")
+    res = [out]
+    if return_scores:
+        res.append(osc)
+    if return_stats:
+        res.append(_read_stats(st))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def unfused_score_select(q, k, w, pos, topk: int, q_scale=None, k_scale=None, return_scores: bool = False,
+                         workspace=None):
+    """Unfused comparison path (full score matrix + radix select)."""
+    import torch
+    _dev(q, "q"), _dev(k, "k"), _dev(w, "w", torch.float32), _dev(pos, "pos", torch.int32)
+    T, H, D = q.shape
+    L = k.shape[0]
+    dt = _dtype_code(q)
+    lib = library()
+    nbytes = lib.litetopk_workspace_bytes(KIND_UNFUSED, T, H, D, L, topk, 0, dt, None)
+    ws = _workspace(nbytes, q.device, workspace)
+    out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    osc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    rc = lib.litetopk_unfused_score_select(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(pos), T, H,
+                                           D, L, dt, topk, _ptr(out), _ptr(osc), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_unfused_score_select")
+    return (out, osc) if return_scores else out
+
+
+def retrieve(q, db, topk: int, sample=None, opts: Opts | None = None, return_scores: bool = False,
+             return_stats: bool = False, workspace=None):
+    """Fused inner-product retrieval top-k (litetopk_retrieve); q [T, D], db [N, D] bfloat16."""
+    import torch
+    _dev(q, "q"), _dev(db, "db")
+    if sample is not None:
+        _dev(sample, "sample", torch.int32)
+    T, D = q.shape
+    N = db.shape[0]
+    dt = _dtype_code(q)
+    ns = 0 if sample is None else sample.numel()
+    lib = library()
+    o = opts.c() if opts is not None else None
+    nbytes = lib.litetopk_workspace_bytes(KIND_RETRIEVE, T, 1, D, N, topk, ns, dt,
+                                          ctypes.byref(o) if o is not None else None)
+    if nbytes == 0:
+        raise LtkError(-1, "litetopk_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    osc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    st = _stats_buf(q.device) if return_stats else None
+    rc = lib.litetopk_retrieve(_ptr(q), _ptr(db), T, D, N, dt, topk, _ptr(sample), ns, _ptr(out), _ptr(osc),
+                               _ptr(ws), ws.numel() * ws.element_size(),
+                               ctypes.byref(o) if o is not None else None, _ptr(st), _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_retrieve")
+    res = [out]
+    if return_scores:
+        res.append(osc)
+    if return_stats:
+        res.append(_read_stats(st))
+    return res[0] if len(res) == 1 else tuple(res)

@@ -1,0 +1,221 @@
+// api.hip -- the C ABI declared in include/litetopk.h: argument checks,
+// workspace carving and kernel launches on the caller's stream.
+#include <atomic>
+#include <string.h>
+
+#include "internal.hpp"
+
+namespace ltk {
+
+static std::atomic<int> g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
+
+static int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return LTK_EHIP;
+    if (dev >= 0 && dev < 64) {
+        const int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (c != 0) return c > 0 ? LTK_OK : LTK_EUNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LTK_EHIP;
+    const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev >= 0 && dev < 64) g_arch_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? LTK_OK : LTK_EUNSUPPORTED;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Opts {
+    int nbins, refresh_every, l_splits, sorted;
+    int64_t ccap;
+};
+
+static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
+    r.nbins = kDefaultBins;
+    r.refresh_every = 1;
+    r.l_splits = 0;
+    r.sorted = 0;
+    r.ccap = default_ccap;
+    if (!o) return LTK_OK;
+    if (o->nbins < 0 || o->nbins > kMaxBins) return LTK_EINVAL;
+    if (o->nbins) r.nbins = o->nbins;
+    if (o->refresh_every) r.refresh_every = o->refresh_every;   // negative: never
+    if (o->l_splits < 0 || o->l_splits > 4096) return LTK_EINVAL;
+    r.l_splits = o->l_splits;
+    r.sorted = o->sorted_output != 0;
+    if (o->cand_capacity < 0 || o->cand_capacity > (int64_t)1 << 31) return LTK_EINVAL;
+    if (o->cand_capacity) r.ccap = o->cand_capacity;
+    return LTK_OK;
+}
+
+// Head blocks of 32 on the MFMA M dimension.
+static int head_blocks(int H) { return (H + 31) / 32; }
+
+static int check_indexer_sizes(int32_t T, int32_t H, int32_t D, int64_t L, int32_t dtype, int32_t topk) {
+    if (T < 0 || L < 1 || L > (int64_t)0x7fffff00 || topk < 1 || topk > 65536) return LTK_EINVAL;
+    if (dtype < LTK_F32 || dtype > LTK_FP8_E4M3FN) return LTK_EINVAL;
+    if (H < 1 || H > 64 || (D != 64 && D != 128)) return LTK_EUNSUPPORTED;
+    return LTK_OK;
+}
+
+// Key-range splits so that a launch holds at least ~2048 workgroups when the
+// context is long enough (each split keeps >= 4096 keys).
+static int auto_splits(int nqg, int64_t L, int requested) {
+    if (requested > 0) return requested;
+    int s = 1;
+    while ((int64_t)nqg * s < 2048 && L / (s * 2) >= 4096) s *= 2;
+    return s;
+}
+
+}  // namespace ltk
+
+using namespace ltk;
+
+extern "C" {
+
+const char* litetopk_strerror(int status) {
+    switch (status) {
+        case LTK_OK: return "ok";
+        case LTK_EINVAL: return "invalid argument";
+        case LTK_EUNSUPPORTED: return "unsupported shape, dtype or device (gfx950 only)";
+        case LTK_EWORKSPACE: return "workspace too small";
+        case LTK_EHIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int litetopk_device_check(void) { return device_check(); }
+
+size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, int64_t L, int32_t topk,
+                                int32_t n_sample, int32_t dtype, const ltk_opts* opts) {
+    if (kind == LTK_KIND_UNFUSED) {
+        if (T < 0 || L < 1) return 0;
+        return align_up((size_t)T * (size_t)L * 4, 256);
+    }
+    if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
+    (void)H; (void)D; (void)dtype;
+    Opts o;
+    if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? kDefaultCcapRetrieve : kDefaultCcap, o) != LTK_OK) return 0;
+    return ws_layout(T, L, n_sample, o.ccap).total;
+}
+
+int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
+                          const int32_t* pos, int32_t T, int32_t H, int32_t D, int64_t L, int32_t dtype,
+                          int32_t topk, const int32_t* sample, int32_t n_sample, int32_t* out_idx, float* out_score,
+                          void* ws, size_t ws_bytes, const ltk_opts* opts, ltk_stats* stats, void* stream) {
+    int st = check_indexer_sizes(T, H, D, L, dtype, topk);
+    if (st != LTK_OK) return st;
+    if (n_sample < 0 || (n_sample > 0 && !sample)) return LTK_EINVAL;
+    if (T > 0 && (!q || !k || !w || !pos || !out_idx || !ws)) return LTK_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return LTK_EINVAL;
+    const bool fp8 = dtype == LTK_FP8_E4M3FN;
+    if (fp8 && (!q_scale || !k_scale)) return LTK_EINVAL;
+    if (!fp8 && (q_scale || k_scale)) return LTK_EINVAL;
+    Opts o;
+    if ((st = resolve_opts(opts, kDefaultCcap, o)) != LTK_OK) return st;
+    if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
+    const WsLayout lay = ws_layout(T, L, n_sample, o.ccap);
+    if (ws_bytes < lay.total) return LTK_EWORKSPACE;
+    if (T == 0) return LTK_OK;
+    if ((st = device_check()) != LTK_OK) return st;
+
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    IdxArgs a{};
+    a.q = static_cast<const uint8_t*>(q);
+    a.q_scale = q_scale;
+    a.k = static_cast<const uint8_t*>(k);
+    a.k_scale = k_scale;
+    a.w = w;
+    a.pos = pos;
+    a.T = T;
+    a.H = H;
+    a.L = (int)L;
+    a.topk = topk;
+    a.nbins = o.nbins;
+    a.n_sample = n_sample > 0 ? n_sample : 1;
+    const int nqg = (T + kQPG - 1) / kQPG;
+    a.n_splits = auto_splits(nqg, L, o.l_splits);
+    a.s_splits = 1;
+    while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= 8) a.s_splits *= 2;
+    a.refresh_every = o.refresh_every;
+    a.sorted = o.sorted;
+    a.ccap = o.ccap;
+    a.tail = reinterpret_cast<uint32_t*>(wsb + lay.tail);
+    a.flags = reinterpret_cast<uint32_t*>(wsb + lay.flags);
+    a.nu = reinterpret_cast<uint32_t*>(wsb + lay.nu);
+    a.bitmap = reinterpret_cast<uint32_t*>(wsb + lay.bitmap);
+    a.meta = wsb + lay.meta;
+    a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
+    a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
+    a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.stats = stats;
+    a.S = nullptr;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_prepare_sample(a, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;
+    if (launch_indexer_fused(dtype, D, head_blocks(H), a, s) != hipSuccess) return LTK_EHIP;
+    return LTK_OK;
+}
+
+int litetopk_unfused_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                  const float* w, const int32_t* pos, int32_t T, int32_t H, int32_t D, int64_t L,
+                                  int32_t dtype, int32_t topk, int32_t* out_idx, float* out_score, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    int st = check_indexer_sizes(T, H, D, L, dtype, topk);
+    if (st != LTK_OK) return st;
+    if (T > 0 && (!q || !k || !w || !pos || !out_idx || !ws)) return LTK_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return LTK_EINVAL;
+    const bool fp8 = dtype == LTK_FP8_E4M3FN;
+    if (fp8 && (!q_scale || !k_scale)) return LTK_EINVAL;
+    if (!fp8 && (q_scale || k_scale)) return LTK_EINVAL;
+    if (ws_bytes < (size_t)T * (size_t)L * 4) return LTK_EWORKSPACE;
+    if (T == 0) return LTK_OK;
+    if ((st = device_check()) != LTK_OK) return st;
+    IdxArgs a{};
+    a.q = static_cast<const uint8_t*>(q);
+    a.q_scale = q_scale;
+    a.k = static_cast<const uint8_t*>(k);
+    a.k_scale = k_scale;
+    a.w = w;
+    a.pos = pos;
+    a.T = T;
+    a.H = H;
+    a.L = (int)L;
+    a.topk = topk;
+    a.nbins = kDefaultBins;
+    const int nqg = (T + kQPG - 1) / kQPG;
+    a.n_splits = auto_splits(nqg, L, 0);
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.S = static_cast<float*>(ws);
+    if (launch_indexer_unfused(dtype, D, head_blocks(H), a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LTK_EHIP;
+    return LTK_OK;
+}
+
+int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64_t L, int32_t n_sample,
+                         int32_t* out_sample, void* ws, size_t ws_bytes, void* stream) {
+    if (T < 0 || topk < 1 || L < 1 || L > (int64_t)0x7fffff00 || n_sample < 0) return LTK_EINVAL;
+    if (n_sample == 0) return LTK_OK;
+    if ((T > 0 && !prev_idx) || !out_sample || !ws) return LTK_EINVAL;
+    if ((int64_t)n_sample > L) return LTK_EINVAL;
+    if (ws_bytes < (size_t)L * 4) return LTK_EWORKSPACE;
+    int st = device_check();
+    if (st != LTK_OK) return st;
+    if (launch_next_sample(prev_idx, (size_t)T * (size_t)topk, (int)L, n_sample, out_sample,
+                           static_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LTK_EHIP;
+    return LTK_OK;
+}
+
+int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype, int32_t topk,
+                      const int32_t* sample, int32_t n_sample, int32_t* out_idx, float* out_score, void* ws,
+                      size_t ws_bytes, const ltk_opts* opts, ltk_stats* stats, void* stream) {
+    (void)q; (void)db; (void)T; (void)D; (void)N; (void)dtype; (void)topk; (void)sample; (void)n_sample;
+    (void)out_idx; (void)out_score; (void)ws; (void)ws_bytes; (void)opts; (void)stats; (void)stream;
+    return LTK_EUNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// Score contraction on the matrix cores.  Heads sit on the MFMA M dimension
+// and keys on N, so the head reduction of the DSA-style indexer score
+// I[t,s] = sum_h w[t,h] * max(0, q[t,h].k[s]) stays inside each lane (the
+// lane holds 16 heads of one key per 32x32 block), plus one exchange between
+// the two 32-lane halves of the wave.  K (= head dimension) is split so that
+// every lane reads one contiguous half of its row: the lane of half `h`
+// holds elements [h*D/2, (h+1)*D/2) of row (lane & 31), and MFMA step j
+// consumes the j-th EPL-element slice of that half for both operands.  The
+// same slicing for A and B makes the dot product over D exact whatever the
+// instruction's internal order of K, because both operands use it.
+//
+// All score arithmetic is written once here and shared by the sample pass,
+// the fused scan, the overflow fallback and the unfused baseline, so a key
+// gets bit-identical fp32 scores in all of them.  The library is compiled
+// with -ffp-contract=off so that no pass fuses differently.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ltk {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+template <int DT> struct DTraits;
+template <> struct DTraits<DT_F32> { static constexpr int ESZ = 4, EPL = 1; };    // v_mfma_f32_32x32x2_f32
+template <> struct DTraits<DT_BF16> { static constexpr int ESZ = 2, EPL = 8; };   // v_mfma_f32_32x32x16_bf16
+template <> struct DTraits<DT_FP8> { static constexpr int ESZ = 1, EPL = 32; };   // v_mfma_f32_32x32x64_f8f6f4
+
+// One lane's share of a 32-row operand block: its contiguous half row.
+template <int DT, int D>
+struct HalfRow {
+    static constexpr int ESZ = DTraits<DT>::ESZ;
+    static constexpr int BYTES = D / 2 * ESZ;
+    static constexpr int NV = BYTES / 16;
+    static constexpr int KSTEPS = (D / 2) / DTraits<DT>::EPL;
+    static_assert(BYTES % 16 == 0, "half rows are whole 16-byte vectors");
+    u32x4 v[NV];
+};
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+template <int DT, int D>
+__device__ __forceinline__ void load_half_row(HalfRow<DT, D>& f, const uint8_t* row, int half) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row + (size_t)half * HalfRow<DT, D>::BYTES);
+#pragma unroll
+    for (int i = 0; i < HalfRow<DT, D>::NV; ++i) f.v[i] = p[i];
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void zero_half_row(HalfRow<DT, D>& f) {
+#pragma unroll
+    for (int i = 0; i < HalfRow<DT, D>::NV; ++i) f.v[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// acc += A_slice_j x B_slice_j
+template <int DT, int D>
+__device__ __forceinline__ void mfma_step(const HalfRow<DT, D>& a, const HalfRow<DT, D>& b, int j, v16f& acc) {
+    if constexpr (DT == DT_F32) {
+        const float av = __uint_as_float(a.v[j >> 2][j & 3]);
+        const float bv = __uint_as_float(b.v[j >> 2][j & 3]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    } else if constexpr (DT == DT_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v[j]),
+                                                      __builtin_bit_cast(bf16x8, b.v[j]), acc, 0, 0, 0);
+    } else {
+        const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a.v[2 * j], a.v[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b.v[2 * j], b.v[2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+        // format 0 = e4m3 for both operands; zero scales select the unscaled instruction
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+    }
+}
+
+// Two independent slots (query a x key block A, query b x key block B),
+// HB head blocks each; the four MFMA chains are interleaved.
+template <int DT, int D, int HB>
+__device__ __forceinline__ void mfma_2slots(const HalfRow<DT, D> (&qa)[HB], const HalfRow<DT, D>& ka,
+                                            const HalfRow<DT, D> (&qb)[HB], const HalfRow<DT, D>& kb,
+                                            v16f (&acca)[HB], v16f (&accb)[HB]) {
+#pragma unroll
+    for (int m = 0; m < HB; ++m) {
+        acca[m] = v16f{};
+        accb[m] = v16f{};
+    }
+#pragma unroll
+    for (int j = 0; j < HalfRow<DT, D>::KSTEPS; ++j) {
+#pragma unroll
+        for (int m = 0; m < HB; ++m) {
+            mfma_step<DT, D>(qa[m], ka, j, acca[m]);
+            mfma_step<DT, D>(qb[m], kb, j, accb[m]);
+        }
+    }
+}
+
+// Head of accumulator register r of a lane in half `half`, head block m:
+// the 32x32 MFMA result row held by (lane, r) is 8*(r/4) + 4*half + (r%4).
+__device__ __forceinline__ int head_of(int m, int r, int half) { return m * 32 + 8 * (r >> 2) + 4 * half + (r & 3); }
+
+// sum over the lane's heads of w * max(0, x), in a fixed order
+template <int HB>
+__device__ __forceinline__ float relu_wsum(const v16f (&acc)[HB], const float (&w)[HB][16]) {
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < HB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[m][r], __builtin_fmaxf(acc[m][r], 0.0f), p);
+    return p;
+}
+
+// Partial head sums of two slots -> lanes 0-31 get slot a's full sum for key
+// (lane & 31), lanes 32-63 slot b's.  Both halves add (low heads + high heads).
+__device__ __forceinline__ float combine_halves(float pa, float pb) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pa), __float_as_uint(pb), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Affine bin map of the pages ("Filtering"): B = (I - s_min) * delta, clamped
+// into [0, nbins-1] and floored.  Monotone non-decreasing in I.
+__device__ __forceinline__ int bin_of(float I, float smin, float delta, int nbins) {
+    float B = (I - smin) * delta;
+    B = __builtin_fminf(__builtin_fmaxf(B, 0.0f), (float)(nbins - 1));
+    return (int)B;
+}
+
+// Order-preserving map of a finite float to uint32 (-0 is folded onto +0).
+__device__ __forceinline__ uint32_t ord_f32(float f) {
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unord_f32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// 64-bit ranking key: score descending, then index ascending.
+__device__ __forceinline__ uint64_t rank_key(float I, int idx) {
+    return ((uint64_t)ord_f32(I) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ int mbcnt(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+// Top-down accumulation of a histogram (one wave, all 64 lanes): the largest
+// bin b with sum_{b' >= b} h[b'] >= k, and sum_{b' > b} h[b'].  Returns b = -1
+// (above = total) when the total is below k.  Used for the initial threshold
+// bin, the threshold refresh, the final threshold bin and radix digits.
+struct SuffixPick { int bin; uint32_t above; };
+
+__device__ __forceinline__ SuffixPick suffix_pick(const uint32_t* h, int nbins, uint32_t k) {
+    const int lane = lane_id();
+    const int per = (nbins + 63) >> 6;
+    const int lo = lane * per;
+    uint32_t local = 0;
+    for (int i = 0; i < per; ++i)
+        if (lo + i < nbins) local += h[lo + i];
+    // inclusive suffix sum over lanes
+    uint32_t S = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_down(S, off);
+        if (lane + off < 64) S += o;
+    }
+    uint32_t c = S - local;  // entries in bins of higher lanes
+    int best = -1;
+    uint32_t best_above = 0;
+    for (int i = per - 1; i >= 0; --i) {
+        const int b = lo + i;
+        if (b < nbins) {
+            const uint32_t hb = h[b];
+            if (best < 0 && c + hb >= k) {
+                best = b;
+                best_above = c;
+            }
+            c += hb;
+        }
+    }
+    const int bmax = wave_max_i32(best);
+    // bins are split across lanes, so exactly one lane owns bmax
+    uint32_t ab = wave_sum_u32((bmax >= 0 && best == bmax) ? best_above : 0u);
+    if (bmax < 0) ab = __shfl(S, 0);
+    return SuffixPick{bmax, ab};
+}
+
+// Per-query summary of the sample pass.
+struct Meta {
+    float smin;   // lower end of the sample's score range
+    float delta;  // bins per unit score
+    int thr0;     // initial threshold bin
+    int nvalid;   // valid sample keys of this query
+};
+
+}  // namespace ltk

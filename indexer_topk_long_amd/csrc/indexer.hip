@@ -1,0 +1,811 @@
+// indexer.hip -- the fused Indexer-TopK path for gfx950 and its unfused baseline.
+//
+// Phases (LiteTopK pages, "Methodology"):
+//   Sample  : sample_prepare (de-duplicate the reused sample), sample_score
+//             (score it on the matrix cores), sample_stats (score range,
+//             equal-width bins, initial threshold bin = bin of the sample's
+//             k-th largest score)
+//   Filter  : scan_kernel -- MFMA scoring of every causal key, ReLU*w head
+//             reduction, affine bin map, gate against the threshold bin,
+//             wave-local candidate lists written back in batches of 64,
+//             histogram of kept keys and a periodic top-down threshold refresh
+//   Select  : finalize_kernel -- keys in bins above the final threshold bin
+//             go straight out; an exact top-k runs only inside that bin
+//   (overflow) fallback_kernel -- exact re-scoring radix select for rows whose
+//             candidate buffer overflowed (not on the pages; keeps exactness)
+// Unfused baseline (pages, "Problem statement"): unfused_score_kernel writes
+// the full T x L score matrix, unfused_select_kernel radix-selects each row.
+#include <math.h>
+
+#include <algorithm>
+#include <type_traits>
+
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace ltk {
+
+// ---------------------------------------------------------------------------
+// small kernels of the sample pass
+// ---------------------------------------------------------------------------
+
+__global__ void zero_kernel(uint32_t* p, size_t n_words, ltk_stats* stats) {
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (size_t i = i0; i < n_words; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+    if (stats && i0 == 0) {
+        stats->cand_written = 0;
+        stats->max_cand_per_query = 0;
+        stats->overflow_rows = 0;
+    }
+}
+
+// Mark each in-range sample index in a bitmap over the keys (drops duplicates
+// and out-of-range entries).
+__global__ void sample_mark_kernel(const int32_t* sample, int n, int L, uint32_t* bitmap) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const int s = sample[i];
+        if (s >= 0 && s < L) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+    }
+}
+
+// One workgroup of 1024 threads turns the bitmap into the sorted list of
+// distinct sample keys.
+__global__ __launch_bounds__(1024) void sample_compact_kernel(const uint32_t* bitmap, int nwords, int32_t* out,
+                                                              uint32_t* nu) {
+    __shared__ uint32_t wsum[16];
+    __shared__ uint32_t s_base;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+    for (int w0 = 0; w0 < nwords; w0 += 1024) {
+        const int i = w0 + tid;
+        uint32_t word = (i < nwords) ? bitmap[i] : 0u;
+        const uint32_t c = __popc(word);
+        uint32_t incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        uint32_t before = s_base;
+        uint32_t total = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wave) before += wsum[w];
+            total += wsum[w];
+        }
+        uint32_t o = before + incl - c;
+        while (word) {
+            const int b = __ffs(word) - 1;
+            out[o++] = i * 32 + b;
+            word &= word - 1;
+        }
+        __syncthreads();
+        if (tid == 0) s_base += total;
+        __syncthreads();
+    }
+    if (tid == 0) *nu = s_base;
+}
+
+// ---------------------------------------------------------------------------
+// per-wave query state: two queries per wave, one per 32-lane half
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int HB>
+struct QueryRegs {
+    HalfRow<DT, D> q[HB];
+    float w[HB][16];
+};
+
+// Q rows (heads) of query t for this lane and the lane's head weights
+// w'[h] = sigma_q[t] * w[t, h] (zero for padded heads / queries).
+template <int DT, int D, int HB>
+__device__ __forceinline__ void load_query(QueryRegs<DT, D, HB>& r, const IdxArgs& a, int t) {
+    const int lane = lane_id(), half = lane >> 5, row = lane & 31;
+    constexpr int RB = D * DTraits<DT>::ESZ;  // bytes per row
+    const bool tv = t < a.T;
+    const float sq = (DT == DT_FP8 && tv) ? a.q_scale[t] : 1.0f;
+#pragma unroll
+    for (int m = 0; m < HB; ++m) {
+        const int h = m * 32 + row;
+        if (tv && h < a.H)
+            load_half_row<DT, D>(r.q[m], a.q + ((size_t)t * a.H + h) * RB, half);
+        else
+            zero_half_row<DT, D>(r.q[m]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int hh = head_of(m, i, half);
+            r.w[m][i] = (tv && hh < a.H) ? sq * a.w[(size_t)t * a.H + hh] : 0.0f;
+        }
+    }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void load_key(HalfRow<DT, D>& f, const uint8_t* k, int key) {
+    constexpr int RB = D * DTraits<DT>::ESZ;
+    load_half_row<DT, D>(f, k + (size_t)key * RB, lane_id() >> 5);
+}
+
+// Scores of two slots; lane gets slot (lane>>5), key (lane&31) of that slot's block.
+template <int DT, int D, int HB>
+__device__ __forceinline__ float score_2slots(const QueryRegs<DT, D, HB>& qa, const HalfRow<DT, D>& ka,
+                                              const QueryRegs<DT, D, HB>& qb, const HalfRow<DT, D>& kb) {
+    v16f acca[HB], accb[HB];
+    mfma_2slots<DT, D, HB>(qa.q, ka, qb.q, kb, acca, accb);
+    const float pa = relu_wsum<HB>(acca, qa.w);
+    const float pb = relu_wsum<HB>(accb, qb.w);
+    return combine_halves(pa, pb);
+}
+
+// End (exclusive) of the keys any query of the group [t0, t0+8) can see.
+__device__ __forceinline__ int group_key_end(const IdxArgs& a, int t0) {
+    const int lane = lane_id();
+    const int t = t0 + (lane & 7);
+    int e = (t < a.T) ? min(a.pos[t], a.L - 1) + 1 : 0;
+    return wave_max_i32(max(e, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Sample: score the de-duplicated sample keys
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
+    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
+    const int qg = blockIdx.x / a.s_splits, sp = blockIdx.x % a.s_splits;
+    const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
+    const int nu = (int)*a.nu;
+    if (nu == 0) return;
+    const int nblk = (nu + 31) / 32;
+    const int per = (nblk + a.s_splits - 1) / a.s_splits;
+    const int b0 = sp * per, b1 = min(nblk, b0 + per);
+    if (b0 >= b1) return;
+    QueryRegs<DT, D, HB> ra, rb;
+    load_query<DT, D, HB>(ra, a, ta);
+    load_query<DT, D, HB>(rb, a, tb);
+    const int t = half ? tb : ta;
+    for (int blk = b0; blk < b1; ++blk) {
+        const int j = blk * 32 + (lane & 31);
+        const int key = a.sample_u[min(j, nu - 1)];
+        HalfRow<DT, D> kf;
+        load_key<DT, D>(kf, a.k, key);
+        float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+        if constexpr (DT == DT_FP8) I = I * a.k_scale[key];
+        if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
+    }
+}
+
+// Sample statistics of one query: valid sample keys (<= pos), range, delta,
+// histogram and the initial threshold bin.
+__global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];  // [nbins]
+    __shared__ float s_min[4], s_max[4];
+    __shared__ int s_nvalid;
+    const int t = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int nu = (int)*a.nu;
+    const int pos_t = min(a.pos[t], a.L - 1);
+    if (tid == 0) {  // number of sorted sample keys <= pos_t
+        int lo = 0, hi = nu;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (a.sample_u[mid] <= pos_t) lo = mid + 1; else hi = mid;
+        }
+        s_nvalid = lo;
+    }
+    for (int i = tid; i < a.nbins; i += 256) sh[i] = 0u;
+    __syncthreads();
+    const int nv = s_nvalid;
+    const float* S = a.sscore + (size_t)t * a.n_sample;
+    float mn = INFINITY, mx = -INFINITY;
+    for (int j = tid; j < nv; j += 256) {
+        const float v = S[j];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off));
+        mx = fmaxf(mx, __shfl_xor(mx, off));
+    }
+    if (lane == 0) {
+        s_min[wave] = mn;
+        s_max[wave] = mx;
+    }
+    __syncthreads();
+    float smin = fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3]));
+    float smax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    if (nv == 0) {
+        smin = 0.0f;
+        smax = 1.0f;
+    }
+    float width = smax - smin;
+    const float floor_w = 1e-6f * fmaxf(1.0f, fabsf(smax));
+    if (!(width >= floor_w)) width = floor_w;
+    const float delta = (float)a.nbins / width;
+    for (int j = tid; j < nv; j += 256) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
+    __syncthreads();
+    if (wave == 0) {
+        int thr0 = 0;
+        if (nv >= a.topk) thr0 = max(0, suffix_pick(sh, a.nbins, (uint32_t)a.topk).bin);
+        if (lane == 0) {
+            Meta m;
+            m.smin = smin;
+            m.delta = delta;
+            m.thr0 = thr0;
+            m.nvalid = nv;
+            reinterpret_cast<Meta*>(a.meta)[t] = m;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Filter: the fused scan
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(256) void scan_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];
+    const int nbins = a.nbins;
+    uint32_t* hist = sh;                                    // [8][nbins]
+    uint2* stage = reinterpret_cast<uint2*>(sh + kQPG * nbins);   // [8][kStage]
+    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
+    const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
+    const int t0 = qg * kQPG;
+    const int ta = t0 + 2 * wave, tb = ta + 1;
+    const int t = half ? tb : ta;
+    const int qi = 2 * wave + half;                         // this half's local query
+    const uint32_t k = (uint32_t)a.topk;
+
+    for (int i = lane; i < 2 * nbins; i += 64) hist[2 * wave * nbins + i] = 0u;
+
+    const int kend = group_key_end(a, t0);
+    const int per = (((kend + a.n_splits - 1) / a.n_splits) + 31) & ~31;
+    const int k_lo = split * per, k_hi = min(kend, k_lo + per);
+
+    const bool tv = t < a.T;
+    const int my_pos = tv ? min(a.pos[t], a.L - 1) : -1;
+    const int wave_end = min(k_hi, wave_max_i32(my_pos) + 1);   // this wave's last useful key + 1
+    Meta m{0.0f, 1.0f, 0, 0};
+    if (tv) m = reinterpret_cast<const Meta*>(a.meta)[t];
+    int thr = m.thr0;                                           // threshold bin of this half's query
+
+    QueryRegs<DT, D, HB> ra, rb;
+    load_query<DT, D, HB>(ra, a, ta);
+    load_query<DT, D, HB>(rb, a, tb);
+
+    int cnt_a = 0, cnt_b = 0;        // staged entries (wave-uniform)
+    int fl_a = 0, fl_b = 0;          // batches written back (wave-uniform)
+    uint2* st_mine = stage + qi * kStage;
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+    // write back one full batch of query slot s and refresh its threshold
+    auto flush = [&](int s, int& cnt, int& fl) {
+        const int tq = s ? tb : ta;
+        uint2* st = stage + (2 * wave + s) * kStage;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)kFlush);
+        base = __shfl(base, 0);
+        const uint2 e = st[lane];
+        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = e;
+        const int rem = cnt - kFlush;
+        uint2 r{0u, 0u};
+        if (lane < rem) r = st[kFlush + lane];
+        if (lane < rem) st[lane] = r;
+        cnt = rem;
+        ++fl;
+        if (a.refresh_every > 0 && fl % a.refresh_every == 0) {
+            // top-down recount; a plain overwrite that can only raise the threshold
+            const SuffixPick p = suffix_pick(hist + (2 * wave + s) * nbins, nbins, k);
+            if (half == s) thr = max(thr, p.bin);
+        }
+    };
+
+    if (k_lo < wave_end) {
+        HalfRow<DT, D> kf, kn;
+        zero_half_row<DT, D>(kn);
+        load_key<DT, D>(kf, a.k, min(k_lo + (lane & 31), a.L - 1));
+        float sk = 1.0f, skn = 1.0f;
+        if constexpr (DT == DT_FP8) sk = a.k_scale[min(k_lo + (lane & 31), a.L - 1)];
+        for (int kb = k_lo; kb < wave_end; kb += 32) {
+            const int nk = min(kb + 32 + (lane & 31), a.L - 1);
+            if (kb + 32 < wave_end) {
+                load_key<DT, D>(kn, a.k, nk);
+                if constexpr (DT == DT_FP8) skn = a.k_scale[nk];
+            }
+            float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+            if constexpr (DT == DT_FP8) I = I * sk;
+            const int key = kb + (lane & 31);
+            const int b = bin_of(I, m.smin, m.delta, nbins);
+            const bool pass = (key <= my_pos) && (b >= thr);
+            const uint64_t mask = __ballot(pass);
+            if (mask) {
+                const uint32_t ma = (uint32_t)mask, mb = (uint32_t)(mask >> 32);
+                if (pass) {
+                    atomicAdd(&hist[qi * nbins + b], 1u);
+                    const int rank = __popcll(mask & lt_mask & (half ? 0xffffffff00000000ull : 0xffffffffull));
+                    st_mine[(half ? cnt_b : cnt_a) + rank] = make_uint2((uint32_t)key, __float_as_uint(I));
+                }
+                cnt_a += __popc(ma);
+                cnt_b += __popc(mb);
+                if (cnt_a >= kFlush) flush(0, cnt_a, fl_a);
+                if (cnt_b >= kFlush) flush(1, cnt_b, fl_b);
+            }
+            kf = kn;
+            sk = skn;
+        }
+    }
+    // final partial batches
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int cnt = s ? cnt_b : cnt_a;
+        if (cnt > 0) {
+            const int tq = s ? tb : ta;
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)cnt);
+            base = __shfl(base, 0);
+            if (lane < cnt) {
+                const uint2 e = stage[(2 * wave + s) * kStage + lane];
+                if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = e;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Select: finalize
+// ---------------------------------------------------------------------------
+
+// Block-wide bitonic sort (descending) of n <= cap 64-bit keys in LDS.
+__device__ void block_sort_desc(uint64_t* keys, int n) {
+    int p2 = 1;
+    while (p2 < n) p2 <<= 1;
+    for (int i = n + threadIdx.x; i < p2; i += blockDim.x) keys[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= p2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < p2 / 2; i += blockDim.x) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = ((lo & size) == 0);
+                const uint64_t x = keys[lo], y = keys[hi];
+                if ((x < y) == desc) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Order the k outputs of one row by (score desc, index asc).
+__device__ void sort_row_output(int32_t* out, float* osc, int k, uint64_t* keys) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        const int idx = out[i];
+        keys[i] = (idx >= 0) ? rank_key(osc ? osc[i] : 0.0f, idx) : 0ull;
+    }
+    // without scores, order by index only
+    if (!osc)
+        for (int i = threadIdx.x; i < k; i += blockDim.x)
+            keys[i] = (out[i] >= 0) ? (uint64_t)(0xffffffffu - (uint32_t)out[i]) + 1ull : 0ull;
+    __syncthreads();
+    block_sort_desc(keys, k);
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        const uint64_t key = keys[i];
+        if (key == 0ull) {
+            out[i] = -1;
+            if (osc) osc[i] = __builtin_nanf("");
+        } else if (osc) {
+            out[i] = (int32_t)(0xffffffffu - (uint32_t)key);
+            osc[i] = unord_f32((uint32_t)(key >> 32));
+        } else {
+            out[i] = (int32_t)(0xffffffffu - (uint32_t)(key - 1ull));
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];   // [max(nbins, 256)] then (sorted) keys
+    __shared__ int s_pick;
+    __shared__ uint32_t s_above, s_cnt, s_ocnt;
+    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+    const int k = a.topk;
+    const uint32_t n = a.tail[t];
+    int32_t* out = a.out_idx + (size_t)t * k;
+    float* osc = a.out_score ? a.out_score + (size_t)t * k : nullptr;
+    uint64_t* sort_keys = reinterpret_cast<uint64_t*>(sh + ((max(a.nbins, 256) + 1) & ~1));
+    if (tid == 0 && a.stats) {
+        atomicAdd((unsigned long long*)&a.stats->cand_written, (unsigned long long)n);
+        atomicMax(&a.stats->max_cand_per_query, n);
+    }
+    if ((int64_t)n > a.ccap) {   // the buffer overflowed: the fallback recomputes this row
+        if (tid == 0) {
+            a.flags[t] = 1u;
+            if (a.stats) atomicAdd(&a.stats->overflow_rows, 1u);
+        }
+        return;
+    }
+    const uint2* c = a.cand + (size_t)t * a.ccap;
+    if (n <= (uint32_t)k) {      // only when the row has at most k valid keys: keep them all
+        for (uint32_t i = tid; i < n; i += 256) {
+            out[i] = (int32_t)c[i].x;
+            if (osc) osc[i] = __uint_as_float(c[i].y);
+        }
+        for (int i = (int)n + tid; i < k; i += 256) {
+            out[i] = -1;
+            if (osc) osc[i] = __builtin_nanf("");
+        }
+        if (a.sorted) sort_row_output(out, osc, k, sort_keys);
+        return;
+    }
+    const Meta m = reinterpret_cast<const Meta*>(a.meta)[t];
+    const int nbins = a.nbins;
+    uint32_t* hist = sh;
+    for (int i = tid; i < nbins; i += 256) hist[i] = 0u;
+    if (tid == 0) s_ocnt = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += 256) atomicAdd(&hist[bin_of(__uint_as_float(c[i].y), m.smin, m.delta, nbins)], 1u);
+    __syncthreads();
+    if (wave == 0) {   // final threshold bin: top-down recount of the candidates' bins
+        const SuffixPick p = suffix_pick(hist, nbins, (uint32_t)k);
+        if (lane == 0) {
+            s_pick = p.bin;
+            s_above = p.above;
+        }
+    }
+    __syncthreads();
+    const int bstar = s_pick;
+    const uint32_t above = s_above;
+    // bins strictly above the final threshold bin go straight to the output
+    for (uint32_t i = tid; i < n; i += 256) {
+        const uint2 e = c[i];
+        const float I = __uint_as_float(e.y);
+        if (bin_of(I, m.smin, m.delta, nbins) > bstar) {
+            const uint32_t p = atomicAdd(&s_ocnt, 1u);
+            if (p < (uint32_t)k) {
+                out[p] = (int32_t)e.x;
+                if (osc) osc[p] = I;
+            }
+        }
+    }
+    // exact top-(k - above) inside the threshold bin: radix select on (score desc, index asc)
+    uint64_t P = 0ull, mask = 0ull;
+    uint32_t need = (uint32_t)k - above;
+    uint32_t* h256 = sh;   // reuses the histogram space (nbins is no longer needed)
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        __syncthreads();
+        for (int i = tid; i < 256; i += 256) h256[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < n; i += 256) {
+            const uint2 e = c[i];
+            const float I = __uint_as_float(e.y);
+            if (bin_of(I, m.smin, m.delta, nbins) == bstar) {
+                const uint64_t key = rank_key(I, (int)e.x);
+                if ((key & mask) == P) atomicAdd(&h256[(uint32_t)(key >> shift) & 255u], 1u);
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const SuffixPick p = suffix_pick(h256, 256, need);
+            if (lane == 0) {
+                s_pick = p.bin;
+                s_above = p.above;
+                s_cnt = h256[p.bin];
+            }
+        }
+        __syncthreads();
+        const uint32_t d = (uint32_t)s_pick;
+        P |= (uint64_t)d << shift;
+        mask |= 0xffull << shift;
+        need -= s_above;
+        if (s_cnt == need) break;   // every entry with this prefix is taken
+    }
+    for (uint32_t i = tid; i < n; i += 256) {
+        const uint2 e = c[i];
+        const float I = __uint_as_float(e.y);
+        if (bin_of(I, m.smin, m.delta, nbins) == bstar && (rank_key(I, (int)e.x) & mask) >= P) {
+            const uint32_t p = atomicAdd(&s_ocnt, 1u);
+            if (p < (uint32_t)k) {
+                out[p] = (int32_t)e.x;
+                if (osc) osc[p] = I;
+            }
+        }
+    }
+    if (a.sorted) sort_row_output(out, osc, k, sort_keys);
+}
+
+// ---------------------------------------------------------------------------
+// Exact row select by 8-bit radix digits over a stream of (key, score)
+// (overflow fallback and unfused baseline)
+// ---------------------------------------------------------------------------
+
+// Scores re-read from the materialised row (unfused baseline).
+struct MemSource {
+    const float* row;
+    __device__ __forceinline__ void get(int base, int nvalid, int& key, float& I, bool& valid) {
+        key = base + (int)threadIdx.x;
+        valid = key < nvalid;
+        I = valid ? row[key] : 0.0f;
+    }
+};
+
+// Scores recomputed on the matrix cores (overflow fallback): wave w covers
+// keys [base + 64w, base + 64w + 64) as two 32-key slots of the same query.
+template <int DT, int D, int HB>
+struct RescoreSource {
+    QueryRegs<DT, D, HB> r;
+    const uint8_t* k;
+    const float* ks;
+    int L;
+    __device__ __forceinline__ void get(int base, int nvalid, int& key, float& I, bool& valid) {
+        const int wave = threadIdx.x >> 6, lane = lane_id();
+        const int kb0 = base + 64 * wave;
+        HalfRow<DT, D> ka, kbf;
+        load_key<DT, D>(ka, k, min(kb0 + (lane & 31), L - 1));
+        load_key<DT, D>(kbf, k, min(kb0 + 32 + (lane & 31), L - 1));
+        I = score_2slots<DT, D, HB>(r, ka, r, kbf);
+        key = kb0 + lane;
+        if constexpr (DT == DT_FP8) I = I * ks[min(key, L - 1)];
+        valid = key < nvalid;
+    }
+};
+
+template <class Src>
+__device__ void select_row(Src& src, int nvalid, int k, int32_t* out, float* osc, uint32_t* h256) {
+    __shared__ int s_pick;
+    __shared__ uint32_t s_above, s_ocnt, s_taken, s_wc[4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+    if (nvalid <= k) {   // every valid key is in the result
+        for (int base = 0; base < nvalid; base += 256) {
+            int key;
+            float I;
+            bool valid;
+            src.get(base, nvalid, key, I, valid);
+            if (valid) {
+                out[key] = key;
+                if (osc) osc[key] = I;
+            }
+        }
+        for (int i = max(nvalid, 0) + tid; i < k; i += 256) {
+            out[i] = -1;
+            if (osc) osc[i] = __builtin_nanf("");
+        }
+        return;
+    }
+    uint32_t P = 0u, mask = 0u, need = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        __syncthreads();
+        for (int i = tid; i < 256; i += 256) h256[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < nvalid; base += 256) {
+            int key;
+            float I;
+            bool valid;
+            src.get(base, nvalid, key, I, valid);
+            const uint32_t u = ord_f32(I);
+            if (valid && (u & mask) == P) atomicAdd(&h256[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const SuffixPick p = suffix_pick(h256, 256, need);
+            if (lane == 0) {
+                s_pick = p.bin;
+                s_above = p.above;
+            }
+        }
+        __syncthreads();
+        P |= (uint32_t)s_pick << shift;
+        mask |= 0xffu << shift;
+        need -= s_above;
+    }
+    // P is now the k-th largest score; `need` of its ties are taken, lowest index first
+    const uint32_t ngt = (uint32_t)k - need;
+    if (tid == 0) {
+        s_ocnt = 0u;
+        s_taken = 0u;
+    }
+    __syncthreads();
+    for (int base = 0; base < nvalid; base += 256) {
+        int key;
+        float I;
+        bool valid;
+        src.get(base, nvalid, key, I, valid);
+        const uint32_t u = ord_f32(I);
+        const bool gt = valid && u > P;
+        const bool eq = valid && u == P;
+        if (gt) {
+            const uint32_t p = atomicAdd(&s_ocnt, 1u);
+            if (p < ngt) {
+                out[p] = key;
+                if (osc) osc[p] = I;
+            }
+        }
+        const uint64_t em = __ballot(eq);
+        if (lane == 0) s_wc[wave] = (uint32_t)__popcll(em);
+        __syncthreads();
+        uint32_t before = s_taken, total = 0;
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) before += s_wc[w];
+            total += s_wc[w];
+        }
+        if (eq) {
+            const uint32_t rank = before + (uint32_t)mbcnt(em);
+            if (rank < need) {
+                out[ngt + rank] = key;
+                if (osc) osc[ngt + rank] = I;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) s_taken += total;
+    }
+}
+
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(256) void fallback_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];
+    const int t = blockIdx.x;
+    if (a.flags[t] == 0u) return;
+    RescoreSource<DT, D, HB> src;
+    load_query<DT, D, HB>(src.r, a, t);
+    src.k = a.k;
+    src.ks = a.k_scale;
+    src.L = a.L;
+    const int nvalid = max(min(a.pos[t], a.L - 1) + 1, 0);
+    int32_t* out = a.out_idx + (size_t)t * a.topk;
+    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk : nullptr;
+    select_row(src, nvalid, a.topk, out, osc, sh);
+    if (a.sorted) sort_row_output(out, osc, a.topk, reinterpret_cast<uint64_t*>(sh + 256));
+}
+
+// ---------------------------------------------------------------------------
+// Unfused baseline
+// ---------------------------------------------------------------------------
+
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(256) void unfused_score_kernel(IdxArgs a) {
+    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
+    const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
+    const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
+    const int t = half ? tb : ta;
+    const int per = (((a.L + a.n_splits - 1) / a.n_splits) + 31) & ~31;
+    const int k_lo = split * per, k_hi = min(a.L, k_lo + per);
+    QueryRegs<DT, D, HB> ra, rb;
+    load_query<DT, D, HB>(ra, a, ta);
+    load_query<DT, D, HB>(rb, a, tb);
+    const int my_pos = (t < a.T) ? a.pos[t] : -1;
+    for (int kb = k_lo; kb < k_hi; kb += 32) {
+        const int key = kb + (lane & 31);
+        HalfRow<DT, D> kf;
+        load_key<DT, D>(kf, a.k, min(key, a.L - 1));
+        float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+        if constexpr (DT == DT_FP8) I = I * a.k_scale[min(key, a.L - 1)];
+        if (t < a.T && key < k_hi) a.S[(size_t)t * a.L + key] = (key <= my_pos) ? I : -INFINITY;
+    }
+}
+
+__global__ __launch_bounds__(256) void unfused_select_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];
+    const int t = blockIdx.x;
+    MemSource src{a.S + (size_t)t * a.L};
+    const int nvalid = max(min(a.pos[t], a.L - 1) + 1, 0);
+    int32_t* out = a.out_idx + (size_t)t * a.topk;
+    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk : nullptr;
+    select_row(src, nvalid, a.topk, out, osc, sh);
+    if (a.sorted) sort_row_output(out, osc, a.topk, reinterpret_cast<uint64_t*>(sh + 256));
+}
+
+// ---------------------------------------------------------------------------
+// sample carried to the next chunk: keys ranked by selection count
+// ---------------------------------------------------------------------------
+
+__global__ void count_selected_kernel(const int32_t* idx, size_t n, int L, uint32_t* counts) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        const int s = idx[i];
+        if (s >= 0 && s < L) atomicAdd(&counts[s], 1u);
+    }
+}
+
+// counts are < 2^24, so their fp32 values order exactly like the integers
+__global__ void counts_to_f32_kernel(uint32_t* counts, int L) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < L) reinterpret_cast<float*>(counts)[i] = (float)counts[i];
+}
+
+__global__ __launch_bounds__(256) void select_counts_kernel(const float* counts, int L, int n, int32_t* out) {
+    extern __shared__ uint32_t sh[];
+    MemSource src{counts};
+    select_row(src, L, n, out, nullptr, sh);
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+
+template <int V> using ic = std::integral_constant<int, V>;
+
+template <class F>
+static bool dispatch(int dt, int D, int HB, F&& f) {
+#define LTK_CASE(DTV, DV, HBV) \
+    if (dt == DTV && D == DV && HB == HBV) { f(ic<DTV>{}, ic<DV>{}, ic<HBV>{}); return true; }
+    LTK_CASE(DT_F32, 64, 1) LTK_CASE(DT_F32, 64, 2) LTK_CASE(DT_F32, 128, 1) LTK_CASE(DT_F32, 128, 2)
+    LTK_CASE(DT_BF16, 64, 1) LTK_CASE(DT_BF16, 64, 2) LTK_CASE(DT_BF16, 128, 1) LTK_CASE(DT_BF16, 128, 2)
+    LTK_CASE(DT_FP8, 64, 1) LTK_CASE(DT_FP8, 64, 2) LTK_CASE(DT_FP8, 128, 1) LTK_CASE(DT_FP8, 128, 2)
+#undef LTK_CASE
+    return false;
+}
+
+static size_t sort_lds(const IdxArgs& a) {
+    if (!a.sorted) return 0;
+    int p2 = 1;
+    while (p2 < a.topk) p2 <<= 1;
+    return (size_t)p2 * 8;
+}
+
+hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
+                                 uint8_t* ws, hipStream_t st) {
+    const size_t nz = (lay.zero_end - lay.zero_begin) / 4;
+    const int zb = (int)std::min<size_t>((nz + 255) / 256, 2048);
+    zero_kernel<<<std::max(zb, 1), 256, 0, st>>>(reinterpret_cast<uint32_t*>(ws + lay.zero_begin), nz, a.stats);
+    if (n_sample > 0)
+        sample_mark_kernel<<<(n_sample + 255) / 256, 256, 0, st>>>(sample, n_sample, a.L, a.bitmap);
+    sample_compact_kernel<<<1, 1024, 0, st>>>(a.bitmap, (a.L + 31) / 32, a.sample_u, a.nu);
+    return hipGetLastError();
+}
+
+template <class K>
+static void allow_lds(K kernel, size_t bytes) {
+    if (bytes > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)bytes);
+}
+
+hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
+    const int nqg = (a.T + kQPG - 1) / kQPG;
+    hipError_t err = hipSuccess;
+    const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
+        constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
+        sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
+        sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
+        const size_t scan_lds = (size_t)kQPG * a.nbins * 4 + (size_t)kQPG * kStage * 8;
+        allow_lds(scan_kernel<DT_, D_, HB_>, scan_lds);
+        scan_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, scan_lds, st>>>(a);
+        const size_t fin_lds = (size_t)((std::max(a.nbins, 256) + 1) & ~1) * 4 + sort_lds(a);
+        allow_lds(finalize_kernel, fin_lds);
+        finalize_kernel<<<a.T, 256, fin_lds, st>>>(a);
+        const size_t fb_lds = 256 * 4 + sort_lds(a);
+        allow_lds(fallback_kernel<DT_, D_, HB_>, fb_lds);
+        fallback_kernel<DT_, D_, HB_><<<a.T, 256, fb_lds, st>>>(a);
+        err = hipGetLastError();
+    });
+    return ok ? err : hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
+    const int nqg = (a.T + kQPG - 1) / kQPG;
+    hipError_t err = hipSuccess;
+    const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
+        constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
+        unfused_score_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, 0, st>>>(a);
+        const size_t lds = 256 * 4 + sort_lds(a);
+        allow_lds(unfused_select_kernel, lds);
+        unfused_select_kernel<<<a.T, 256, lds, st>>>(a);
+        err = hipGetLastError();
+    });
+    return ok ? err : hipErrorInvalidValue;
+}
+
+hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
+                              uint32_t* counts, hipStream_t st) {
+    zero_kernel<<<std::max(1, std::min((L + 255) / 256, 2048)), 256, 0, st>>>(counts, (size_t)L, nullptr);
+    if (n > 0) count_selected_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(prev_idx, n, L, counts);
+    counts_to_f32_kernel<<<(L + 255) / 256, 256, 0, st>>>(counts, L);
+    select_counts_kernel<<<1, 256, 256 * 4, st>>>(reinterpret_cast<const float*>(counts), L, n_sample, out);
+    return hipGetLastError();
+}
+
+}  // namespace ltk

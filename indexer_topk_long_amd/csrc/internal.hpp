@@ -1,0 +1,90 @@
+// internal.hpp -- host/device shared definitions of the library (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "litetopk.h"
+
+namespace ltk {
+
+constexpr int kQPG = 8;              // queries per workgroup (4 waves x 2 queries)
+constexpr int kStage = 128;          // staging entries per query in LDS (>= 64 + 32)
+constexpr int kFlush = 64;           // write-back batch (one wave64 of 8-byte entries)
+constexpr int kDefaultBins = 256;
+constexpr int kMaxBins = 4096;
+constexpr int64_t kDefaultCcap = 16384;
+constexpr int64_t kDefaultCcapRetrieve = 131072;
+constexpr int kMaxSortedK = 8192;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of one fused call.  The [zero_begin, zero_end) range is cleared
+// by the first kernel of every call.
+struct WsLayout {
+    size_t tail, flags, nu, bitmap, zero_begin, zero_end;
+    size_t meta, sample_u, sscore, cand, total;
+};
+
+inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap) {
+    WsLayout w{};
+    size_t o = 0;
+    w.zero_begin = o;
+    w.tail = o;   o = align_up(o + (size_t)T * 4, 256);
+    w.flags = o;  o = align_up(o + (size_t)T * 4, 256);
+    w.nu = o;     o = align_up(o + 64, 256);
+    w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
+    w.zero_end = o;
+    w.meta = o;     o = align_up(o + (size_t)T * sizeof(int32_t) * 4, 256);
+    w.sample_u = o; o = align_up(o + (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
+    w.sscore = o;   o = align_up(o + (size_t)T * (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
+    w.cand = o;     o = align_up(o + (size_t)T * (size_t)ccap * 8, 256);
+    w.total = o;
+    return w;
+}
+
+// Everything a kernel of the fused indexer path needs.
+struct IdxArgs {
+    const uint8_t* q;        // [T, H, D]
+    const float* q_scale;    // [T] (fp8) or null
+    const uint8_t* k;        // [L, D]
+    const float* k_scale;    // [L] (fp8) or null
+    const float* w;          // [T, H]
+    const int32_t* pos;      // [T]
+    int T, H, L, topk, nbins;
+    int n_sample;            // row stride of sscore
+    int n_splits;            // key-range splits per query group (scan, unfused score)
+    int s_splits;            // sample splits per query group (sample pass)
+    int refresh_every;       // <= 0: never
+    int sorted;
+    int64_t ccap;
+    // workspace
+    uint32_t* tail;
+    uint32_t* flags;
+    uint32_t* nu;
+    uint32_t* bitmap;
+    void* meta;              // Meta[T]
+    int32_t* sample_u;
+    float* sscore;
+    uint2* cand;
+    // outputs
+    int32_t* out_idx;
+    float* out_score;
+    ltk_stats* stats;
+    float* S;                // unfused: [T, L] score matrix
+};
+
+struct LaunchCfg {
+    hipStream_t stream;
+};
+
+// Host launchers (return hipSuccess or the first launch error).
+hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
+                                 uint8_t* ws, hipStream_t st);
+hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
+hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
+hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
+                              uint32_t* counts, hipStream_t st);
+
+}  // namespace ltk

@@ -9,6 +9,7 @@ from .oracle import (  # noqa: F401
     e4m3fn_table,
     indexer_row_scores,
     indexer_scores,
+    next_sample,
     oracle_indexer,
     oracle_retrieval,
     retrieval_row_scores,

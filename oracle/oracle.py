@@ -187,3 +187,13 @@ def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t: int, dtype: s
     for s0 in range(0, N, block):
         out[s0 : s0 + block] = retrieval_scores(qd, decode(db_raw[s0 : s0 + block], dtype))
     return out
+
+
+def next_sample(prev_idx: np.ndarray, L: int, n: int) -> np.ndarray:
+    """Keys 0..L-1 ranked by how many rows of prev_idx selected them (-1 entries
+    ignored), ties to the lower index; the first n.  This is the reading of
+    the pages' "reuse the previous chunk's top-3k tokens as the sample"
+    ("Sampling") for one shared sample per chunk."""
+    p = np.asarray(prev_idx).ravel()
+    counts = np.bincount(p[(p >= 0) & (p < L)], minlength=L)
+    return np.lexsort((np.arange(L), -counts))[:n].astype(np.int32)

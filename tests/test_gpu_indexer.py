@@ -1,0 +1,176 @@
+"""GPU parity of the fused indexer path and the unfused baseline against the
+CPU oracle, and bit-exact agreement of the GPU paths with each other."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import canon, check_rows, say, to_dev
+from workloads import indexer_config, indexer_inputs, random_sample
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_fused(lib, d, topk, opts=None, sample="default"):
+    smp = d["sample"] if isinstance(sample, str) else sample
+    idx, sc = lib.score_select(d["q"], d["k"], d["w"], d["pos"], topk, sample=smp, q_scale=d["q_scale"],
+                               k_scale=d["k_scale"], opts=opts, return_scores=True)
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _run_unfused(lib, d, topk):
+    idx, sc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], topk, q_scale=d["q_scale"],
+                                       k_scale=d["k_scale"], return_scores=True)
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+@pytest.fixture(scope="module")
+def cfg0():
+    return indexer_config(0)
+
+
+def test_device_is_gfx950(lib):
+    assert lib.device_check() == 0
+
+
+def test_unfused_config0_vs_oracle(lib, cfg0):
+    say("unfused config 0")
+    d = to_dev(cfg0)
+    idx, sc = _run_unfused(lib, d, cfg0["topk"])
+    check_rows(cfg0, idx, sc, range(cfg0["T"]), "unfused cfg0")
+
+
+def test_fused_config0_vs_oracle_and_unfused(lib, cfg0):
+    say("fused config 0")
+    d = to_dev(cfg0)
+    idx, sc = _run_fused(lib, d, cfg0["topk"])
+    check_rows(cfg0, idx, sc, range(cfg0["T"]), "fused cfg0")
+    uidx, usc = _run_unfused(lib, d, cfg0["topk"])
+    a, asc = canon(idx, sc)
+    b, bsc = canon(uidx, usc)
+    assert np.array_equal(a, b)
+    assert np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))   # identical fp32 scores
+
+
+SMALL = [
+    # (T, L, H, D, dtype, topk, n_hot) -- ragged T and L, padded heads
+    (37, 3001, 64, 128, "bf16", 100, 200),
+    (37, 3001, 64, 128, "fp8", 100, 200),
+    (19, 2500, 20, 64, "bf16", 64, 100),
+    (16, 1100, 33, 64, "fp8", 300, 50),
+    (9, 777, 8, 128, "f32", 50, 40),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"T{s[0]}_L{s[1]}_H{s[2]}_D{s[3]}_{s[4]}_k{s[5]}")
+def test_fused_small_shapes(lib, shape):
+    T, L, H, D, dt, k, nh = shape
+    say("small", shape)
+    inp = indexer_inputs(T, L, H, D, dt, k, nh, drift=True, tag=21, n_sample=3 * k)
+    d = to_dev(inp)
+    idx, sc = _run_fused(lib, d, k)
+    check_rows(inp, idx, sc, range(T), f"fused {shape}")
+    uidx, usc = _run_unfused(lib, d, k)
+    check_rows(inp, uidx, usc, range(T), f"unfused {shape}")
+    a, asc = canon(idx, sc)
+    b, bsc = canon(uidx, usc)
+    assert np.array_equal(a, b) and np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
+
+
+def _variants(inp):
+    L, k = inp["L"], inp["topk"]
+    base = inp["sample"]
+    worst = np.arange(0, min(3 * k, L), dtype=np.int32)
+    return {
+        "random": base,
+        "empty": np.zeros(0, np.int32),
+        "single": base[:1],
+        "low_index_keys": worst,
+        "dups_invalid": np.concatenate([base[:50]] * 4 + [np.array([-7, -1, L, L + 100], np.int32)]).astype(np.int32),
+        "other_seed": random_sample(3 * k, L, tag=77),
+    }
+
+
+def test_sample_bins_refresh_capacity_independence(lib):
+    """The result does not depend on the sample, the bin count, the refresh
+    period, the key split or the buffer capacity (forced overflow included):
+    the GPU output is bit-identical across all of them."""
+    inp = indexer_inputs(24, 5000, 64, 128, "bf16", 200, 300, drift=True, tag=31, n_sample=600)
+    d = to_dev(inp)
+    import indexer_topk_long_amd as ltk
+    ref, ref_sc = canon(*_run_fused(lib, d, 200))
+    check_rows(inp, *_run_fused(lib, d, 200), range(24), "reference")
+    import torch
+    cases = []
+    for name, smp in _variants(inp).items():
+        cases.append((name, torch.from_numpy(smp).cuda(), None))
+    for nb in (1, 2, 7, 4096):
+        cases.append((f"nbins{nb}", d["sample"], ltk.Opts(nbins=nb)))
+    for r in (3, -1):
+        cases.append((f"refresh{r}", d["sample"], ltk.Opts(refresh_every=r)))
+    for sp in (1, 3, 8):
+        cases.append((f"splits{sp}", d["sample"], ltk.Opts(l_splits=sp)))
+    for cap in (1, 64, 250):
+        cases.append((f"ccap{cap}", d["sample"], ltk.Opts(cand_capacity=cap)))
+    cases.append(("nbins1_ccap1_empty", torch.zeros(0, dtype=torch.int32, device="cuda"),
+                  ltk.Opts(nbins=1, cand_capacity=1, refresh_every=-1)))
+    for name, smp, o in cases:
+        say("variant", name)
+        got, got_sc = canon(*_run_fused(lib, d, 200, opts=o, sample=smp))
+        assert np.array_equal(got, ref), name
+        assert np.array_equal(got_sc.view(np.uint32), ref_sc.view(np.uint32)), name
+
+
+def test_forced_overflow_reports_stats(lib):
+    import indexer_topk_long_amd as ltk
+    inp = indexer_inputs(16, 2000, 64, 128, "fp8", 64, 100, drift=True, tag=41, n_sample=192)
+    d = to_dev(inp)
+    idx, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], 64, sample=d["sample"], q_scale=d["q_scale"],
+                               k_scale=d["k_scale"], opts=ltk.Opts(cand_capacity=8), return_stats=True)
+    assert st.overflow_rows == 16
+    check_rows(inp, idx.cpu().numpy(), None, range(16), "overflow")
+    idx2, st2 = lib.score_select(d["q"], d["k"], d["w"], d["pos"], 64, sample=d["sample"], q_scale=d["q_scale"],
+                                 k_scale=d["k_scale"], return_stats=True)
+    assert st2.overflow_rows == 0 and 64 * 16 <= st2.cand_written and st2.max_cand_per_query >= 64
+    assert np.array_equal(canon(idx.cpu().numpy()), canon(idx2.cpu().numpy()))
+
+
+def test_edge_positions_and_small_k(lib):
+    """Rows with fewer valid keys than k (padding), no valid key, k = 1, unsorted
+    and repeated positions, positions past the context."""
+    T, L = 12, 700
+    pos = np.array([0, 5, 699, 3, 350, -1, 1000, 63, 64, 65, 5, 200], np.int32)
+    for k in (1, 10, 128):
+        inp = indexer_inputs(T, L, 64, 128, "bf16", k, 40, tag=51, pos=pos, n_sample=3 * k)
+        d = to_dev(inp)
+        say("edge k", k)
+        idx, sc = _run_fused(lib, d, k)
+        check_rows(inp, idx, sc, range(T), f"edge k={k}")
+        uidx, usc = _run_unfused(lib, d, k)
+        check_rows(inp, uidx, usc, range(T), f"edge unfused k={k}")
+
+
+def test_sorted_output(lib):
+    import indexer_topk_long_amd as ltk
+    inp = indexer_inputs(10, 3000, 64, 128, "bf16", 150, 200, tag=61, n_sample=450)
+    d = to_dev(inp)
+    idx, sc = _run_fused(lib, d, 150, opts=ltk.Opts(sorted_output=True))
+    for t in range(10):
+        keys = list(zip(-sc[t].astype(np.float64), idx[t]))
+        assert keys == sorted(keys)
+    check_rows(inp, idx, sc, range(10), "sorted")
+
+
+def test_determinism(lib, cfg0):
+    d = to_dev(cfg0)
+    a = _run_fused(lib, d, cfg0["topk"])
+    for _ in range(5):
+        b = _run_fused(lib, d, cfg0["topk"])
+        assert np.array_equal(canon(a[0]), canon(b[0]))
+
+
+def test_next_sample_vs_oracle(lib):
+    import torch
+    from oracle import next_sample
+    g = np.random.default_rng(3)
+    prev = g.integers(-1, 500, size=(64, 40)).astype(np.int32)
+    got = lib.next_sample(torch.from_numpy(prev).cuda(), 500, 120).cpu().numpy()
+    assert np.array_equal(np.sort(got), np.sort(next_sample(prev, 500, 120)))

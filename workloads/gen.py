@@ -105,7 +105,7 @@ def _u_at(p: np.ndarray, L: int, u0: np.ndarray, u1: np.ndarray, drift: bool) ->
 def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot: int,
                    drift: bool = False, w_range=(0.0, 1.0), tag: int = 100,
                    seed: int = SEED_BASE, chunk: int = 0, pos=None, n_sample: int | None = None,
-                   hot_gain: float = 3.0, q_gain: float = 0.5):
+                   hot_gain: float = 3.0, q_gain: float = 0.5, keys=None):
     """Inputs for one indexer chunk.
 
     Keys: k[s] = N(0, I_D) + hot_gain * u(s) for s in a hot set of n_hot keys
@@ -120,13 +120,14 @@ def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot:
     the previous-chunk sample is built by the caller from a previous run).
     """
     u0, u1 = _direction(tag, D, seed)
-    gk = _rng(tag, _S_KEYS, seed)
-    k = gk.standard_normal((L, D), dtype=np.float32)
-    gh = _rng(tag, _S_HOT, seed)
-    n_hot = min(n_hot, L)
-    hot = np.sort(gh.choice(L, size=n_hot, replace=False)) if n_hot > 0 else np.zeros(0, np.int64)
-    if n_hot:
-        k[hot] += (hot_gain * _u_at(hot, L, u0, u1, drift)).astype(np.float32)
+    if keys is None:
+        gk = _rng(tag, _S_KEYS, seed)
+        k = gk.standard_normal((L, D), dtype=np.float32)
+        gh = _rng(tag, _S_HOT, seed)
+        n_hot = min(n_hot, L)
+        hot = np.sort(gh.choice(L, size=n_hot, replace=False)) if n_hot > 0 else np.zeros(0, np.int64)
+        if n_hot:
+            k[hot] += (hot_gain * _u_at(hot, L, u0, u1, drift)).astype(np.float32)
 
     if pos is None:
         end = L + chunk * T
@@ -140,7 +141,10 @@ def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot:
     w = gw.uniform(w_range[0], w_range[1], size=(T, H)).astype(np.float32)
 
     q_raw, q_scale = to_storage(q, dtype, axes=(1, 2))
-    k_raw, k_scale = to_storage(k, dtype, axes=(1,))
+    if keys is None:
+        k_raw, k_scale = to_storage(k, dtype, axes=(1,))
+    else:  # the same (already rounded) keys as another chunk of this context
+        k_raw, k_scale, hot = keys
     out = dict(kind="indexer", T=T, L=L, H=H, D=D, dtype=dtype, topk=topk,
                q=q_raw, k=k_raw, q_scale=q_scale, k_scale=k_scale, w=w,
                pos=pos.astype(np.int32), hot=hot.astype(np.int64))
@@ -156,13 +160,23 @@ def random_sample(n: int, upto: int, tag: int = 0, seed: int = SEED_BASE, stream
     return np.sort(g.choice(upto, size=n, replace=False)).astype(np.int32)
 
 
-def indexer_config(i: int, chunk: int = 0, seed: int = SEED_BASE):
-    """The seeded inputs of indexer workload ``i`` (0-3); chunk -1 is the previous chunk."""
+def indexer_config(i: int, chunk: int = 0, seed: int = SEED_BASE, with_prev: bool = False):
+    """The seeded inputs of indexer workload ``i`` (0-3); chunk -1 is the previous chunk.
+
+    With ``with_prev``, the result also holds ``prev``: the previous chunk's
+    queries, weights, positions and bootstrap sample over the same keys.
+    """
     c = CONFIGS[i]
     assert c["kind"] == "indexer"
-    return indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
-                          drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk,
-                          n_sample=c["n_sample"])
+    out = indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
+                         drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk,
+                         n_sample=c["n_sample"], keys=None)
+    if with_prev:
+        p = indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
+                           drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk - 1,
+                           n_sample=c["n_sample"], keys=(out["k"], out["k_scale"], out["hot"]))
+        out["prev"] = p
+    return out
 
 
 def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, sigma: float = 0.3,
