@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of the fused Indexer-TopK on one MI355X.
+
+Workload (default): the 1M-context prefill chunk -- 8,192 queries at the last
+8,192 positions of L = 1,048,576 causal keys, H = 64 indexer heads, D = 128,
+fp8 e4m3fn queries/keys with per-token fp32 scales, k = 2,048, sample = the
+previous chunk's top-6,144 keys (computed untimed by running the previous
+chunk through the same library).  Inputs are synthetic and seeded, resident in
+device memory before timing starts.
+
+One step = one litetopk_score_select call: sample pass, fused scan, finalize,
+overflow fallback.  Metric: scored query-key pairs per second.  The line also
+carries the roofline of the dominant kernel (the fused scan, timed with HIP
+events on its stream), the unfused full-matrix baseline timed the same way,
+bytes written per query, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(inp, torch):
+    dt = inp["dtype"]
+
+    def raw(x):
+        x = np.ascontiguousarray(x)
+        if dt == "f32":
+            return torch.from_numpy(x).cuda()
+        if dt == "bf16":
+            return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(x).cuda().view(torch.float8_e4m3fn)
+
+    d = dict(q=raw(inp["q"]), k=raw(inp["k"]), w=torch.from_numpy(inp["w"]).cuda(),
+             pos=torch.from_numpy(inp["pos"].astype(np.int32)).cuda(), q_scale=None, k_scale=None)
+    if dt == "fp8":
+        d["q_scale"] = torch.from_numpy(inp["q_scale"]).cuda()
+        d["k_scale"] = torch.from_numpy(inp["k_scale"]).cuda()
+    return d
+
+
+def cpu_baseline(inp, n_rows: int):
+    """The CPU oracle, as it stands, on n_rows query rows spread over the chunk."""
+    from oracle import oracle_indexer
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    T, L = inp["T"], inp["L"]
+    rows = np.linspace(0, T - 1, n_rows).astype(np.int64)
+    pairs = int(sum(min(int(inp["pos"][t]), L - 1) + 1 for t in rows))
+    t0 = time.perf_counter()
+    oracle_indexer(inp, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} of {T} query rows (evenly spaced), all their causal keys: {pairs} pairs "
+                      f"in {dt:.2f} s, fp64 numpy, including the fp64 decode of the keys"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3, help="indexer workload 0-3 (3 = the 1M-context chunk)")
+    ap.add_argument("--unfused-steps", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import indexer_topk_long_amd as ltk
+    from workloads import CONFIGS, indexer_config
+
+    cfg = CONFIGS[args.config]
+    log(f"generating workload {cfg['name']} ...")
+    t0 = time.perf_counter()
+    inp = indexer_config(args.config, with_prev=True)
+    log(f"  generated in {time.perf_counter() - t0:.1f} s")
+    T, L, H, D, k = inp["T"], inp["L"], inp["H"], inp["D"], inp["topk"]
+    d = to_dev(inp, torch)
+    prev = dict(inp["prev"])
+    prev.update(k=inp["k"], k_scale=inp["k_scale"])
+    pd = to_dev(prev, torch)
+    n_sample = cfg["n_sample"]
+
+    # previous chunk (bootstrapped with a seeded random sample), then its top-3k
+    boot = torch.from_numpy(prev["sample"]).cuda()
+    prev_idx = ltk.score_select(pd["q"], pd["k"], pd["w"], pd["pos"], k, sample=boot, q_scale=pd["q_scale"],
+                                k_scale=pd["k_scale"])
+    sample = ltk.next_sample(prev_idx, L, n_sample)
+    del pd, prev_idx
+    torch.cuda.synchronize()
+    log("  previous-chunk sample ready")
+
+    ws_bytes = ltk.workspace_bytes(ltk.KIND_SCORE_SELECT, T, H, D, L, k, n_sample, {"f32": 0, "bf16": 1, "fp8": 2}[inp["dtype"]])
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step(opts=None, **kw):
+        return ltk.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                k_scale=d["k_scale"], opts=opts, workspace=ws, **kw)
+
+    for _ in range(args.warmup):
+        ref = step()
+    torch.cuda.synchronize()
+    ev = ltk.HipEvents(args.steps)
+    opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        out = step(opts[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
+    ev.close()
+    log(f"  fused: {ms_step:.3f} ms/step, scan kernel {scan_ms:.3f} ms")
+
+    pos = inp["pos"].astype(np.int64)
+    pairs = int(np.sum(np.minimum(pos, L - 1) + 1))
+    flops = 2.0 * H * D * pairs
+    peak = {"fp8": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS, "f32": FP32_PEAK_TFLOPS}[inp["dtype"]]
+    achieved = flops / (scan_ms * 1e-3) / 1e12
+
+    _, st = step(return_stats=True)
+    cands = st.cand_written / T
+    bytes_q = (8.0 * st.cand_written + 4.0 * T * k) / T
+    full_q = 4.0 * L
+
+    # unfused baseline (full fp32 score matrix + radix select), same inputs
+    unf = None
+    if args.unfused_steps > 0:
+        uws = torch.empty((T * L * 4), dtype=torch.uint8, device="cuda")
+        uout = ltk.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                        k_scale=d["k_scale"], workspace=uws)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(torch.sort(uout, dim=1).values, torch.sort(out, dim=1).values))
+        t0 = time.perf_counter()
+        for _ in range(args.unfused_steps):
+            ltk.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                     k_scale=d["k_scale"], workspace=uws)
+        torch.cuda.synchronize()
+        ums = (time.perf_counter() - t0) * 1e3 / args.unfused_steps
+        unf = {"ms_per_step": round(ums, 3), "value": pairs / (ums * 1e-3), "unit": "pairs/s",
+               "bytes_written_per_query": 4.0 * L + 4.0 * k, "same_index_sets_as_fused": same}
+        del uws
+        log(f"  unfused: {ums:.3f} ms/step, same sets: {same}")
+    consistent = bool(torch.equal(torch.sort(out, dim=1).values, torch.sort(ref, dim=1).values))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("  timing the CPU oracle ...")
+        cpu = cpu_baseline(inp, args.cpu_rows)
+
+    line = {
+        "metric": "scored query-key pairs/s at 1M context, k=2048",
+        "value": pairs / (ms_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp["dtype"],
+        "data": "synthetic (seeded concentrated-score generator; previous-chunk sample)",
+        "config": {"workload": f"{cfg['name']}: T={T} queries at positions {int(pos[0])}..{int(pos[-1])}, "
+                               f"L={L} causal keys, H={H}, D={D}, {inp['dtype']}, k={k}, "
+                               f"sample=previous chunk top-{n_sample}",
+                   "T": T, "L": L, "H": H, "D": D, "topk": k, "n_sample": n_sample, "pairs": pairs},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "scan_kernel (fused score + filter)", "kernel_ms": round(scan_ms, 4),
+                     "algorithmic_flops_per_launch": flops},
+        "bytes_written_per_query": round(bytes_q, 1),
+        "full_matrix_bytes_per_query": full_q,
+        "candidates_per_query": round(cands, 1),
+        "overflow_rows": st.overflow_rows,
+        "repeat_consistent": consistent,
+        "unfused_baseline": unf,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

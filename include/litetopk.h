@@ -65,11 +65,13 @@ typedef enum {
 /* Tuning options (HOST struct).  Pass NULL for the defaults; a zero field
  * also means "default".  None of them changes the result, only the work. */
 typedef struct {
-    int32_t nbins;          /* equal-width bins over the sample's score range; 1..4096, default 256 */
+    int32_t nbins;          /* equal-width bins over the sample's score range; 1..1024, default 256 */
     int32_t refresh_every;  /* threshold refresh after every N candidate batches; default 1; <0 = never */
     int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
     int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
     int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072) */
+    void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan */
+    void* scan_event_stop;  /* optional hipEvent_t recorded just after it (profiling; NULL = none) */
 } ltk_opts;
 
 /* Optional counters (DEVICE struct, written by the call; pass NULL to skip). */

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     KIND_RETRIEVE,
     KIND_SCORE_SELECT,
     KIND_UNFUSED,
+    HipEvents,
     LtkError,
     Opts,
     Stats,

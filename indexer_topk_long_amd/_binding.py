@@ -16,7 +16,8 @@ _c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, c
 
 class _COpts(ctypes.Structure):
     _fields_ = [("nbins", _c_i32), ("refresh_every", _c_i32), ("l_splits", _c_i32),
-                ("sorted_output", _c_i32), ("cand_capacity", _c_i64)]
+                ("sorted_output", _c_i32), ("cand_capacity", _c_i64),
+                ("scan_event_start", _c_p), ("scan_event_stop", _c_p)]
 
 
 @dataclass
@@ -27,10 +28,12 @@ class Opts:
     l_splits: int = 0
     sorted_output: bool = False
     cand_capacity: int = 0
+    scan_event_start: int | None = None   # raw hipEvent_t handles (profiling)
+    scan_event_stop: int | None = None
 
     def c(self) -> _COpts:
         return _COpts(self.nbins, self.refresh_every, self.l_splits, int(bool(self.sorted_output)),
-                      self.cand_capacity)
+                      self.cand_capacity, self.scan_event_start, self.scan_event_stop)
 
 
 @dataclass
@@ -246,3 +249,33 @@ def retrieve(q, db, topk: int, sample=None, opts: Opts | None = None, return_sco
     if return_stats:
         res.append(_read_stats(st))
     return res[0] if len(res) == 1 else tuple(res)
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime already loaded by torch (for timing one kernel)."""
+
+    def __init__(self, n: int):
+        library()
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(a)) or self.hip.hipEventCreate(ctypes.byref(b)):
+                raise RuntimeError("hipEventCreate failed")
+            self.pairs.append((a.value, b.value))
+
+    def elapsed_ms(self, i: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), self.pairs[i][0], self.pairs[i][1])
+        if rc:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        self.pairs = []

@@ -28,6 +28,7 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 struct Opts {
     int nbins, refresh_every, l_splits, sorted;
     int64_t ccap;
+    hipEvent_t ev0, ev1;
 };
 
 static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
@@ -36,8 +37,11 @@ static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
     r.l_splits = 0;
     r.sorted = 0;
     r.ccap = default_ccap;
+    r.ev0 = r.ev1 = nullptr;
     if (!o) return LTK_OK;
-    if (o->nbins < 0 || o->nbins > kMaxBins) return LTK_EINVAL;
+    r.ev0 = static_cast<hipEvent_t>(o->scan_event_start);
+    r.ev1 = static_cast<hipEvent_t>(o->scan_event_stop);
+    if (o->nbins < 0 || o->nbins > kMaxBins) return LTK_EINVAL;   // LDS holds 16 x nbins counters
     if (o->nbins) r.nbins = o->nbins;
     if (o->refresh_every) r.refresh_every = o->refresh_every;   // negative: never
     if (o->l_splits < 0 || o->l_splits > 4096) return LTK_EINVAL;
@@ -59,13 +63,16 @@ static int check_indexer_sizes(int32_t T, int32_t H, int32_t D, int64_t L, int32
 }
 
 // Key-range splits so that a launch holds at least ~2048 workgroups when the
-// context is long enough (each split keeps >= 4096 keys).
+// context is long enough (each split keeps >= 16384 keys).
 static int auto_splits(int nqg, int64_t L, int requested) {
     if (requested > 0) return requested;
     int s = 1;
-    while ((int64_t)nqg * s < 2048 && L / (s * 2) >= 4096) s *= 2;
+    while ((int64_t)nqg * s < 2048 && L / (s * 2) >= 16384) s *= 2;
     return s;
 }
+
+// Queries per scan workgroup: 8 waves x 1 query.
+static int scan_qpg(int) { return 8; }
 
 }  // namespace ltk
 
@@ -134,7 +141,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.nbins = o.nbins;
     a.n_sample = n_sample > 0 ? n_sample : 1;
     const int nqg = (T + kQPG - 1) / kQPG;
-    a.n_splits = auto_splits(nqg, L, o.l_splits);
+    a.n_splits = auto_splits((T + scan_qpg(dtype) - 1) / scan_qpg(dtype), L, o.l_splits);
     a.s_splits = 1;
     while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= 8) a.s_splits *= 2;
     a.refresh_every = o.refresh_every;
@@ -152,6 +159,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.out_score = out_score;
     a.stats = stats;
     a.S = nullptr;
+    a.ev_scan_start = o.ev0;
+    a.ev_scan_stop = o.ev1;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_prepare_sample(a, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;

@@ -99,6 +99,17 @@ __device__ __forceinline__ void mfma_2slots(const HalfRow<DT, D> (&qa)[HB], cons
     }
 }
 
+// One slot: query block q x one 32-key block (HB independent chains).
+template <int DT, int D, int HB>
+__device__ __forceinline__ void mfma_1slot(const HalfRow<DT, D> (&q)[HB], const HalfRow<DT, D>& kf, v16f (&acc)[HB]) {
+#pragma unroll
+    for (int m = 0; m < HB; ++m) acc[m] = v16f{};
+#pragma unroll
+    for (int j = 0; j < HalfRow<DT, D>::KSTEPS; ++j)
+#pragma unroll
+        for (int m = 0; m < HB; ++m) mfma_step<DT, D>(q[m], kf, j, acc[m]);
+}
+
 // Head of accumulator register r of a lane in half `half`, head block m:
 // the 32x32 MFMA result row held by (lane, r) is 8*(r/4) + 4*half + (r%4).
 __device__ __forceinline__ int head_of(int m, int r, int half) { return m * 32 + 8 * (r >> 2) + 4 * half + (r & 3); }

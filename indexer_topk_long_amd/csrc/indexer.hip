@@ -243,111 +243,243 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 // ---------------------------------------------------------------------------
 // Filter: the fused scan
 // ---------------------------------------------------------------------------
+//
+// One workgroup = 8 waves sharing K tiles that are streamed into LDS with
+// direct global->LDS loads (double-buffered, 32 KB of keys per tile), so the
+// eight waves read each key from device memory once.  fp8 waves own two
+// queries (one per 32-lane half, both scored against the same 32 keys);
+// bf16/fp32 waves own one query scored against two 32-key blocks.  Two waves
+// per SIMD let one wave's VALU epilogue overlap the other's MFMAs.
+
+constexpr int kScanWaves = 8;
+constexpr int kTileBytes = 32768;
+
+template <int DT> struct ScanShape { static constexpr int QPW = 1; };
+
+template <int DT, int D>
+struct TileGeom {
+    static constexpr int RB = D * DTraits<DT>::ESZ;        // bytes per key row
+    static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
+    static constexpr int TK = kTileBytes / RB;             // keys per tile
+    static constexpr int NINST = TK * CPR / 64;            // wave-wide 1 KB loads per tile
+    static constexpr int PER_WAVE = NINST / kScanWaves;
+    static constexpr int SCALE_BYTES = (DT == DT_FP8) ? TK * 4 : 0;
+    static constexpr int STAGE_BYTES = kTileBytes + SCALE_BYTES;
+    static_assert(NINST % kScanWaves == 0, "tile loads split evenly over the waves");
+    static_assert(TK % 64 == 0, "per-key scales load in whole 64-lane wave loads");
+};
+
+// XOR swizzle of the 16-byte chunks of a row, so that the 8 lanes served
+// together by a 128-bit LDS read (8 consecutive rows, same logical chunk)
+// hit distinct banks.
+template <int CPR>
+__device__ __forceinline__ int chunk_swz(int r) { return CPR >= 8 ? (r & 7) : ((r >> 1) & 3); }
+
+// Direct global -> LDS copies (gfx950 global_load_lds): every lane moves 16
+// (or 4) bytes, landing at lds + 16*lane (4*lane); lds must be wave-uniform.
+__device__ __forceinline__ void lds_direct16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_direct4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Issue this wave's share of the direct loads of the tile starting at key0.
+template <int DT, int D>
+__device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* st, int wave, int lane) {
+    using G = TileGeom<DT, D>;
+#pragma unroll
+    for (int j = 0; j < G::PER_WAVE; ++j) {
+        const int inst = wave + j * kScanWaves;
+        const int p = inst * 64 + lane;
+        const int r = p / G::CPR, pc = p % G::CPR;
+        const int c = pc ^ chunk_swz<G::CPR>(r);
+        const int key = min(key0 + r, a.L - 1);
+        lds_direct16(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
+    }
+    if constexpr (DT == DT_FP8) {
+        // one per-key scale per lane (keys past the context re-read the last one)
+#pragma unroll
+        for (int j = wave; j < G::TK / 64; j += kScanWaves) {
+            const int key = min(key0 + j * 64 + lane, a.L - 1);
+            lds_direct4(a.k_scale + key, st + kTileBytes + j * 256);
+        }
+    }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void read_frag(HalfRow<DT, D>& f, const uint8_t* st, int r0, int lane) {
+    using G = TileGeom<DT, D>;
+    const int r = r0 + (lane & 31), h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < HalfRow<DT, D>::NV; ++i) {
+        const int c = h * (G::CPR / 2) + i;
+        f.v[i] = *reinterpret_cast<const u32x4*>(st + r * G::RB + ((c ^ chunk_swz<G::CPR>(r)) * 16));
+    }
+}
+
+// Smallest fp32 score whose bin is >= thr (bin_of is monotone), found by
+// bisection over the ordered float encoding: the gate I >= tau is then
+// exactly the gate bin_of(I) >= thr, and the bin is only computed for keys
+// that pass.
+__device__ __forceinline__ float tau_of(int thr, float smin, float delta, int nbins) {
+    if (thr <= 0) return -INFINITY;
+    uint32_t lo = ord_f32(-3.402823466e38f), hi = ord_f32(3.402823466e38f);   // bin(lo) < thr <= bin(hi)
+    while (hi - lo > 1u) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (bin_of(unord_f32(mid), smin, delta, nbins) >= thr) hi = mid; else lo = mid;
+    }
+    return unord_f32(hi);
+}
 
 template <int DT, int D, int HB>
-__global__ __launch_bounds__(256) void scan_kernel(IdxArgs a) {
-    extern __shared__ uint32_t sh[];
+__global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
+    using G = TileGeom<DT, D>;
+    constexpr int QPW = ScanShape<DT>::QPW;
+    constexpr int QPG = kScanWaves * QPW;
+    extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
     const int nbins = a.nbins;
-    uint32_t* hist = sh;                                    // [8][nbins]
-    uint2* stage = reinterpret_cast<uint2*>(sh + kQPG * nbins);   // [8][kStage]
+    uint8_t* tiles = shm;                                                  // 2 stages
+    uint32_t* hist = reinterpret_cast<uint32_t*>(shm + 2 * G::STAGE_BYTES);  // [QPG][nbins]
+    uint2* stage = reinterpret_cast<uint2*>(hist + QPG * nbins);           // [QPG][kStage]
     const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
-    const int t0 = qg * kQPG;
-    const int ta = t0 + 2 * wave, tb = ta + 1;
-    const int t = half ? tb : ta;
-    const int qi = 2 * wave + half;                         // this half's local query
+    const int t0 = qg * QPG;
+    const int s0 = t0 + QPW * wave, s1 = s0 + (QPW - 1);                  // the wave's queries
+    const int t = (QPW == 2 && half) ? s1 : s0;                           // this lane's query
+    const int qi = QPW * wave + ((QPW == 2) ? half : 0);                  // its local index
     const uint32_t k = (uint32_t)a.topk;
 
-    for (int i = lane; i < 2 * nbins; i += 64) hist[2 * wave * nbins + i] = 0u;
+    for (int i = lane; i < QPW * nbins; i += 64) hist[QPW * wave * nbins + i] = 0u;
 
-    const int kend = group_key_end(a, t0);
-    const int per = (((kend + a.n_splits - 1) / a.n_splits) + 31) & ~31;
+    // keys any query of the group can see, split into tile-aligned ranges
+    int e = 0;
+    for (int i = lane; i < QPG; i += 64) {
+        const int tt = t0 + i;
+        if (tt < a.T) e = max(e, min(a.pos[tt], a.L - 1) + 1);
+    }
+    const int kend = wave_max_i32(e);
+    const int per = ((kend + a.n_splits - 1) / a.n_splits + G::TK - 1) / G::TK * G::TK;
     const int k_lo = split * per, k_hi = min(kend, k_lo + per);
 
     const bool tv = t < a.T;
     const int my_pos = tv ? min(a.pos[t], a.L - 1) : -1;
-    const int wave_end = min(k_hi, wave_max_i32(my_pos) + 1);   // this wave's last useful key + 1
+    const int wave_end = min(k_hi, wave_max_i32(my_pos) + 1);
     Meta m{0.0f, 1.0f, 0, 0};
     if (tv) m = reinterpret_cast<const Meta*>(a.meta)[t];
-    int thr = m.thr0;                                           // threshold bin of this half's query
+    int thr = m.thr0;
+    float tau = tau_of(thr, m.smin, m.delta, nbins);
 
     QueryRegs<DT, D, HB> ra, rb;
-    load_query<DT, D, HB>(ra, a, ta);
-    load_query<DT, D, HB>(rb, a, tb);
+    load_query<DT, D, HB>(ra, a, s0);
+    if constexpr (QPW == 2) load_query<DT, D, HB>(rb, a, s1);
 
-    int cnt_a = 0, cnt_b = 0;        // staged entries (wave-uniform)
-    int fl_a = 0, fl_b = 0;          // batches written back (wave-uniform)
-    uint2* st_mine = stage + qi * kStage;
+    int cnt[QPW] = {};   // staged entries per query (wave-uniform)
+    int fl[QPW] = {};    // batches written back per query
     const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-    // write back one full batch of query slot s and refresh its threshold
-    auto flush = [&](int s, int& cnt, int& fl) {
-        const int tq = s ? tb : ta;
-        uint2* st = stage + (2 * wave + s) * kStage;
+    auto flush = [&](int s) {
+        const int tq = s0 + s;
+        const int lq = QPW * wave + s;
+        uint2* st = stage + lq * kStage;
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)kFlush);
         base = __shfl(base, 0);
-        const uint2 e = st[lane];
-        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = e;
-        const int rem = cnt - kFlush;
+        const uint2 en = st[lane];
+        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = en;
+        const int rem = cnt[s] - kFlush;
         uint2 r{0u, 0u};
         if (lane < rem) r = st[kFlush + lane];
         if (lane < rem) st[lane] = r;
-        cnt = rem;
-        ++fl;
-        if (a.refresh_every > 0 && fl % a.refresh_every == 0) {
+        cnt[s] = rem;
+        ++fl[s];
+        if (a.refresh_every > 0 && fl[s] % a.refresh_every == 0) {
             // top-down recount; a plain overwrite that can only raise the threshold
-            const SuffixPick p = suffix_pick(hist + (2 * wave + s) * nbins, nbins, k);
-            if (half == s) thr = max(thr, p.bin);
+            const SuffixPick p = suffix_pick(hist + lq * nbins, nbins, k);
+            if (QPW == 1 || half == s) {
+                if (p.bin > thr) {
+                    thr = p.bin;
+                    tau = tau_of(thr, m.smin, m.delta, nbins);
+                }
+            }
         }
     };
 
-    if (k_lo < wave_end) {
-        HalfRow<DT, D> kf, kn;
-        zero_half_row<DT, D>(kn);
-        load_key<DT, D>(kf, a.k, min(k_lo + (lane & 31), a.L - 1));
-        float sk = 1.0f, skn = 1.0f;
-        if constexpr (DT == DT_FP8) sk = a.k_scale[min(k_lo + (lane & 31), a.L - 1)];
-        for (int kb = k_lo; kb < wave_end; kb += 32) {
-            const int nk = min(kb + 32 + (lane & 31), a.L - 1);
-            if (kb + 32 < wave_end) {
-                load_key<DT, D>(kn, a.k, nk);
-                if constexpr (DT == DT_FP8) skn = a.k_scale[nk];
-            }
-            float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-            if constexpr (DT == DT_FP8) I = I * sk;
-            const int key = kb + (lane & 31);
-            const int b = bin_of(I, m.smin, m.delta, nbins);
-            const bool pass = (key <= my_pos) && (b >= thr);
-            const uint64_t mask = __ballot(pass);
-            if (mask) {
+    auto process = [&](float I, int key) {
+        const bool pass = (key <= my_pos) && (I >= tau);
+        const uint64_t mask = __ballot(pass);
+        if (mask) {
+            if (pass) atomicAdd(&hist[qi * nbins + bin_of(I, m.smin, m.delta, nbins)], 1u);
+            if constexpr (QPW == 2) {
                 const uint32_t ma = (uint32_t)mask, mb = (uint32_t)(mask >> 32);
                 if (pass) {
-                    atomicAdd(&hist[qi * nbins + b], 1u);
                     const int rank = __popcll(mask & lt_mask & (half ? 0xffffffff00000000ull : 0xffffffffull));
-                    st_mine[(half ? cnt_b : cnt_a) + rank] = make_uint2((uint32_t)key, __float_as_uint(I));
+                    stage[qi * kStage + (half ? cnt[1] : cnt[0]) + rank] = make_uint2((uint32_t)key, __float_as_uint(I));
                 }
-                cnt_a += __popc(ma);
-                cnt_b += __popc(mb);
-                if (cnt_a >= kFlush) flush(0, cnt_a, fl_a);
-                if (cnt_b >= kFlush) flush(1, cnt_b, fl_b);
+                cnt[0] += __popc(ma);
+                cnt[1] += __popc(mb);
+                if (cnt[0] >= kFlush) flush(0);
+                if (cnt[1] >= kFlush) flush(1);
+            } else {
+                if (pass) stage[qi * kStage + cnt[0] + mbcnt(mask)] = make_uint2((uint32_t)key, __float_as_uint(I));
+                cnt[0] += __popcll(mask);
+                if (cnt[0] >= kFlush) flush(0);
             }
-            kf = kn;
-            sk = skn;
+        }
+    };
+
+    const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
+    if (ntiles > 0) load_tile<DT, D>(a, k_lo, tiles, wave, lane);
+    for (int it = 0; it < ntiles; ++it) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (it + 1 < ntiles) load_tile<DT, D>(a, k_lo + (it + 1) * G::TK, tiles + ((it + 1) & 1) * G::STAGE_BYTES, wave, lane);
+        const int key0 = k_lo + it * G::TK;
+        const uint8_t* st = tiles + (it & 1) * G::STAGE_BYTES;
+        const float* sks = reinterpret_cast<const float*>(st + kTileBytes);
+        if constexpr (QPW == 2) {
+#pragma unroll 1
+            for (int blk = 0; blk < G::TK / 32; ++blk) {
+                const int kb = key0 + 32 * blk;
+                if (kb >= wave_end) break;
+                HalfRow<DT, D> kf;
+                read_frag<DT, D>(kf, st, 32 * blk, lane);
+                float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+                if constexpr (DT == DT_FP8) I = I * sks[32 * blk + (lane & 31)];
+                process(I, kb + (lane & 31));
+            }
+        } else {
+#pragma unroll 1
+            for (int blk = 0; blk < G::TK / 64; ++blk) {
+                const int kb = key0 + 64 * blk;
+                if (kb >= wave_end) break;
+                // the two 32-key slots one after the other: only one slot's
+                // fragment and accumulators are live (same arithmetic as score_2slots)
+                HalfRow<DT, D> kf;
+                v16f acc[HB];
+                read_frag<DT, D>(kf, st, 64 * blk, lane);
+                mfma_1slot<DT, D, HB>(ra.q, kf, acc);
+                const float pa = relu_wsum<HB>(acc, ra.w);
+                read_frag<DT, D>(kf, st, 64 * blk + 32, lane);
+                mfma_1slot<DT, D, HB>(ra.q, kf, acc);
+                const float pb = relu_wsum<HB>(acc, ra.w);
+                float I = combine_halves(pa, pb);
+                if constexpr (DT == DT_FP8) I = I * sks[64 * blk + lane];
+                process(I, kb + lane);
+            }
         }
     }
     // final partial batches
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int cnt = s ? cnt_b : cnt_a;
-        if (cnt > 0) {
-            const int tq = s ? tb : ta;
+    for (int s = 0; s < QPW; ++s) {
+        if (cnt[s] > 0) {
+            const int tq = s0 + s;
             uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)cnt);
+            if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)cnt[s]);
             base = __shfl(base, 0);
-            if (lane < cnt) {
-                const uint2 e = stage[(2 * wave + s) * kStage + lane];
-                if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = e;
+            if (lane < cnt[s]) {
+                const uint2 en = stage[(QPW * wave + s) * kStage + lane];
+                if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = en;
             }
         }
     }
@@ -771,9 +903,13 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
-        const size_t scan_lds = (size_t)kQPG * a.nbins * 4 + (size_t)kQPG * kStage * 8;
+        constexpr int QPG = kScanWaves * ScanShape<DT_>::QPW;
+        const size_t scan_lds = 2 * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + (size_t)QPG * a.nbins * 4 +
+                                (size_t)QPG * kStage * 8;
         allow_lds(scan_kernel<DT_, D_, HB_>, scan_lds);
-        scan_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, scan_lds, st>>>(a);
+        if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
+        scan_kernel<DT_, D_, HB_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
+        if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
         const size_t fin_lds = (size_t)((std::max(a.nbins, 256) + 1) & ~1) * 4 + sort_lds(a);
         allow_lds(finalize_kernel, fin_lds);
         finalize_kernel<<<a.T, 256, fin_lds, st>>>(a);

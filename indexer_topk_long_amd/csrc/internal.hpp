@@ -13,7 +13,7 @@ constexpr int kQPG = 8;              // queries per workgroup (4 waves x 2 queri
 constexpr int kStage = 128;          // staging entries per query in LDS (>= 64 + 32)
 constexpr int kFlush = 64;           // write-back batch (one wave64 of 8-byte entries)
 constexpr int kDefaultBins = 256;
-constexpr int kMaxBins = 4096;
+constexpr int kMaxBins = 1024;
 constexpr int64_t kDefaultCcap = 16384;
 constexpr int64_t kDefaultCcapRetrieve = 131072;
 constexpr int kMaxSortedK = 8192;
@@ -73,6 +73,7 @@ struct IdxArgs {
     float* out_score;
     ltk_stats* stats;
     float* S;                // unfused: [T, L] score matrix
+    hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch
 };
 
 struct LaunchCfg {

@@ -1,0 +1,60 @@
+"""The five workloads at full size on the GPU, in the launch configuration the
+benchmark uses: sampled rows against the CPU oracle, every row against the
+unfused baseline (bit-identical sets and scores), structural checks on all
+rows, and the bytes written per query."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import canon, check_rows, say, to_dev
+from workloads import CONFIGS, indexer_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _prev_sample(lib, inp, d):
+    """The previous chunk (bootstrapped with a seeded random sample) through the
+    library, then its top-3k by selection count: the sample of this chunk."""
+    import torch
+    prev = dict(inp["prev"])
+    prev.update(k=inp["k"], k_scale=inp["k_scale"])
+    pd = to_dev(prev)
+    pidx = lib.score_select(pd["q"], d["k"], pd["w"], pd["pos"], inp["topk"], sample=pd["sample"],
+                            q_scale=pd["q_scale"], k_scale=d["k_scale"])
+    return lib.next_sample(pidx, inp["L"], 3 * inp["topk"]), torch
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_full_size_config(lib, cfg):
+    import torch
+    say(f"config {cfg}: generating")
+    inp = indexer_config(cfg, with_prev=True)
+    d = to_dev(inp)
+    sample, _ = _prev_sample(lib, inp, d)
+    T, L, k = inp["T"], inp["L"], inp["topk"]
+    say(f"config {cfg}: fused")
+    idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                   k_scale=d["k_scale"], return_scores=True, return_stats=True)
+    idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
+    # structure on every row: k distinct causal keys
+    s = np.sort(idx_h, axis=1)
+    assert np.all(s >= 0) and np.all(np.diff(s, axis=1) > 0)
+    assert np.all(s[:, -1] <= inp["pos"])
+    assert st.overflow_rows == 0
+    # at most 5x fewer bytes written than the full score matrix (4 L bytes per query)
+    bytes_q = (8.0 * st.cand_written + 4.0 * T * k) / T
+    say(f"config {cfg}: candidates/query {st.cand_written / T:.0f}, bytes/query {bytes_q:.0f} vs {4 * L}")
+    assert bytes_q * 5 <= 4 * L
+    # sampled rows against the oracle
+    rows = sorted(set([0, 1, T // 2, T - 2, T - 1] + list(np.random.default_rng(cfg).choice(T, 5, replace=False))))
+    say(f"config {cfg}: oracle rows {rows}")
+    check_rows(inp, idx_h, sc_h, rows, f"config {cfg}")
+    # every row against the unfused baseline
+    say(f"config {cfg}: unfused")
+    uidx, usc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                         k_scale=d["k_scale"], return_scores=True)
+    a, asc = canon(idx_h, sc_h)
+    b, bsc = canon(uidx.cpu().numpy(), usc.cpu().numpy())
+    del uidx, usc
+    torch.cuda.empty_cache()
+    assert np.array_equal(a, b)
+    assert np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))

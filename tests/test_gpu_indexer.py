@@ -102,7 +102,7 @@ def test_sample_bins_refresh_capacity_independence(lib):
     cases = []
     for name, smp in _variants(inp).items():
         cases.append((name, torch.from_numpy(smp).cuda(), None))
-    for nb in (1, 2, 7, 4096):
+    for nb in (1, 2, 7, 1024):
         cases.append((f"nbins{nb}", d["sample"], ltk.Opts(nbins=nb)))
     for r in (3, -1):
         cases.append((f"refresh{r}", d["sample"], ltk.Opts(refresh_every=r)))

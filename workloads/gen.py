@@ -56,13 +56,14 @@ def _unit(v: np.ndarray, axis: int = -1) -> np.ndarray:
     return v / np.linalg.norm(v, axis=axis, keepdims=True)
 
 
-def to_storage(x: np.ndarray, dtype: str, axes=None):
+def to_storage(x: np.ndarray, dtype: str, axes=None, inplace: bool = False):
     """Round fp32 values to the storage format ``dtype``.
 
     Returns ``(raw, scale)``: ``raw`` holds fp32 values, bf16 bit patterns
     (uint16) or e4m3fn bit patterns (uint8); ``scale`` is None except for fp8,
     where it is the fp32 per-token scale amax/448 over ``axes`` (so that no
-    value saturates) and ``raw`` encodes ``x / scale``.
+    value saturates) and ``raw`` encodes ``x / scale``.  With ``inplace`` the
+    fp8 path may overwrite ``x``.
     """
     import torch
 
@@ -71,14 +72,17 @@ def to_storage(x: np.ndarray, dtype: str, axes=None):
         return x, None
     if dtype == "bf16":
         t = torch.from_numpy(x).to(torch.bfloat16)
-        return t.view(torch.int16).numpy().view(np.uint16).copy(), None
+        return t.view(torch.int16).numpy().view(np.uint16), None
     if dtype == "fp8":
-        amax = np.abs(x).max(axis=axes, keepdims=True).astype(np.float32)
+        # amax without an |x| temporary (large arrays are costly to allocate)
+        amax = np.maximum(x.max(axis=axes, keepdims=True), -x.min(axis=axes, keepdims=True)).astype(np.float32)
         scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
         scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-        y = (x / scale).astype(np.float32)
-        t = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
-        raw = t.view(torch.uint8).numpy().copy()
+        if not inplace:
+            x = x.copy()
+        np.divide(x, scale, out=x)
+        t = torch.from_numpy(x).to(torch.float8_e4m3fn)
+        raw = t.view(torch.uint8).numpy()
         return raw, scale.reshape(-1).astype(np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
@@ -127,7 +131,9 @@ def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot:
         n_hot = min(n_hot, L)
         hot = np.sort(gh.choice(L, size=n_hot, replace=False)) if n_hot > 0 else np.zeros(0, np.int64)
         if n_hot:
-            k[hot] += (hot_gain * _u_at(hot, L, u0, u1, drift)).astype(np.float32)
+            for s0 in range(0, n_hot, 1 << 16):
+                h = hot[s0 : s0 + (1 << 16)]
+                k[h] += (hot_gain * _u_at(h, L, u0, u1, drift)).astype(np.float32)
 
     if pos is None:
         end = L + chunk * T
@@ -135,14 +141,17 @@ def indexer_inputs(T: int, L: int, H: int, D: int, dtype: str, topk: int, n_hot:
     pos = np.asarray(pos, dtype=np.int64)
     assert pos.shape == (T,)
     gq = _rng(tag, _S_QUERIES if chunk == 0 else _S_PREV_QUERIES + 16 * (-chunk - 1), seed)
-    q = gq.standard_normal((T, H, D), dtype=np.float32) / np.float32(math.sqrt(D))
+    q = gq.standard_normal((T, H, D), dtype=np.float32)
+    q /= np.float32(math.sqrt(D))
     q += (q_gain * _u_at(np.clip(pos, 0, L - 1), L, u0, u1, drift)).astype(np.float32)[:, None, :]
     gw = _rng(tag, _S_WEIGHTS + 16 * (-chunk), seed)
     w = gw.uniform(w_range[0], w_range[1], size=(T, H)).astype(np.float32)
 
-    q_raw, q_scale = to_storage(q, dtype, axes=(1, 2))
+    q_raw, q_scale = to_storage(q, dtype, axes=(1, 2), inplace=True)
+    del q
     if keys is None:
-        k_raw, k_scale = to_storage(k, dtype, axes=(1,))
+        k_raw, k_scale = to_storage(k, dtype, axes=(1,), inplace=True)
+        del k
     else:  # the same (already rounded) keys as another chunk of this context
         k_raw, k_scale, hot = keys
     out = dict(kind="indexer", T=T, L=L, H=H, D=D, dtype=dtype, topk=topk,
