@@ -85,7 +85,19 @@ def main():
     ap.add_argument("--unfused-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        n = args.copy_probe // 4
+        src = torch.arange(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {4 * n} bytes x 3")
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "

@@ -114,6 +114,14 @@ __device__ __forceinline__ void mfma_1slot(const HalfRow<DT, D> (&q)[HB], const 
 // the 32x32 MFMA result row held by (lane, r) is 8*(r/4) + 4*half + (r%4).
 __device__ __forceinline__ int head_of(int m, int r, int half) { return m * 32 + 8 * (r >> 2) + 4 * half + (r & 3); }
 
+// max(0, x) of a finite float as one integer max on its bits: the bit
+// pattern of a float read as int32 is negative exactly when the sign bit is
+// set, so negative values and -0 become +0 and the rest pass unchanged.  (A
+// float max would first quiet NaNs: two instructions per head instead of one.)
+__device__ __forceinline__ float relu_bits(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // sum over the lane's heads of w * max(0, x), in a fixed order
 template <int HB>
 __device__ __forceinline__ float relu_wsum(const v16f (&acc)[HB], const float (&w)[HB][16]) {
@@ -121,7 +129,7 @@ __device__ __forceinline__ float relu_wsum(const v16f (&acc)[HB], const float (&
 #pragma unroll
     for (int m = 0; m < HB; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[m][r], __builtin_fmaxf(acc[m][r], 0.0f), p);
+        for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[m][r], relu_bits(acc[m][r]), p);
     return p;
 }
 

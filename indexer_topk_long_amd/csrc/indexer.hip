@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 // ---------------------------------------------------------------------------
 //
 // One workgroup = 8 waves sharing K tiles that are streamed into LDS with
-// direct global->LDS loads (double-buffered, 32 KB of keys per tile), so the
+// direct global->LDS loads (three 32 KB stages: one computed, two loading), so the
 // eight waves read each key from device memory once.  fp8 waves own two
 // queries (one per 32-lane half, both scored against the same 32 keys);
 // bf16/fp32 waves own one query scored against two 32-key blocks.  Two waves
@@ -253,6 +253,7 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 
 constexpr int kScanWaves = 8;
 constexpr int kTileBytes = 32768;
+constexpr int kScanStages = 3;     // tiles in flight: compute one, two loading
 
 template <int DT> struct ScanShape { static constexpr int QPW = 1; };
 
@@ -267,13 +268,39 @@ struct TileGeom {
     static constexpr int STAGE_BYTES = kTileBytes + SCALE_BYTES;
     static_assert(NINST % kScanWaves == 0, "tile loads split evenly over the waves");
     static_assert(TK % 64 == 0, "per-key scales load in whole 64-lane wave loads");
+    static constexpr int SCALE_INST = (DT == DT_FP8) ? TK / 64 : 0;       // wave loads of scales per tile
+    static_assert(SCALE_INST <= kScanWaves, "at most one scale load per wave");
 };
 
-// XOR swizzle of the 16-byte chunks of a row, so that the 8 lanes served
-// together by a 128-bit LDS read (8 consecutive rows, same logical chunk)
-// hit distinct banks.
-template <int CPR>
-__device__ __forceinline__ int chunk_swz(int r) { return CPR >= 8 ? (r & 7) : ((r >> 1) & 3); }
+// Wait until at most n of this wave's vector-memory operations are in flight.
+// Vector-memory operations complete in issue order, so this means that
+// everything but the n most recent (the next tile's loads) has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else static_assert(N <= 9, "extend wait_vm");
+}
+
+// XOR swizzle of the 16-byte chunks of a row.  LDS serves a 128-bit read 16
+// lanes at a time from 64 four-byte banks (one 256-byte bank line); those 16
+// lanes read 16 consecutive rows at the same logical chunk, so the chunk index
+// is XORed with the row's position among the rows sharing a bank line slot,
+// making the 16 physical 16-byte slots distinct.
+template <int RB, int CPR>
+__device__ __forceinline__ int chunk_swz(int r) {
+    constexpr int RPL = (RB < 256) ? 256 / RB : 1;       // rows per 256-byte bank line
+    constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+    return (r / RPL) & MASK;
+}
 
 // Direct global -> LDS copies (gfx950 global_load_lds): every lane moves 16
 // (or 4) bytes, landing at lds + 16*lane (4*lane); lds must be wave-uniform.
@@ -293,7 +320,7 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* s
         const int inst = wave + j * kScanWaves;
         const int p = inst * 64 + lane;
         const int r = p / G::CPR, pc = p % G::CPR;
-        const int c = pc ^ chunk_swz<G::CPR>(r);
+        const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
         const int key = min(key0 + r, a.L - 1);
         lds_direct16(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
     }
@@ -314,7 +341,7 @@ __device__ __forceinline__ void read_frag(HalfRow<DT, D>& f, const uint8_t* st, 
 #pragma unroll
     for (int i = 0; i < HalfRow<DT, D>::NV; ++i) {
         const int c = h * (G::CPR / 2) + i;
-        f.v[i] = *reinterpret_cast<const u32x4*>(st + r * G::RB + ((c ^ chunk_swz<G::CPR>(r)) * 16));
+        f.v[i] = *reinterpret_cast<const u32x4*>(st + r * G::RB + ((c ^ chunk_swz<G::RB, G::CPR>(r)) * 16));
     }
 }
 
@@ -339,8 +366,8 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     constexpr int QPG = kScanWaves * QPW;
     extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
     const int nbins = a.nbins;
-    uint8_t* tiles = shm;                                                  // 2 stages
-    uint32_t* hist = reinterpret_cast<uint32_t*>(shm + 2 * G::STAGE_BYTES);  // [QPG][nbins]
+    uint8_t* tiles = shm;                                                  // kScanStages stages
+    uint32_t* hist = reinterpret_cast<uint32_t*>(shm + kScanStages * G::STAGE_BYTES);  // [QPG][nbins]
     uint2* stage = reinterpret_cast<uint2*>(hist + QPG * nbins);           // [QPG][kStage]
     const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
@@ -393,6 +420,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         if (lane < rem) st[lane] = r;
         cnt[s] = rem;
         ++fl[s];
+        wait_vm<0>();   // keep the in-flight vector-memory ops to tile loads only
         if (a.refresh_every > 0 && fl[s] % a.refresh_every == 0) {
             // top-down recount; a plain overwrite that can only raise the threshold
             const SuffixPick p = suffix_pick(hist + lq * nbins, nbins, k);
@@ -429,13 +457,25 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     };
 
     const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
+    constexpr int LPW_HI = G::PER_WAVE + (G::SCALE_INST > 0 ? 1 : 0);   // loads per tile, waves < SCALE_INST
+    constexpr int LPW_LO = G::PER_WAVE;                                  // loads per tile, other waves
     if (ntiles > 0) load_tile<DT, D>(a, k_lo, tiles, wave, lane);
+    if (ntiles > 1) load_tile<DT, D>(a, k_lo + G::TK, tiles + G::STAGE_BYTES, wave, lane);
+    int sbuf = 0;   // stage holding tile `it`
     for (int it = 0; it < ntiles; ++it) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (it + 1 < ntiles) {   // tile it+1 may still be loading
+            if (wave < G::SCALE_INST) wait_vm<LPW_HI>(); else wait_vm<LPW_LO>();
+        } else {
+            wait_vm<0>();
+        }
         __syncthreads();
-        if (it + 1 < ntiles) load_tile<DT, D>(a, k_lo + (it + 1) * G::TK, tiles + ((it + 1) & 1) * G::STAGE_BYTES, wave, lane);
+        if (it + 2 < ntiles) {
+            const int nb = (sbuf + 2) % kScanStages;
+            load_tile<DT, D>(a, k_lo + (it + 2) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
+        }
         const int key0 = k_lo + it * G::TK;
-        const uint8_t* st = tiles + (it & 1) * G::STAGE_BYTES;
+        const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
+        sbuf = (sbuf + 1) % kScanStages;
         const float* sks = reinterpret_cast<const float*>(st + kTileBytes);
         if constexpr (QPW == 2) {
 #pragma unroll 1
@@ -448,13 +488,13 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 if constexpr (DT == DT_FP8) I = I * sks[32 * blk + (lane & 31)];
                 process(I, kb + (lane & 31));
             }
-        } else {
+        } else if constexpr (HalfRow<DT, D>::NV > 4) {
+            // wide fragments (bf16/fp32 at D = 128): the two 32-key slots of a
+            // block one after the other, keeping one slot's registers live
 #pragma unroll 1
             for (int blk = 0; blk < G::TK / 64; ++blk) {
                 const int kb = key0 + 64 * blk;
                 if (kb >= wave_end) break;
-                // the two 32-key slots one after the other: only one slot's
-                // fragment and accumulators are live (same arithmetic as score_2slots)
                 HalfRow<DT, D> kf;
                 v16f acc[HB];
                 read_frag<DT, D>(kf, st, 64 * blk, lane);
@@ -466,6 +506,35 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 float I = combine_halves(pa, pb);
                 if constexpr (DT == DT_FP8) I = I * sks[64 * blk + lane];
                 process(I, kb + lane);
+            }
+        } else {
+            // 32-key slots, software-pipelined: the MFMAs of slot s+1 are issued
+            // before the ReLU*w reduction of slot s, so the matrix core and the
+            // VALU of one wave overlap; two slots make one 64-key block.
+            constexpr int NS = G::TK / 32;
+            HalfRow<DT, D> kf;
+            v16f accC[HB], accN[HB];
+            read_frag<DT, D>(kf, st, 0, lane);
+            mfma_1slot<DT, D, HB>(ra.q, kf, accC);
+            float pprev = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                if (sl + 1 < NS) {
+                    read_frag<DT, D>(kf, st, 32 * (sl + 1), lane);
+                    mfma_1slot<DT, D, HB>(ra.q, kf, accN);
+                }
+                const float p = relu_wsum<HB>(accC, ra.w);
+                if (sl & 1) {
+                    float I = combine_halves(pprev, p);
+                    if constexpr (DT == DT_FP8) I = I * sks[32 * (sl - 1) + lane];
+                    process(I, key0 + 32 * (sl - 1) + lane);
+                } else {
+                    pprev = p;
+                }
+                if (sl + 1 < NS) {
+#pragma unroll
+                    for (int m = 0; m < HB; ++m) accC[m] = accN[m];
+                }
             }
         }
     }
@@ -904,7 +973,7 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
         constexpr int QPG = kScanWaves * ScanShape<DT_>::QPW;
-        const size_t scan_lds = 2 * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + (size_t)QPG * a.nbins * 4 +
+        const size_t scan_lds = kScanStages * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + (size_t)QPG * a.nbins * 4 +
                                 (size_t)QPG * kStage * 8;
         allow_lds(scan_kernel<DT_, D_, HB_>, scan_lds);
         if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
