@@ -114,8 +114,10 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
  * serves vector retrieval; "Large-scale retrieval", k from 1,024).
  *
  *  q [T, D] queries, db [N, D] database rows, both dtype (LTK_BF16 only),
- *  D a multiple of 64 up to 1024, 1 <= N < 2^31; sample [n_sample] database
- *  rows used to estimate the score range.  Other arguments as above.
+ *  D in {64, 128, 256, 512, 768}, 1 <= N < 2^31; sample [n_sample] database
+ *  rows used to estimate the score range (duplicates and out-of-range
+ *  entries ignored).  opts->l_splits sets the number of database splits.
+ *  Other arguments as above.
  */
 int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype,
                       int32_t topk, const int32_t* sample, int32_t n_sample, int32_t* out_idx,

@@ -74,6 +74,9 @@ static int auto_splits(int nqg, int64_t L, int requested) {
 // Queries per scan workgroup: 8 waves x 1 query.
 static int scan_qpg(int) { return 8; }
 
+// Shared retrieval histograms: nbins fine counters + one per 16-bin super-bin, per query.
+static size_t retr_hist_words(int32_t T, int nbins) { return (size_t)T * (size_t)(nbins + (nbins + 15) / 16); }
+
 }  // namespace ltk
 
 using namespace ltk;
@@ -103,7 +106,7 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     (void)H; (void)D; (void)dtype;
     Opts o;
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? kDefaultCcapRetrieve : kDefaultCcap, o) != LTK_OK) return 0;
-    return ws_layout(T, L, n_sample, o.ccap).total;
+    return ws_layout(T, L, n_sample, o.ccap, kind == LTK_KIND_RETRIEVE ? retr_hist_words(T, o.nbins) : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -222,9 +225,80 @@ int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64
 int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype, int32_t topk,
                       const int32_t* sample, int32_t n_sample, int32_t* out_idx, float* out_score, void* ws,
                       size_t ws_bytes, const ltk_opts* opts, ltk_stats* stats, void* stream) {
-    (void)q; (void)db; (void)T; (void)D; (void)N; (void)dtype; (void)topk; (void)sample; (void)n_sample;
-    (void)out_idx; (void)out_score; (void)ws; (void)ws_bytes; (void)opts; (void)stats; (void)stream;
-    return LTK_EUNSUPPORTED;
+    if (T < 0 || N < 1 || N > (int64_t)0x7fffff00 || topk < 1 || topk > 65536 || n_sample < 0) return LTK_EINVAL;
+    if (dtype != LTK_BF16) return dtype < LTK_F32 || dtype > LTK_FP8_E4M3FN ? LTK_EINVAL : LTK_EUNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256 && D != 512 && D != 768) return LTK_EUNSUPPORTED;
+    if (n_sample > 0 && !sample) return LTK_EINVAL;
+    if (T > 0 && (!q || !db || !out_idx || !ws)) return LTK_EINVAL;
+    if (!aligned16(q) || !aligned16(db) || !aligned16(ws)) return LTK_EINVAL;
+    Opts o;
+    int st;
+    if ((st = resolve_opts(opts, kDefaultCcapRetrieve, o)) != LTK_OK) return st;
+    if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
+    const WsLayout lay = ws_layout(T, N, n_sample, o.ccap, retr_hist_words(T, o.nbins));
+    if (ws_bytes < lay.total) return LTK_EWORKSPACE;
+    if (T == 0) return LTK_OK;
+    if ((st = device_check()) != LTK_OK) return st;
+
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    // the sample pass, finalize and the shared kernels take the indexer's argument block
+    IdxArgs f{};
+    f.T = T;
+    f.H = 1;
+    f.L = (int)N;
+    f.topk = topk;
+    f.nbins = o.nbins;
+    f.n_sample = n_sample > 0 ? n_sample : 1;
+    f.sorted = o.sorted;
+    f.ccap = o.ccap;
+    f.pos = nullptr;   // no causal mask
+    f.tail = reinterpret_cast<uint32_t*>(wsb + lay.tail);
+    f.flags = reinterpret_cast<uint32_t*>(wsb + lay.flags);
+    f.nu = reinterpret_cast<uint32_t*>(wsb + lay.nu);
+    f.bitmap = reinterpret_cast<uint32_t*>(wsb + lay.bitmap);
+    f.meta = wsb + lay.meta;
+    f.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
+    f.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
+    f.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+    f.out_idx = out_idx;
+    f.out_score = out_score;
+    f.stats = stats;
+
+    RetrArgs r{};
+    r.q = static_cast<const uint8_t*>(q);
+    r.db = static_cast<const uint8_t*>(db);
+    r.T = T;
+    r.N = (int)N;
+    r.topk = topk;
+    r.nbins = o.nbins;
+    r.nsuper = (o.nbins + 15) / 16;
+    r.n_sample = f.n_sample;
+    r.n_qgroups = (T + 127) / 128;   // 4 waves x 32 queries per workgroup
+    // database splits: about 2048 workgroups, each >= 2048 rows
+    int ns = o.l_splits;
+    if (ns <= 0) {
+        ns = 1;
+        while ((int64_t)r.n_qgroups * ns < 2048 && N / ((int64_t)ns * 2) >= 2048) ns *= 2;
+    }
+    r.n_splits = ns;
+    r.sorted = o.sorted;
+    r.ccap = o.ccap;
+    r.tail = f.tail;
+    r.flags = f.flags;
+    r.nu = f.nu;
+    r.sample_u = f.sample_u;
+    r.sscore = f.sscore;
+    r.meta = f.meta;
+    r.cand = f.cand;
+    r.hist_g = reinterpret_cast<uint32_t*>(wsb + lay.hist);
+    r.hist_c = r.hist_g + (size_t)T * o.nbins;
+    r.out_idx = out_idx;
+    r.out_score = out_score;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_prepare_sample(f, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;
+    if (launch_retrieve(D, r, f, s) != hipSuccess) return LTK_EHIP;
+    return LTK_OK;
 }
 
 }  // extern "C"

@@ -23,11 +23,13 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace of one fused call.  The [zero_begin, zero_end) range is cleared
 // by the first kernel of every call.
 struct WsLayout {
-    size_t tail, flags, nu, bitmap, zero_begin, zero_end;
+    size_t tail, flags, nu, bitmap, hist, zero_begin, zero_end;
     size_t meta, sample_u, sscore, cand, total;
 };
 
-inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap) {
+// hist_words: 32-bit counters of the histograms shared across workgroups
+// (retrieval: T x (nbins + super-bins)); 0 for the indexer.
+inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0) {
     WsLayout w{};
     size_t o = 0;
     w.zero_begin = o;
@@ -35,6 +37,7 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap) 
     w.flags = o;  o = align_up(o + (size_t)T * 4, 256);
     w.nu = o;     o = align_up(o + 64, 256);
     w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
+    w.hist = o;   o = align_up(o + hist_words * 4, 256);
     w.zero_end = o;
     w.meta = o;     o = align_up(o + (size_t)T * sizeof(int32_t) * 4, 256);
     w.sample_u = o; o = align_up(o + (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
@@ -76,8 +79,26 @@ struct IdxArgs {
     hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch
 };
 
-struct LaunchCfg {
-    hipStream_t stream;
+// Everything a kernel of the fused retrieval path needs.
+struct RetrArgs {
+    const uint8_t* q;        // [T, D] bf16
+    const uint8_t* db;       // [N, D] bf16
+    int T, N, topk, nbins, nsuper;
+    int n_sample;            // row stride of sscore
+    int n_splits, n_qgroups; // database splits x query groups of 256
+    int sorted;
+    int64_t ccap;
+    uint32_t* tail;
+    uint32_t* flags;
+    const uint32_t* nu;
+    const int32_t* sample_u;
+    float* sscore;
+    void* meta;              // Meta[T]
+    uint2* cand;
+    uint32_t* hist_g;        // [T][nbins] shared fine histograms
+    uint32_t* hist_c;        // [T][nsuper] shared super-bin histograms
+    int32_t* out_idx;
+    float* out_score;
 };
 
 // Host launchers (return hipSuccess or the first launch error).
@@ -85,6 +106,9 @@ hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_
                                  uint8_t* ws, hipStream_t st);
 hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
 hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
+hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st);
+hipError_t launch_finalize(const IdxArgs& a, hipStream_t st);
+hipError_t launch_retrieve(int D, const RetrArgs& a, const IdxArgs& fin, hipStream_t st);
 hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
                               uint32_t* counts, hipStream_t st);
 

@@ -1,0 +1,214 @@
+// kernels_common.hpp -- device helpers shared by the indexer and retrieval kernels.
+#pragma once
+
+#include <math.h>
+
+#include "device.hpp"
+
+namespace ltk {
+
+// Wait until at most n of this wave's vector-memory operations are in flight.
+// Vector-memory operations complete in issue order, so this means that
+// everything but the n most recent (the next tile's loads) has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else static_assert(N <= 9, "extend wait_vm");
+}
+
+// XOR swizzle of the 16-byte chunks of a row.  LDS serves a 128-bit read 16
+// lanes at a time from 64 four-byte banks (one 256-byte bank line); those 16
+// lanes read 16 consecutive rows at the same logical chunk, so the chunk index
+// is XORed with the row's position among the rows sharing a bank line slot,
+// making the 16 physical 16-byte slots distinct.
+template <int RB, int CPR>
+__device__ __forceinline__ int chunk_swz(int r) {
+    constexpr int RPL = (RB < 256) ? 256 / RB : 1;       // rows per 256-byte bank line
+    constexpr int MASK = (CPR < 16 ? CPR : 16) - 1;
+    return (r / RPL) & MASK;
+}
+
+// Direct global -> LDS copies (gfx950 global_load_lds): every lane moves 16
+// (or 4) bytes, landing at lds + 16*lane (4*lane); lds must be wave-uniform.
+__device__ __forceinline__ void lds_direct16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_direct4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Smallest fp32 score whose bin is >= thr (bin_of is monotone), found by
+// bisection over the ordered float encoding: the gate I >= tau is then
+// exactly the gate bin_of(I) >= thr, and the bin is only computed for keys
+// that pass.
+__device__ __forceinline__ float tau_of(int thr, float smin, float delta, int nbins) {
+    if (thr <= 0) return -INFINITY;
+    uint32_t lo = ord_f32(-3.402823466e38f), hi = ord_f32(3.402823466e38f);   // bin(lo) < thr <= bin(hi)
+    while (hi - lo > 1u) {
+        const uint32_t mid = lo + ((hi - lo) >> 1);
+        if (bin_of(unord_f32(mid), smin, delta, nbins) >= thr) hi = mid; else lo = mid;
+    }
+    return unord_f32(hi);
+}
+
+// Block-wide bitonic sort (descending) of n <= cap 64-bit keys in LDS.
+__device__ inline void block_sort_desc(uint64_t* keys, int n) {
+    int p2 = 1;
+    while (p2 < n) p2 <<= 1;
+    for (int i = n + threadIdx.x; i < p2; i += blockDim.x) keys[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= p2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < p2 / 2; i += blockDim.x) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = ((lo & size) == 0);
+                const uint64_t x = keys[lo], y = keys[hi];
+                if ((x < y) == desc) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Order the k outputs of one row by (score desc, index asc).
+__device__ inline void sort_row_output(int32_t* out, float* osc, int k, uint64_t* keys) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        const int idx = out[i];
+        keys[i] = (idx >= 0) ? rank_key(osc ? osc[i] : 0.0f, idx) : 0ull;
+    }
+    // without scores, order by index only
+    if (!osc)
+        for (int i = threadIdx.x; i < k; i += blockDim.x)
+            keys[i] = (out[i] >= 0) ? (uint64_t)(0xffffffffu - (uint32_t)out[i]) + 1ull : 0ull;
+    __syncthreads();
+    block_sort_desc(keys, k);
+    for (int i = threadIdx.x; i < k; i += blockDim.x) {
+        const uint64_t key = keys[i];
+        if (key == 0ull) {
+            out[i] = -1;
+            if (osc) osc[i] = __builtin_nanf("");
+        } else if (osc) {
+            out[i] = (int32_t)(0xffffffffu - (uint32_t)key);
+            osc[i] = unord_f32((uint32_t)(key >> 32));
+        } else {
+            out[i] = (int32_t)(0xffffffffu - (uint32_t)(key - 1ull));
+        }
+    }
+    __syncthreads();
+}
+
+// Scores re-read from the materialised row (unfused baseline).
+struct MemSource {
+    const float* row;
+    __device__ __forceinline__ void get(int base, int nvalid, int& key, float& I, bool& valid) {
+        key = base + (int)threadIdx.x;
+        valid = key < nvalid;
+        I = valid ? row[key] : 0.0f;
+    }
+};
+
+template <class Src>
+__device__ void select_row(Src& src, int nvalid, int k, int32_t* out, float* osc, uint32_t* h256) {
+    __shared__ int s_pick;
+    __shared__ uint32_t s_above, s_ocnt, s_taken, s_wc[4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+    if (nvalid <= k) {   // every valid key is in the result
+        for (int base = 0; base < nvalid; base += 256) {
+            int key;
+            float I;
+            bool valid;
+            src.get(base, nvalid, key, I, valid);
+            if (valid) {
+                out[key] = key;
+                if (osc) osc[key] = I;
+            }
+        }
+        for (int i = max(nvalid, 0) + tid; i < k; i += 256) {
+            out[i] = -1;
+            if (osc) osc[i] = __builtin_nanf("");
+        }
+        return;
+    }
+    uint32_t P = 0u, mask = 0u, need = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        __syncthreads();
+        for (int i = tid; i < 256; i += 256) h256[i] = 0u;
+        __syncthreads();
+        for (int base = 0; base < nvalid; base += 256) {
+            int key;
+            float I;
+            bool valid;
+            src.get(base, nvalid, key, I, valid);
+            const uint32_t u = ord_f32(I);
+            if (valid && (u & mask) == P) atomicAdd(&h256[(u >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const SuffixPick p = suffix_pick(h256, 256, need);
+            if (lane == 0) {
+                s_pick = p.bin;
+                s_above = p.above;
+            }
+        }
+        __syncthreads();
+        P |= (uint32_t)s_pick << shift;
+        mask |= 0xffu << shift;
+        need -= s_above;
+    }
+    // P is now the k-th largest score; `need` of its ties are taken, lowest index first
+    const uint32_t ngt = (uint32_t)k - need;
+    if (tid == 0) {
+        s_ocnt = 0u;
+        s_taken = 0u;
+    }
+    __syncthreads();
+    for (int base = 0; base < nvalid; base += 256) {
+        int key;
+        float I;
+        bool valid;
+        src.get(base, nvalid, key, I, valid);
+        const uint32_t u = ord_f32(I);
+        const bool gt = valid && u > P;
+        const bool eq = valid && u == P;
+        if (gt) {
+            const uint32_t p = atomicAdd(&s_ocnt, 1u);
+            if (p < ngt) {
+                out[p] = key;
+                if (osc) osc[p] = I;
+            }
+        }
+        const uint64_t em = __ballot(eq);
+        if (lane == 0) s_wc[wave] = (uint32_t)__popcll(em);
+        __syncthreads();
+        uint32_t before = s_taken, total = 0;
+        for (int w = 0; w < 4; ++w) {
+            if (w < wave) before += s_wc[w];
+            total += s_wc[w];
+        }
+        if (eq) {
+            const uint32_t rank = before + (uint32_t)mbcnt(em);
+            if (rank < need) {
+                out[ngt + rank] = key;
+                if (osc) osc[ngt + rank] = I;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) s_taken += total;
+    }
+}
+
+}  // namespace ltk

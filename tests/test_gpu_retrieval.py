@@ -1,0 +1,95 @@
+"""GPU parity of the fused retrieval path (inner-product top-k) against the
+CPU oracle, and bit-exact independence from sample, bins, splits and capacity."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import canon, check_row, say
+from workloads import retrieval_config, retrieval_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _q_dev(r):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(r["q"]).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _db_host_bits(db):
+    import torch
+    return db.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _check(r, idx, sc, rows, where):
+    from oracle import retrieval_row_scores
+    dbh = _db_host_bits(r["db"])
+    N = r["N"]
+    v = np.arange(N)
+    swaps = 0
+    for t in rows:
+        s = retrieval_row_scores(r["q"], dbh, int(t))
+        swaps += check_row(idx[t], None if sc is None else sc[t], v, s, r["topk"], "bf16", f"{where} row {t}") or 0
+    return swaps
+
+
+SMALL = [(40, 5000, 64, 100), (33, 7001, 128, 64), (20, 3000, 768, 50), (70, 4500, 256, 300), (9, 2100, 512, 2000)]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"T{s[0]}_N{s[1]}_D{s[2]}_k{s[3]}")
+def test_retrieval_small(lib, shape):
+    import torch
+    T, N, D, k = shape
+    say("retrieval small", shape)
+    r = retrieval_inputs(T, N, D, k, n_centres=max(2, N // 400), sigma=0.3, n_sample=3 * k if 3 * k < N else N // 2,
+                         device="cuda", block=4096)
+    q = _q_dev(r)
+    smp = torch.from_numpy(r["sample"]).cuda()
+    idx, sc = lib.retrieve(q, r["db"], k, sample=smp, return_scores=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    _check(r, idx, sc, range(T), f"retrieve {shape}")
+
+
+def test_retrieval_independence(lib):
+    import torch
+    import indexer_topk_long_amd as ltk
+    T, N, D, k = 45, 9000, 128, 80
+    r = retrieval_inputs(T, N, D, k, n_centres=20, sigma=0.3, n_sample=240, device="cuda", block=4096)
+    q = _q_dev(r)
+    smp = torch.from_numpy(r["sample"]).cuda()
+    ref, ref_sc = canon(*[x.cpu().numpy() for x in lib.retrieve(q, r["db"], k, sample=smp, return_scores=True)])
+    _check(r, *[x.cpu().numpy() for x in lib.retrieve(q, r["db"], k, sample=smp, return_scores=True)], range(T), "ref")
+    cases = [
+        ("empty_sample", torch.zeros(0, dtype=torch.int32, device="cuda"), None),
+        ("dups_invalid", torch.tensor([5, 5, 5, -1, N, N + 9, 17, 17], dtype=torch.int32, device="cuda"), None),
+        ("nbins1", smp, ltk.Opts(nbins=1)),
+        ("nbins1024", smp, ltk.Opts(nbins=1024)),
+        ("splits1", smp, ltk.Opts(l_splits=1)),
+        ("splits7", smp, ltk.Opts(l_splits=7)),
+        ("ccap1", smp, ltk.Opts(cand_capacity=1)),
+        ("ccap100", smp, ltk.Opts(cand_capacity=100)),
+        ("sorted", smp, ltk.Opts(sorted_output=True)),
+    ]
+    for name, s_, o in cases:
+        say("variant", name)
+        got, got_sc = canon(*[x.cpu().numpy() for x in lib.retrieve(q, r["db"], k, sample=s_, opts=o, return_scores=True)])
+        assert np.array_equal(got, ref), name
+        assert np.array_equal(got_sc.view(np.uint32), ref_sc.view(np.uint32)), name
+
+
+def test_retrieval_full_size(lib):
+    """The 8M x 768 retrieval workload at full size: sampled queries against the
+    oracle, structure and candidate counts on every query."""
+    import torch
+    say("config 4: generating on the GPU")
+    r = retrieval_config(4, device="cuda")
+    T, N, k = r["T"], r["N"], r["topk"]
+    q = _q_dev(r)
+    smp = torch.from_numpy(r["sample"]).cuda()
+    say("config 4: fused")
+    idx, sc, st = lib.retrieve(q, r["db"], k, sample=smp, return_scores=True, return_stats=True)
+    idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
+    s = np.sort(idx_h, axis=1)
+    assert np.all(s >= 0) and np.all(np.diff(s, axis=1) > 0) and np.all(s < N)
+    say(f"config 4: candidates/query {st.cand_written / T:.0f}, max {st.max_cand_per_query}, overflow rows {st.overflow_rows}")
+    rows = [0, 1, 511, 1022, 1023] + list(np.random.default_rng(4).choice(T, 3, replace=False))
+    say(f"config 4: oracle rows {rows}")
+    _check(r, idx_h, sc_h, rows, "config 4")
