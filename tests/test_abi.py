@@ -1,0 +1,120 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, the header is plain C with the struct layout the binding
+uses, and every argument error is reported before any device call."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import indexer_topk_long_amd as ltk
+from indexer_topk_long_amd import build as B
+
+OK, EINVAL, EUNSUP, EWS, EHIP = 0, -1, -2, -3, -4
+F32, BF16, FP8 = 0, 1, 2
+P = ctypes.c_void_p
+A16 = P(0x10000)          # a 16-byte-aligned fake device address (never dereferenced)
+MIS = P(0x10004)          # a misaligned one
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.lib_path()):
+        B.build()
+    return ltk.library()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = ltk.exported_symbols()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_header_is_c_and_matches_binding_layout(tmp_path):
+    src = tmp_path / "probe.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "litetopk.h"\n'
+        'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(ltk_opts), offsetof(ltk_opts, cand_capacity),'
+        ' offsetof(ltk_opts, scan_event_stop), sizeof(ltk_stats), offsetof(ltk_stats, overflow_rows)); return 0;}\n')
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", B.INCLUDE, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    from indexer_topk_long_amd._binding import _COpts
+    assert got[0] == ctypes.sizeof(_COpts)
+    assert got[1] == _COpts.cand_capacity.offset and got[2] == _COpts.scan_event_stop.offset
+    assert got[3] == 16 and got[4] == 12     # Stats: u64 + u32 + u32, read as two int64 by the binding
+
+
+def test_strerror(L):
+    for code in (OK, EINVAL, EUNSUP, EWS, EHIP):
+        assert len(ltk.strerror(code)) >= 2 and ltk.strerror(code) != "unknown status"
+    assert ltk.strerror(12345) == "unknown status"
+
+
+def test_workspace_sizes(L):
+    ws = lambda *a: ltk.workspace_bytes(*a)
+    a = ws(0, 64, 4, 64, 4096, 256, 768, F32)
+    b = ws(0, 128, 4, 64, 4096, 256, 768, F32)
+    c = ws(0, 64, 4, 64, 4096, 256, 1536, F32)
+    assert 0 < a < b and a < c
+    assert 100 * 1000 * 4 <= ws(2, 100, 4, 64, 1000, 10, 0, F32) < 100 * 1000 * 4 + 256
+    assert ws(1, 1024, 1, 768, 8_000_000, 1024, 3072, BF16) > 1024 * 131072 * 8
+    assert ws(0, -1, 4, 64, 4096, 256, 0, F32) == 0 and ws(0, 4, 4, 64, 0, 256, 0, F32) == 0
+    assert ws(0, 4, 4, 64, 100, 256, 0, F32, ltk.Opts(nbins=5000)) == 0
+    # config 3 workspace: candidates (8192 x 16384 x 8 B) dominate, about the pages' 1.5 GB of auxiliary memory
+    assert 1.0e9 < ws(0, 8192, 64, 128, 1 << 20, 2048, 6144, FP8) < 1.6e9
+
+
+def _ss(L, **kw):
+    a = dict(q=A16, qs=None, k=A16, ks=None, w=A16, pos=A16, T=4, H=4, D=64, Lk=100, dt=F32, topk=8,
+             sample=None, ns=0, out=A16, osc=None, ws=A16, wsb=1 << 30, opts=None, stats=None, stream=None)
+    a.update(kw)
+    o = a["opts"].c() if a["opts"] is not None else None
+    return L.litetopk_score_select(a["q"], a["qs"], a["k"], a["ks"], a["w"], a["pos"], a["T"], a["H"], a["D"],
+                                   a["Lk"], a["dt"], a["topk"], a["sample"], a["ns"], a["out"], a["osc"], a["ws"],
+                                   a["wsb"], ctypes.byref(o) if o is not None else None, a["stats"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(H=0), EUNSUP), (dict(H=65), EUNSUP), (dict(D=96), EUNSUP),
+    (dict(dt=7), EINVAL), (dict(topk=0), EINVAL), (dict(topk=65537), EINVAL), (dict(Lk=0), EINVAL),
+    (dict(q=None), EINVAL), (dict(k=None), EINVAL), (dict(w=None), EINVAL), (dict(pos=None), EINVAL),
+    (dict(out=None), EINVAL), (dict(ws=None), EINVAL), (dict(q=MIS), EINVAL), (dict(k=MIS), EINVAL),
+    (dict(ws=MIS), EINVAL), (dict(dt=FP8), EINVAL), (dict(dt=FP8, qs=A16), EINVAL), (dict(qs=A16), EINVAL),
+    (dict(ns=3), EINVAL), (dict(ns=-1), EINVAL), (dict(wsb=100), EWS),
+    (dict(opts=ltk.Opts(nbins=1025)), EINVAL), (dict(opts=ltk.Opts(l_splits=-2)), EINVAL),
+    (dict(opts=ltk.Opts(sorted_output=True), topk=9000), EINVAL), (dict(opts=ltk.Opts(cand_capacity=-5)), EINVAL),
+    (dict(T=0), OK),
+])
+def test_score_select_argument_errors(L, kw, code):
+    assert _ss(L, **kw) == code
+
+
+def _rt(L, **kw):
+    a = dict(q=A16, db=A16, T=4, D=128, N=1000, dt=BF16, topk=8, sample=None, ns=0, out=A16, osc=None, ws=A16,
+             wsb=1 << 30, opts=None, stats=None, stream=None)
+    a.update(kw)
+    return L.litetopk_retrieve(a["q"], a["db"], a["T"], a["D"], a["N"], a["dt"], a["topk"], a["sample"], a["ns"],
+                               a["out"], a["osc"], a["ws"], a["wsb"], None, a["stats"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=FP8), EUNSUP), (dict(dt=F32), EUNSUP), (dict(dt=9), EINVAL), (dict(D=100), EUNSUP),
+    (dict(D=1024), EUNSUP), (dict(N=0), EINVAL), (dict(topk=0), EINVAL), (dict(db=None), EINVAL),
+    (dict(db=MIS), EINVAL), (dict(ns=5), EINVAL), (dict(wsb=10), EWS), (dict(T=0), OK),
+])
+def test_retrieve_argument_errors(L, kw, code):
+    assert _rt(L, **kw) == code
+
+
+def test_unfused_and_next_sample_argument_errors(L):
+    f = L.litetopk_unfused_score_select
+    assert f(A16, None, A16, None, A16, A16, 4, 4, 64, 100, F32, 8, A16, None, A16, 10, None) == EWS
+    assert f(A16, None, A16, None, A16, A16, 4, 4, 64, 100, FP8, 8, A16, None, A16, 1 << 20, None) == EINVAL
+    assert f(A16, None, A16, None, A16, A16, 0, 4, 64, 100, F32, 8, A16, None, A16, 0, None) == OK
+    ns = L.litetopk_next_sample
+    ns.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
+    assert ns(A16, 4, 8, 100, 101, A16, A16, 400, None) == EINVAL      # more samples than keys
+    assert ns(A16, 4, 8, 100, 10, A16, A16, 399, None) == EWS
+    assert ns(A16, 4, 8, 100, 0, A16, A16, 0, None) == OK
