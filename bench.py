@@ -14,7 +14,7 @@ carries the roofline of the dominant kernel (the fused scan, timed with HIP
 events on its stream), the unfused full-matrix baseline timed the same way,
 bytes written per query, and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--config 3]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload prefill-1m-fp8]
 """
 from __future__ import annotations
 
@@ -28,6 +28,13 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+# HBM-side bytes per launch of the fused scan at the 1M-context workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings
+# (profiles/scan_kernel_prefill-1m-fp8.md).  Valid only for the kernel sources
+# with this digest; reported as null otherwise.
+SCAN_TRAFFIC = {"digest": "2b17e0a8e38ebba6", "workload": "prefill-1m-fp8", "bytes": 4.554e9 + 1.555e8}
+KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
@@ -57,6 +64,15 @@ def to_dev(inp, torch):
     return d
 
 
+def scan_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "indexer_topk_long_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def cpu_baseline(inp, n_rows: int):
     """The CPU oracle, as it stands, on n_rows query rows spread over the chunk."""
     from oracle import oracle_indexer
@@ -81,7 +97,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=3, help="indexer workload 0-3 (3 = the 1M-context chunk)")
+    ap.add_argument("--workload", default="prefill-1m-fp8", help="indexer workload name (default: the 1M-context chunk)")
     ap.add_argument("--unfused-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,12 +122,12 @@ def main():
 
     import torch
     import indexer_topk_long_amd as ltk
-    from workloads import CONFIGS, indexer_config
+    from workloads import WORKLOADS, indexer_workload
 
-    cfg = CONFIGS[args.config]
+    cfg = WORKLOADS[args.workload]
     log(f"generating workload {cfg['name']} ...")
     t0 = time.perf_counter()
-    inp = indexer_config(args.config, with_prev=True)
+    inp = indexer_workload(args.workload, with_prev=True)
     log(f"  generated in {time.perf_counter() - t0:.1f} s")
     T, L, H, D, k = inp["T"], inp["L"], inp["H"], inp["D"], inp["topk"]
     d = to_dev(inp, torch)
@@ -201,12 +217,14 @@ def main():
         "vs_baseline": None,
         "dtype": inp["dtype"],
         "data": "synthetic (seeded concentrated-score generator; previous-chunk sample)",
-        "config": {"workload": f"{cfg['name']}: T={T} queries at positions {int(pos[0])}..{int(pos[-1])}, "
+        "config": {"workload": f"{args.workload}: T={T} queries at positions {int(pos[0])}..{int(pos[-1])}, "
                                f"L={L} causal keys, H={H}, D={D}, {inp['dtype']}, k={k}, "
                                f"sample=previous chunk top-{n_sample}",
                    "T": T, "L": L, "H": H, "D": D, "topk": k, "n_sample": n_sample, "pairs": pairs},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": (SCAN_TRAFFIC["bytes"] if scan_source_digest() == SCAN_TRAFFIC["digest"]
+                                 and args.workload == SCAN_TRAFFIC["workload"] else None),
                      "kernel": "scan_kernel (fused score + filter)", "kernel_ms": round(scan_ms, 4),
                      "algorithmic_flops_per_launch": flops},
         "bytes_written_per_query": round(bytes_q, 1),

@@ -62,7 +62,7 @@ def test_workspace_sizes(L):
     assert ws(1, 1024, 1, 768, 8_000_000, 1024, 3072, BF16) > 1024 * 131072 * 8
     assert ws(0, -1, 4, 64, 4096, 256, 0, F32) == 0 and ws(0, 4, 4, 64, 0, 256, 0, F32) == 0
     assert ws(0, 4, 4, 64, 100, 256, 0, F32, ltk.Opts(nbins=5000)) == 0
-    # config 3 workspace: candidates (8192 x 16384 x 8 B) dominate, about the pages' 1.5 GB of auxiliary memory
+    # 1M-context fp8 chunk workspace: candidates (8192 x 16384 x 8 B) dominate, about the pages' 1.5 GB of auxiliary memory
     assert 1.0e9 < ws(0, 8192, 64, 128, 1 << 20, 2048, 6144, FP8) < 1.6e9
 
 

@@ -3,19 +3,19 @@ import numpy as np
 import pytest
 
 from oracle import decode, indexer_row_scores, oracle_indexer
-from workloads import CONFIGS, indexer_config, indexer_inputs, retrieval_inputs, to_storage
+from workloads import WORKLOADS, indexer_inputs, indexer_workload, retrieval_inputs, to_storage
 
 
-def test_config0_shapes():
-    inp = indexer_config(0)
-    c = CONFIGS[0]
+def test_tiny_workload_shapes():
+    inp = indexer_workload("tiny-4k-fp32")
+    c = WORKLOADS["tiny-4k-fp32"]
     assert inp["q"].shape == (c["T"], c["H"], c["D"]) and inp["q"].dtype == np.float32
     assert inp["k"].shape == (c["L"], c["D"])
     assert inp["w"].shape == (c["T"], c["H"]) and inp["w"].min() >= 0.5 and inp["w"].max() <= 1.0
     assert inp["pos"].tolist() == list(range(4032, 4096))
     assert len(inp["hot"]) == 128 and len(np.unique(inp["hot"])) == 128
     assert len(inp["sample"]) == 768 and len(np.unique(inp["sample"])) == 768
-    prev = indexer_config(0, chunk=-1)
+    prev = indexer_workload("tiny-4k-fp32", chunk=-1)
     assert prev["pos"].tolist() == list(range(3968, 4032))
     assert np.array_equal(prev["k"], inp["k"]) and not np.array_equal(prev["q"], inp["q"])
 
@@ -56,13 +56,13 @@ def test_fp8_scales_per_token():
 def test_score_concentration_and_chunk_overlap():
     """Most scores sit in a narrow band far below the top (the curse-of-dimensionality
     concentration the method exploits); adjacent chunks share top sets."""
-    inp = indexer_config(0)
+    inp = indexer_workload("tiny-4k-fp32")
     v, s = indexer_row_scores(inp, 0)
     kth = np.sort(s)[-inp["topk"]]
     assert np.percentile(s, 90) < kth < s.max()
     assert (np.percentile(s, 75) - np.percentile(s, 25)) < 0.25 * (s.max() - np.percentile(s, 25))
     cur, _ = oracle_indexer(inp, rows=[0, 63])
-    prev, _ = oracle_indexer(indexer_config(0, chunk=-1))
+    prev, _ = oracle_indexer(indexer_workload("tiny-4k-fp32", chunk=-1))
     cnt = np.bincount(prev[prev >= 0].ravel(), minlength=inp["L"])
     top3k = np.lexsort((np.arange(inp["L"]), -cnt))[: 3 * inp["topk"]]
     for row in cur:                        # the previous chunk's top-3k covers most of this top-k

@@ -1,12 +1,12 @@
-"""The five workloads at full size on the GPU, in the launch configuration the
-benchmark uses: sampled rows against the CPU oracle, every row against the
+"""The prefill workloads at full size on the GPU, launched as the benchmark
+launches them: sampled rows against the CPU oracle, every row against the
 unfused baseline (bit-identical sets and scores), structural checks on all
 rows, and the bytes written per query."""
 import numpy as np
 import pytest
 
 from tests.gpu_util import canon, check_rows, say, to_dev
-from workloads import CONFIGS, indexer_config
+from workloads import indexer_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -23,15 +23,15 @@ def _prev_sample(lib, inp, d):
     return lib.next_sample(pidx, inp["L"], 3 * inp["topk"]), torch
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
-def test_full_size_config(lib, cfg):
+@pytest.mark.parametrize("name", ["prefill-64k-bf16", "prefill-256k-bf16", "prefill-1m-fp8"])
+def test_full_size_prefill(lib, name):
     import torch
-    say(f"config {cfg}: generating")
-    inp = indexer_config(cfg, with_prev=True)
+    say(f"{name}: generating")
+    inp = indexer_workload(name, with_prev=True)
     d = to_dev(inp)
     sample, _ = _prev_sample(lib, inp, d)
     T, L, k = inp["T"], inp["L"], inp["topk"]
-    say(f"config {cfg}: fused")
+    say(f"{name}: fused")
     idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
                                    k_scale=d["k_scale"], return_scores=True, return_stats=True)
     idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
@@ -42,14 +42,14 @@ def test_full_size_config(lib, cfg):
     assert st.overflow_rows == 0
     # at most 5x fewer bytes written than the full score matrix (4 L bytes per query)
     bytes_q = (8.0 * st.cand_written + 4.0 * T * k) / T
-    say(f"config {cfg}: candidates/query {st.cand_written / T:.0f}, bytes/query {bytes_q:.0f} vs {4 * L}")
+    say(f"{name}: candidates/query {st.cand_written / T:.0f}, bytes/query {bytes_q:.0f} vs {4 * L}")
     assert bytes_q * 5 <= 4 * L
     # sampled rows against the oracle
-    rows = sorted(set([0, 1, T // 2, T - 2, T - 1] + list(np.random.default_rng(cfg).choice(T, 5, replace=False))))
-    say(f"config {cfg}: oracle rows {rows}")
-    check_rows(inp, idx_h, sc_h, rows, f"config {cfg}")
+    rows = sorted(set([0, 1, T // 2, T - 2, T - 1] + list(np.random.default_rng(len(name)).choice(T, 5, replace=False))))
+    say(f"{name}: oracle rows {rows}")
+    check_rows(inp, idx_h, sc_h, rows, name)
     # every row against the unfused baseline
-    say(f"config {cfg}: unfused")
+    say(f"{name}: unfused")
     uidx, usc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
                                          k_scale=d["k_scale"], return_scores=True)
     a, asc = canon(idx_h, sc_h)

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import canon, check_rows, say, to_dev
-from workloads import indexer_config, indexer_inputs, random_sample
+from workloads import indexer_inputs, indexer_workload, random_sample
 
 pytestmark = pytest.mark.gpu
 
@@ -23,27 +23,27 @@ def _run_unfused(lib, d, topk):
 
 
 @pytest.fixture(scope="module")
-def cfg0():
-    return indexer_config(0)
+def tiny():
+    return indexer_workload("tiny-4k-fp32")
 
 
 def test_device_is_gfx950(lib):
     assert lib.device_check() == 0
 
 
-def test_unfused_config0_vs_oracle(lib, cfg0):
-    say("unfused config 0")
-    d = to_dev(cfg0)
-    idx, sc = _run_unfused(lib, d, cfg0["topk"])
-    check_rows(cfg0, idx, sc, range(cfg0["T"]), "unfused cfg0")
+def test_unfused_tiny_vs_oracle(lib, tiny):
+    say("unfused tiny-4k-fp32")
+    d = to_dev(tiny)
+    idx, sc = _run_unfused(lib, d, tiny["topk"])
+    check_rows(tiny, idx, sc, range(tiny["T"]), "unfused tiny")
 
 
-def test_fused_config0_vs_oracle_and_unfused(lib, cfg0):
-    say("fused config 0")
-    d = to_dev(cfg0)
-    idx, sc = _run_fused(lib, d, cfg0["topk"])
-    check_rows(cfg0, idx, sc, range(cfg0["T"]), "fused cfg0")
-    uidx, usc = _run_unfused(lib, d, cfg0["topk"])
+def test_fused_tiny_vs_oracle_and_unfused(lib, tiny):
+    say("fused tiny-4k-fp32")
+    d = to_dev(tiny)
+    idx, sc = _run_fused(lib, d, tiny["topk"])
+    check_rows(tiny, idx, sc, range(tiny["T"]), "fused tiny")
+    uidx, usc = _run_unfused(lib, d, tiny["topk"])
     a, asc = canon(idx, sc)
     b, bsc = canon(uidx, usc)
     assert np.array_equal(a, b)
@@ -159,11 +159,11 @@ def test_sorted_output(lib):
     check_rows(inp, idx, sc, range(10), "sorted")
 
 
-def test_determinism(lib, cfg0):
-    d = to_dev(cfg0)
-    a = _run_fused(lib, d, cfg0["topk"])
+def test_determinism(lib, tiny):
+    d = to_dev(tiny)
+    a = _run_fused(lib, d, tiny["topk"])
     for _ in range(5):
-        b = _run_fused(lib, d, cfg0["topk"])
+        b = _run_fused(lib, d, tiny["topk"])
         assert np.array_equal(canon(a[0]), canon(b[0]))
 
 

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import canon, check_row, say
-from workloads import retrieval_config, retrieval_inputs
+from workloads import retrieval_inputs, retrieval_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -79,17 +79,17 @@ def test_retrieval_full_size(lib):
     """The 8M x 768 retrieval workload at full size: sampled queries against the
     oracle, structure and candidate counts on every query."""
     import torch
-    say("config 4: generating on the GPU")
-    r = retrieval_config(4, device="cuda")
+    say("retrieval-8m-d768-bf16: generating on the GPU")
+    r = retrieval_workload(device="cuda")
     T, N, k = r["T"], r["N"], r["topk"]
     q = _q_dev(r)
     smp = torch.from_numpy(r["sample"]).cuda()
-    say("config 4: fused")
+    say("retrieval-8m-d768-bf16: fused")
     idx, sc, st = lib.retrieve(q, r["db"], k, sample=smp, return_scores=True, return_stats=True)
     idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
     s = np.sort(idx_h, axis=1)
     assert np.all(s >= 0) and np.all(np.diff(s, axis=1) > 0) and np.all(s < N)
-    say(f"config 4: candidates/query {st.cand_written / T:.0f}, max {st.max_cand_per_query}, overflow rows {st.overflow_rows}")
+    say(f"retrieval-8m-d768-bf16: candidates/query {st.cand_written / T:.0f}, max {st.max_cand_per_query}, overflow rows {st.overflow_rows}")
     rows = [0, 1, 511, 1022, 1023] + list(np.random.default_rng(4).choice(T, 3, replace=False))
-    say(f"config 4: oracle rows {rows}")
-    _check(r, idx_h, sc_h, rows, "config 4")
+    say(f"retrieval-8m-d768-bf16: oracle rows {rows}")
+    _check(r, idx_h, sc_h, rows, "retrieval-8m")

@@ -6,13 +6,13 @@ import pytest
 
 from oracle import indexer_row_scores, oracle_indexer, topk_row
 from oracle.model import sfs_row, threshold_from_hist
-from workloads import indexer_config, random_sample
+from workloads import indexer_workload, random_sample
 
 
 @pytest.fixture(scope="module")
 def cfg0():
-    inp = indexer_config(0)
-    prev = indexer_config(0, chunk=-1)
+    inp = indexer_workload("tiny-4k-fp32")
+    prev = indexer_workload("tiny-4k-fp32", chunk=-1)
     pi, _ = oracle_indexer(prev)
     L = inp["L"]
     cnt = np.bincount(pi[pi >= 0].ravel(), minlength=L)

@@ -7,7 +7,7 @@ import pytest
 
 import oracle as O
 from tests import oracle_pins as P
-from workloads import indexer_config, indexer_inputs
+from workloads import indexer_inputs, indexer_workload
 
 
 @pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda f: f.__name__)
@@ -15,8 +15,8 @@ def test_pin(check):
     check(O)
 
 
-def test_invariant_config0():
-    inp = indexer_config(0)
+def test_invariant_tiny_workload():
+    inp = indexer_workload("tiny-4k-fp32")
     P.check_invariant_on_workload(O, inp, range(inp["T"]))
 
 
@@ -27,7 +27,7 @@ def test_invariant_small_bf16_fp8():
 
 
 def test_oracle_rows_subset_consistent():
-    inp = indexer_config(0)
+    inp = indexer_workload("tiny-4k-fp32")
     full, _ = O.oracle_indexer(inp)
     rows = [3, 17, 63]
     part, _ = O.oracle_indexer(inp, rows=rows)

@@ -4,11 +4,12 @@ Nothing in this package scores, bins or selects: it draws random numbers and
 rounds them to the storage formats the kernels read.
 """
 from .gen import (  # noqa: F401
-    CONFIGS,
-    indexer_config,
+    INDEXER_WORKLOADS,
+    WORKLOADS,
+    indexer_workload,
     indexer_inputs,
     random_sample,
-    retrieval_config,
+    retrieval_workload,
     retrieval_inputs,
     to_storage,
 )

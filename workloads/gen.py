@@ -29,21 +29,22 @@ SEED_BASE = 20260713
 _S_KEYS, _S_HOT, _S_QUERIES, _S_WEIGHTS, _S_SAMPLE, _S_PREV_QUERIES, _S_DB = 0, 1, 2, 3, 4, 5, 6
 _S_DIR = 7
 
-# The five workloads.  Index 0 is small enough for the oracle to finish in
-# seconds; 1-3 are the indexer prefill chunks at 64K / 256K / 1M context;
-# 4 is the retrieval workload.
-CONFIGS = {
-    0: dict(kind="indexer", name="tiny-4k-fp32", T=64, L=4096, H=4, D=64, dtype="f32",
-            topk=256, n_hot=128, drift=False, w_range=(0.5, 1.0), n_sample=768),
-    1: dict(kind="indexer", name="prefill-64k-bf16", T=2048, L=65536, H=64, D=128, dtype="bf16",
-            topk=2048, n_hot=4096, drift=True, w_range=(0.0, 1.0), n_sample=6144),
-    2: dict(kind="indexer", name="prefill-256k-bf16", T=8192, L=262144, H=64, D=128, dtype="bf16",
-            topk=2048, n_hot=16384, drift=True, w_range=(0.0, 1.0), n_sample=6144),
-    3: dict(kind="indexer", name="prefill-1m-fp8", T=8192, L=1048576, H=64, D=128, dtype="fp8",
-            topk=2048, n_hot=65536, drift=True, w_range=(0.0, 1.0), n_sample=6144),
-    4: dict(kind="retrieval", name="retrieval-8m-d768-bf16", T=1024, N=8_000_000, D=768,
-            dtype="bf16", topk=1024, n_centres=1000, sigma=0.3, n_sample=3072),
+# The workloads, by name.  "tiny-4k-fp32" is small enough for the oracle to
+# finish in seconds; the three prefill chunks sit at 64K / 256K / 1M context;
+# the last one is the retrieval workload.  "tag" seeds the workload's streams.
+WORKLOADS = {
+    "tiny-4k-fp32": dict(kind="indexer", tag=0, T=64, L=4096, H=4, D=64, dtype="f32",
+                         topk=256, n_hot=128, drift=False, w_range=(0.5, 1.0), n_sample=768),
+    "prefill-64k-bf16": dict(kind="indexer", tag=1, T=2048, L=65536, H=64, D=128, dtype="bf16",
+                             topk=2048, n_hot=4096, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    "prefill-256k-bf16": dict(kind="indexer", tag=2, T=8192, L=262144, H=64, D=128, dtype="bf16",
+                              topk=2048, n_hot=16384, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    "prefill-1m-fp8": dict(kind="indexer", tag=3, T=8192, L=1048576, H=64, D=128, dtype="fp8",
+                           topk=2048, n_hot=65536, drift=True, w_range=(0.0, 1.0), n_sample=6144),
+    "retrieval-8m-d768-bf16": dict(kind="retrieval", tag=4, T=1024, N=8_000_000, D=768,
+                                   dtype="bf16", topk=1024, n_centres=1000, sigma=0.3, n_sample=3072),
 }
+INDEXER_WORKLOADS = [n for n, c in WORKLOADS.items() if c["kind"] == "indexer"]
 
 FP8_MAX = 448.0  # largest finite OCP e4m3fn value
 
@@ -169,20 +170,21 @@ def random_sample(n: int, upto: int, tag: int = 0, seed: int = SEED_BASE, stream
     return np.sort(g.choice(upto, size=n, replace=False)).astype(np.int32)
 
 
-def indexer_config(i: int, chunk: int = 0, seed: int = SEED_BASE, with_prev: bool = False):
-    """The seeded inputs of indexer workload ``i`` (0-3); chunk -1 is the previous chunk.
+def indexer_workload(name: str, chunk: int = 0, seed: int = SEED_BASE, with_prev: bool = False):
+    """The seeded inputs of the named indexer workload; chunk -1 is the previous chunk.
 
     With ``with_prev``, the result also holds ``prev``: the previous chunk's
     queries, weights, positions and bootstrap sample over the same keys.
     """
-    c = CONFIGS[i]
+    c = WORKLOADS[name]
     assert c["kind"] == "indexer"
     out = indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
-                         drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk,
+                         drift=c["drift"], w_range=c["w_range"], tag=c["tag"], seed=seed, chunk=chunk,
                          n_sample=c["n_sample"], keys=None)
+    out["name"] = name
     if with_prev:
         p = indexer_inputs(c["T"], c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"],
-                           drift=c["drift"], w_range=c["w_range"], tag=i, seed=seed, chunk=chunk - 1,
+                           drift=c["drift"], w_range=c["w_range"], tag=c["tag"], seed=seed, chunk=chunk - 1,
                            n_sample=c["n_sample"], keys=(out["k"], out["k_scale"], out["hot"]))
         out["prev"] = p
     return out
@@ -229,9 +231,10 @@ def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, s
                 sample=sample, centre_of_query=cq)
 
 
-def retrieval_config(i: int = 4, device: str = "cpu", seed: int = SEED_BASE, N: int | None = None,
-                     T: int | None = None):
-    c = CONFIGS[i]
+def retrieval_workload(name: str = "retrieval-8m-d768-bf16", device: str = "cpu", seed: int = SEED_BASE,
+                       N: int | None = None, T: int | None = None):
+    """The seeded inputs of the named retrieval workload (optionally with fewer rows or queries)."""
+    c = WORKLOADS[name]
     assert c["kind"] == "retrieval"
     return retrieval_inputs(T or c["T"], N or c["N"], c["D"], c["topk"], c["n_centres"], c["sigma"],
-                            c["n_sample"], tag=i, seed=seed, device=device)
+                            c["n_sample"], tag=c["tag"], seed=seed, device=device)
