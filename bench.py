@@ -92,6 +92,50 @@ def cpu_baseline(inp, n_rows: int):
                       f"in {dt:.2f} s, fp64 numpy, including the fp64 decode of the keys"}
 
 
+def bench_retrieval(args):
+    """Separate line: the 8M x 768 bf16 retrieval workload (k = 1,024, random 3,072-row sample)."""
+    import torch
+    import indexer_topk_long_amd as ltk
+    from workloads import retrieval_workload
+
+    log("generating retrieval-8m-d768-bf16 on the GPU ...")
+    r = retrieval_workload(args.workload, device="cuda")
+    T, N, D, k = r["T"], r["N"], r["D"], r["topk"]
+    q = torch.from_numpy(np.ascontiguousarray(r["q"]).view(np.int16)).cuda().view(torch.bfloat16)
+    smp = torch.from_numpy(r["sample"]).cuda()
+    ws = torch.empty(ltk.workspace_bytes(ltk.KIND_RETRIEVE, T, 1, D, N, k, len(r["sample"]), 1), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        ltk.retrieve(q, r["db"], k, sample=smp, workspace=ws)
+    torch.cuda.synchronize()
+    ev = ltk.HipEvents(args.steps)
+    opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ltk.retrieve(q, r["db"], k, sample=smp, opts=opts[i], workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
+    ev.close()
+    _, st = ltk.retrieve(q, r["db"], k, sample=smp, workspace=ws, return_stats=True)
+    pairs = T * N
+    flops = 2.0 * D * pairs
+    ach = flops / (scan_ms * 1e-3) / 1e12
+    line = {"metric": "scored query-row pairs/s, retrieval k=1024", "value": pairs / (ms * 1e-3), "unit": "pairs/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded Gaussian-mixture database, random sample)",
+            "config": {"workload": f"{args.workload}: T={T} queries, N={N} rows, D={D}, bf16, k={k}, "
+                                   f"sample={len(r['sample'])} random rows", "pairs": pairs},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "retr_scan_kernel", "kernel_ms": round(scan_ms, 4),
+                         "db_read_GBps_at_kernel_time": round(N * D * 2 / (scan_ms * 1e-3) / 1e9, 1)},
+            "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
+            "overflow_rows": st.overflow_rows, "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +169,8 @@ def main():
     from workloads import WORKLOADS, indexer_workload
 
     cfg = WORKLOADS[args.workload]
+    if cfg["kind"] == "retrieval":
+        return bench_retrieval(args)
     log(f"generating workload {cfg['name']} ...")
     t0 = time.perf_counter()
     inp = indexer_workload(args.workload, with_prev=True)

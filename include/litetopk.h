@@ -70,7 +70,7 @@ typedef struct {
     int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
     int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
     int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072) */
-    void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan */
+    void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan kernel */
     void* scan_event_stop;  /* optional hipEvent_t recorded just after it (profiling; NULL = none) */
 } ltk_opts;
 

@@ -294,6 +294,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     r.hist_c = r.hist_g + (size_t)T * o.nbins;
     r.out_idx = out_idx;
     r.out_score = out_score;
+    r.ev_scan_start = o.ev0;
+    r.ev_scan_stop = o.ev1;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_prepare_sample(f, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;

@@ -99,6 +99,7 @@ struct RetrArgs {
     uint32_t* hist_c;        // [T][nsuper] shared super-bin histograms
     int32_t* out_idx;
     float* out_score;
+    hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch
 };
 
 // Host launchers (return hipSuccess or the first launch error).

@@ -338,7 +338,9 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_scan_kernel<D>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int nsplit_pad = (a.n_splits + 7) / 8 * 8;
+    if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
     retr_scan_kernel<D><<<nsplit_pad * a.n_qgroups, kRetrWaves * 64, lds, st>>>(a);
+    if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_finalize(fin, st)) != hipSuccess) return e;
     int p2 = 1;
