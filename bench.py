@@ -171,7 +171,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     if cfg["kind"] == "retrieval":
         return bench_retrieval(args)
-    log(f"generating workload {cfg['name']} ...")
+    log(f"generating workload {args.workload} ...")
     t0 = time.perf_counter()
     inp = indexer_workload(args.workload, with_prev=True)
     log(f"  generated in {time.perf_counter() - t0:.1f} s")
