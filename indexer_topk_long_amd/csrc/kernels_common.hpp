@@ -12,24 +12,18 @@ namespace ltk {
 // everything but the n most recent (the next tile's loads) has landed.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else static_assert(N <= 9, "extend wait_vm");
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// XOR swizzle of the 16-byte chunks of a row.  LDS serves a 128-bit read 16
-// lanes at a time from 64 four-byte banks (one 256-byte bank line); those 16
-// lanes read 16 consecutive rows at the same logical chunk, so the chunk index
-// is XORed with the row's position among the rows sharing a bank line slot,
-// making the 16 physical 16-byte slots distinct.
+// XOR swizzle of the 16-byte chunks of a row.  LDS has 64 four-byte banks (a
+// 256-byte bank line).  The MFMA fragment read of the scans is the half-row
+// read: lane l takes row (l & 31), and the two 32-lane halves take different
+// chunks, so consecutive lanes read consecutive rows at the same logical
+// chunk.  XORing the chunk index with the row's position among the rows that
+// share a bank-line slot spreads them over distinct 16-byte slots.  Measured
+// on gfx950 this read costs 4 LDS cycles per 1 KB instruction, the same as a
+// linear read; an unswizzled (or 32-bank-keyed) layout costs twice that.
 template <int RB, int CPR>
 __device__ __forceinline__ int chunk_swz(int r) {
     constexpr int RPL = (RB < 256) ? 256 / RB : 1;       // rows per 256-byte bank line

@@ -89,11 +89,13 @@ def _variants(inp):
     }
 
 
-def test_sample_bins_refresh_capacity_independence(lib):
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_sample_bins_refresh_capacity_independence(lib, dt):
     """The result does not depend on the sample, the bin count, the refresh
     period, the key split or the buffer capacity (forced overflow included):
-    the GPU output is bit-identical across all of them."""
-    inp = indexer_inputs(24, 5000, 64, 128, "bf16", 200, 300, drift=True, tag=31, n_sample=600)
+    the GPU output is bit-identical across all of them.  For fp8 at D = 128
+    this also covers the scan's filter, whose threshold differs per case."""
+    inp = indexer_inputs(24, 5000, 64, 128, dt, 200, 300, drift=True, tag=31, n_sample=600)
     d = to_dev(inp)
     import indexer_topk_long_amd as ltk
     ref, ref_sc = canon(*_run_fused(lib, d, 200))
@@ -117,6 +119,21 @@ def test_sample_bins_refresh_capacity_independence(lib):
         got, got_sc = canon(*_run_fused(lib, d, 200, opts=o, sample=smp))
         assert np.array_equal(got, ref), name
         assert np.array_equal(got_sc.view(np.uint32), ref_sc.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("w_range", [(-1.0, 1.0), (-1.0, 0.0)], ids=["mixed_sign", "non_positive"])
+def test_fp8_signed_head_weights(lib, w_range):
+    """Head weights of either sign (the scan's filter bounds its bf16 estimate
+    by a second sum over |w|): fused = oracle = unfused, bit-identical scores."""
+    say("fp8 signed weights", w_range)
+    inp = indexer_inputs(40, 6000, 64, 128, "fp8", 150, 300, drift=True, w_range=w_range, tag=43, n_sample=450)
+    d = to_dev(inp)
+    idx, sc = _run_fused(lib, d, 150)
+    check_rows(inp, idx, sc, range(40), f"fused {w_range}")
+    uidx, usc = _run_unfused(lib, d, 150)
+    a, asc = canon(idx, sc)
+    b, bsc = canon(uidx, usc)
+    assert np.array_equal(a, b) and np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
 
 
 def test_forced_overflow_reports_stats(lib):
