@@ -75,7 +75,20 @@ static int auto_splits(int nqg, int64_t L, int requested) {
 static int scan_qpg(int) { return 8; }
 
 // Shared retrieval histograms: nbins fine counters + one per 16-bin super-bin, per query.
-static size_t retr_hist_words(int32_t T, int nbins) { return (size_t)T * (size_t)(nbins + (nbins + 15) / 16); }
+// Retrieval database splits: the caller's count, else about 2048 workgroups
+// (4 waves x 32 queries each) of at least 2048 rows.
+static int retr_splits(int32_t T, int64_t N, int l_splits) {
+    if (l_splits > 0) return l_splits;
+    const int64_t nqg = (T + 127) / 128;
+    int ns = 1;
+    while (nqg * ns < 2048 && N / ((int64_t)ns * 2) >= 2048) ns *= 2;
+    return ns;
+}
+// Zeroed shared counters of the retrieval scan: fine and super-bin
+// histograms, then the per-(query, split) candidate counts.
+static size_t retr_hist_words(int32_t T, int nbins, int ns) {
+    return (size_t)T * (size_t)(nbins + (nbins + 15) / 16) + (size_t)T * (size_t)ns;
+}
 
 }  // namespace ltk
 
@@ -106,7 +119,8 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     (void)H; (void)D; (void)dtype;
     Opts o;
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? kDefaultCcapRetrieve : kDefaultCcap, o) != LTK_OK) return 0;
-    return ws_layout(T, L, n_sample, o.ccap, kind == LTK_KIND_RETRIEVE ? retr_hist_words(T, o.nbins) : 0).total;
+    return ws_layout(T, L, n_sample, o.ccap,
+                     kind == LTK_KIND_RETRIEVE ? retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits)) : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -235,7 +249,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     int st;
     if ((st = resolve_opts(opts, kDefaultCcapRetrieve, o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
-    const WsLayout lay = ws_layout(T, N, n_sample, o.ccap, retr_hist_words(T, o.nbins));
+    const int ns = retr_splits(T, N, o.l_splits);
+    const WsLayout lay = ws_layout(T, N, n_sample, o.ccap, retr_hist_words(T, o.nbins, ns));
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -274,13 +289,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     r.nsuper = (o.nbins + 15) / 16;
     r.n_sample = f.n_sample;
     r.n_qgroups = (T + 127) / 128;   // 4 waves x 32 queries per workgroup
-    // database splits: about 2048 workgroups, each >= 2048 rows
-    int ns = o.l_splits;
-    if (ns <= 0) {
-        ns = 1;
-        while ((int64_t)r.n_qgroups * ns < 2048 && N / ((int64_t)ns * 2) >= 2048) ns *= 2;
-    }
     r.n_splits = ns;
+    r.cap_s = o.ccap / ns;
     r.sorted = o.sorted;
     r.ccap = o.ccap;
     r.tail = f.tail;
@@ -292,6 +302,7 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     r.cand = f.cand;
     r.hist_g = reinterpret_cast<uint32_t*>(wsb + lay.hist);
     r.hist_c = r.hist_g + (size_t)T * o.nbins;
+    r.seg_cnt = r.hist_c + (size_t)T * r.nsuper;
     r.out_idx = out_idx;
     r.out_score = out_score;
     r.ev_scan_start = o.ev0;

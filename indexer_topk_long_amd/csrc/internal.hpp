@@ -17,6 +17,7 @@ constexpr int kMaxBins = 1024;
 constexpr int64_t kDefaultCcap = 16384;
 constexpr int64_t kDefaultCcapRetrieve = 131072;
 constexpr int kMaxSortedK = 8192;
+constexpr size_t kMaxLds = 160 * 1024;   // LDS one gfx950 workgroup may allocate
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -97,6 +98,8 @@ struct RetrArgs {
     uint2* cand;
     uint32_t* hist_g;        // [T][nbins] shared fine histograms
     uint32_t* hist_c;        // [T][nsuper] shared super-bin histograms
+    uint32_t* seg_cnt;       // [T][n_splits] candidates each split found (zeroed before the scan)
+    int64_t cap_s;           // candidate slots per (query, split): ccap / n_splits
     int32_t* out_idx;
     float* out_score;
     hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch

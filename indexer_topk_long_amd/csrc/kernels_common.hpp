@@ -16,6 +16,14 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Wait, visibly to the compiler, until every vector-memory load issued so far
+// has landed (s_waitcnt vmcnt(0); expcnt and lgkmcnt untouched).  Used once
+// after the per-wave register loads that precede a streaming loop: the
+// compiler's wait analysis merges the loop entry (those loads pending) with
+// the back edge and otherwise re-inserts waits for them before their uses in
+// every iteration, waits that then also stall on the tile loads in flight.
+__device__ __forceinline__ void drain_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // XOR swizzle of the 16-byte chunks of a row.  LDS has 64 four-byte banks (a
 // 256-byte bank line).  The MFMA fragment read of the scans is the half-row
 // read: lane l takes row (l & 31), and the two 32-lane halves take different
@@ -38,6 +46,20 @@ __device__ __forceinline__ void lds_direct16(const void* g, void* lds) {
 }
 __device__ __forceinline__ void lds_direct4(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// The same 16-byte direct copy issued as inline assembly (M0 = LDS base, then
+// the load).  The compiler treats a pending LDS DMA issued through the builtin
+// as possibly aliasing every later LDS access: it drains all loads in flight
+// (vmcnt(0)) before each barrier, so no more than one tile can be in flight
+// across a barrier.  A kernel that streams several tiles ahead uses this form
+// and orders the copies itself: wait_vm on all but the newest tiles' loads,
+// then a barrier.  Vector memory operations complete in issue order, so the
+// compiler's own vmcnt waits stay correct with these copies in flight.
+__device__ __forceinline__ void lds_direct16_async(const void* g, void* lds) {
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(off) : "memory", "m0");
 }
 
 // Smallest fp32 score whose bin is >= thr (bin_of is monotone), found by

@@ -12,8 +12,11 @@
 //
 // The database is split across workgroups.  Their per-query histograms are
 // one shared array in device memory: every kept candidate adds to it with an
-// atomic, and a workgroup refreshes its threshold bins from the shared
-// counts.  Counts only ever cover real database rows, so any refresh is at
+// atomic (no return value, so the wave does not wait), and a workgroup
+// refreshes its threshold bins from the shared counts.  Candidates go to a
+// fixed slice of the query's buffer per split, counted in LDS, so keeping one
+// costs no round trip to device memory; a compaction pass then packs the
+// slices of each query before the select.  Counts only ever cover real database rows, so any refresh is at
 // most the true threshold bin and the result stays exact; sharing lets the
 // threshold rise even though no single split holds k matching rows.
 #include <math.h>
@@ -33,13 +36,24 @@ constexpr int kRetrRows = 32;             // database rows per LDS tile
 constexpr int kRetrRefreshCands = 64;     // candidates a wave adds before it refreshes
 constexpr int kSuperBins = 16;            // fine bins per super-bin of the shared histogram
 
+constexpr int kRetrStashRegs = 8;         // accumulator registers staged per rare-path round
+
 template <int D>
 struct RetrGeom {
     static constexpr int RB = 2 * D;                       // bf16 row bytes
     static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
     static constexpr int TILE = kRetrRows * RB;            // bytes per tile
     static constexpr int NINST = kRetrRows * CPR / 64;     // wave-wide 1 KB loads per tile
+    static constexpr int LPW = NINST / kRetrWaves;         // loads per wave per tile
     static constexpr int KSTEPS = D / 16;                  // v_mfma_f32_32x32x16_bf16 steps
+    static_assert(NINST % kRetrWaves == 0, "tile loads split evenly over the waves");
+    // per wave: thresholds, candidate counts, bin-map origin and scale of its 32 queries; score stash
+    static constexpr size_t FIXED_LDS = (size_t)kRetrWaves * kRetrQ * 4 * 4 + (size_t)kRetrWaves * kRetrStashRegs * 64 * 4;
+    // tile stages: as many as fit (at most 4), so tiles are requested two or
+    // three tiles ahead of their use (one tile of MFMA work is ~0.7 us at D = 768)
+    static constexpr int NST = ((kMaxLds - FIXED_LDS) / TILE) < 4 ? (int)((kMaxLds - FIXED_LDS) / TILE) : 4;
+    static_assert(NST >= 2, "at least double buffering");
+    static constexpr size_t LDS = (size_t)NST * TILE + FIXED_LDS;
 };
 
 // Query block of 32 rows: lane holds row (lane & 31), half (lane >> 5).
@@ -101,7 +115,7 @@ __device__ __forceinline__ void retr_load_tile(const RetrArgs& a, int row0, uint
         const int r = p / G::CPR, pc = p % G::CPR;
         const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
         const int row = min(row0 + r, a.N - 1);
-        lds_direct16(a.db + (size_t)row * G::RB + c * 16, st + inst * 1024);
+        lds_direct16_async(a.db + (size_t)row * G::RB + c * 16, st + inst * 1024);
     }
 }
 
@@ -114,9 +128,12 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void retr_scan_kernel(RetrArgs a) {
     using G = RetrGeom<D>;
     extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
-    uint8_t* tiles = shm;                                                 // 2 stages
-    float* tau_l = reinterpret_cast<float*>(shm + 2 * G::TILE);           // [waves][32 queries]
-    float* stash = tau_l + kRetrWaves * kRetrQ;                            // [waves][16][64] scores
+    uint8_t* tiles = shm;                                                 // G::NST stages
+    float* tau_l = reinterpret_cast<float*>(shm + G::NST * G::TILE);      // [waves][32 queries]
+    uint32_t* cnt_l = reinterpret_cast<uint32_t*>(tau_l + kRetrWaves * kRetrQ);   // [waves][32]
+    float* smin_l = reinterpret_cast<float*>(cnt_l + kRetrWaves * kRetrQ);        // [waves][32]
+    float* delta_l = smin_l + kRetrWaves * kRetrQ;                                 // [waves][32]
+    float* stash = delta_l + kRetrWaves * kRetrQ;                          // [waves][8][64] scores
     const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
 
     // (split, query group) from the block index so that the query groups of
@@ -133,6 +150,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     HalfRow<DT_BF16, D> qf;
     load_qblock<D>(qf, a, q0);
+    drain_vm_loads();
     const Meta* meta = reinterpret_cast<const Meta*>(a.meta);
 
     // thresholds of the wave's 32 queries: lane i < 32 owns query q0 + i
@@ -144,18 +162,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         thr_own = m_own.thr0;
     }
     float* my_tau = tau_l + wave * kRetrQ;
-    if (lane < 32) my_tau[lane] = own_valid ? tau_of(thr_own, m_own.smin, m_own.delta, a.nbins) : INFINITY;
+    uint32_t* my_cnt = cnt_l + wave * kRetrQ;
+    if (lane < 32) {
+        my_tau[lane] = own_valid ? tau_of(thr_own, m_own.smin, m_own.delta, a.nbins) : INFINITY;
+        my_cnt[lane] = 0u;
+        smin_l[wave * kRetrQ + lane] = m_own.smin;
+        delta_l[wave * kRetrQ + lane] = m_own.delta;
+    }
+    uint2* cand_base = a.cand + (size_t)split * a.cap_s;   // + q * ccap: this split's slice of query q
     float tau[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) tau[r] = my_tau[reg_query(0, r, half)];
     int added = 0;   // candidates this wave added since its last refresh (wave-uniform)
 
-    retr_load_tile<D>(a, r_lo, tiles, wave, lane);
+    constexpr int LEAD = G::NST - 1;   // tiles requested ahead of the one computed
+#pragma unroll
+    for (int j = 0; j < LEAD; ++j)
+        if (j < ntiles) retr_load_tile<D>(a, r_lo + j * kRetrRows, tiles + j * G::TILE, wave, lane);
+    int sbuf = 0;   // stage of tile `it`
     for (int it = 0; it < ntiles; ++it) {
-        wait_vm<0>();
-        __syncthreads();
-        if (it + 1 < ntiles) retr_load_tile<D>(a, r_lo + (it + 1) * kRetrRows, tiles + ((it + 1) & 1) * G::TILE, wave, lane);
-        const uint8_t* st = tiles + (it & 1) * G::TILE;
+        // tiles it+1 .. it+LEAD-1 (those that exist) may still be loading
+        const int later = min(LEAD - 1, ntiles - 1 - it);
+        if (later <= 0) wait_vm<0>();
+        else if (later == 1) wait_vm<G::LPW>();
+        else wait_vm<2 * G::LPW>();
+        __syncthreads();   // every wave's share of tile `it` has landed; the stage of tile it-1 is free
+        if (it + LEAD < ntiles)
+            retr_load_tile<D>(a, r_lo + (it + LEAD) * kRetrRows, tiles + ((sbuf + LEAD) % G::NST) * G::TILE, wave, lane);
+        const uint8_t* st = tiles + sbuf * G::TILE;
+        sbuf = (sbuf + 1) % G::NST;
         const int rr = lane & 31;
         const int row = r_lo + it * kRetrRows + rr;
         // B fragments read from LDS four steps ahead of their MFMA; the
@@ -185,38 +220,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) pm |= (rv && acc[r] >= tau[r]) ? (1u << r) : 0u;
         if (__ballot(pm != 0u)) {
-            // rare: keep the passing (row, score) pairs, register by register,
-            // from a wave-private LDS copy of the scores (one loop body, no
-            // per-register copies of the write-back code)
-            float* sv = stash + wave * 16 * 64;
+            // candidates (most tiles hold one or two): every lane walks only its
+            // own passing registers, reading their scores back from a wave-private
+            // LDS copy (dynamic register index), taking a slot of the query's
+            // slice with an LDS atomic and adding to the shared histograms
+            // without waiting for a reply
+            float* sv = stash + wave * kRetrStashRegs * 64;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sv[r * 64 + lane] = acc[r];
-#pragma unroll 1
-            for (int r = 0; r < 16; ++r) {
-                const bool pass = (pm >> r) & 1u;
-                const uint64_t mask = __ballot(pass);
-                if (!mask) continue;
-                const float I = sv[r * 64 + lane];
-#pragma unroll 1
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t mh = (uint32_t)(mask >> (32 * h));
-                    if (!mh) continue;
-                    const int q = reg_query(q0, r, h);
-                    const int leader = 32 * h + __ffs(mh) - 1;
-                    uint32_t base = 0;
-                    if (lane == leader) base = atomicAdd(&a.tail[q], (uint32_t)__popc(mh));
-                    base = __shfl(base, leader);
-                    if (pass && half == h) {
-                        const uint32_t p = base + (uint32_t)__popc(mh & ((1u << rr) - 1u));
-                        if ((int64_t)p < a.ccap) a.cand[(size_t)q * a.ccap + p] = make_uint2((uint32_t)row, __float_as_uint(I));
-                        const Meta mq = meta[q];
-                        const int b = bin_of(I, mq.smin, mq.delta, a.nbins);
+            for (int rb = 0; rb < 16; rb += kRetrStashRegs) {
+                uint32_t pr = (pm >> rb) & ((1u << kRetrStashRegs) - 1u);
+                if (__ballot(pr != 0u)) {
+#pragma unroll
+                    for (int r = 0; r < kRetrStashRegs; ++r) sv[r * 64 + lane] = acc[rb + r];
+                    while (pr) {
+                        const int reg = rb + __ffs(pr) - 1;
+                        pr &= pr - 1u;
+                        const float I = sv[(reg - rb) * 64 + lane];
+                        const int ql = reg_query(0, reg, half);
+                        const int q = q0 + ql;
+                        const uint32_t p = atomicAdd(&my_cnt[ql], 1u);
+                        if ((int64_t)p < a.cap_s)
+                            cand_base[(size_t)q * a.ccap + p] = make_uint2((uint32_t)row, __float_as_uint(I));
+                        const int b = bin_of(I, smin_l[wave * kRetrQ + ql], delta_l[wave * kRetrQ + ql], a.nbins);
                         atomicAdd(&a.hist_g[(size_t)q * a.nbins + b], 1u);
                         atomicAdd(&a.hist_c[(size_t)q * a.nsuper + b / kSuperBins], 1u);
                     }
                 }
-                added += __popcll(mask);
             }
+            added += __popcll(__ballot(pm != 0u));   // lanes that kept a candidate (a lower bound)
         }
         // refresh from the shared histograms once this wave has added enough
         // candidates: accumulate counts from the top bin down (super-bins
@@ -274,6 +305,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     }
+    // candidates this split found for each of the wave's queries (may exceed the slice)
+    if (own_valid) a.seg_cnt[(size_t)(q0 + lane) * a.n_splits + split] = my_cnt[lane];
+}
+
+// ---------------------------------------------------------------------------
+// Compaction: pack the per-split slices of each query's candidate buffer into
+// a prefix, in place.  Entry v of the packed order comes from slice s (the
+// split holding it) at s * cap_s + (v - start of s) >= v, so rounds that stage
+// a range of v in LDS, then write it back, never overwrite an entry a later
+// round still has to read.  A slice that overflowed sends the query to the
+// exact fallback (its tail is set past the buffer capacity).
+// ---------------------------------------------------------------------------
+
+constexpr int kCompactStage = 8192;   // entries staged per round (64 KB of LDS)
+
+__global__ __launch_bounds__(256) void retr_compact_kernel(RetrArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
+    uint2* stage = reinterpret_cast<uint2*>(shm);                         // [kCompactStage]
+    uint32_t* start = reinterpret_cast<uint32_t*>(stage + kCompactStage); // [n_splits + 1]
+    __shared__ uint32_t s_part[256];
+    __shared__ uint32_t s_total, s_over;
+    const int t = blockIdx.x, tid = threadIdx.x, ns = a.n_splits;
+    const uint32_t cap = (uint32_t)a.cap_s;
+    const uint32_t* cnt = a.seg_cnt + (size_t)t * ns;
+    // exclusive prefix of the kept counts: each thread sums a contiguous run of splits
+    const int per = (ns + 255) / 256, lo = tid * per, hi = min(ns, lo + per);
+    uint32_t run = 0, over = 0;
+    uint64_t found = 0;
+    for (int s = lo; s < hi; ++s) {
+        const uint32_t c = cnt[s];
+        found += c;
+        over |= (c > cap) ? 1u : 0u;
+        run += min(c, cap);
+    }
+    s_part[tid] = run;
+    if (tid == 0) { s_total = 0u; s_over = 0u; }
+    __syncthreads();
+    if (over) atomicOr(&s_over, 1u);
+    atomicAdd(&s_total, (uint32_t)min<uint64_t>(found, 0xffffffffull));
+    if (tid == 0) {   // 256 partial sums, serially
+        uint32_t acc = 0;
+        for (int i = 0; i < 256; ++i) {
+            const uint32_t v = s_part[i];
+            s_part[i] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    uint32_t acc = s_part[tid];
+    for (int s = lo; s < hi; ++s) {
+        start[s] = acc;
+        acc += min(cnt[s], cap);
+    }
+    if (tid == 255) start[ns] = acc;
+    __syncthreads();
+    const uint32_t kept = start[ns];
+    if (s_over) {   // the fallback recomputes this row
+        if (tid == 0) a.tail[t] = (uint32_t)max<int64_t>((int64_t)s_total, a.ccap + 1);
+        return;
+    }
+    uint2* c = a.cand + (size_t)t * a.ccap;
+    for (uint32_t r0 = 0; r0 < kept; r0 += kCompactStage) {
+        const uint32_t r1 = min(kept, r0 + (uint32_t)kCompactStage);
+        for (uint32_t v = r0 + tid; v < r1; v += 256) {
+            int l = 0, h = ns;   // last split with start <= v
+            while (h - l > 1) {
+                const int m = (l + h) >> 1;
+                if (start[m] <= v) l = m; else h = m;
+            }
+            stage[v - r0] = c[(size_t)l * cap + (v - start[l])];
+        }
+        __syncthreads();
+        for (uint32_t v = r0 + tid; v < r1; v += 256) c[v] = stage[v - r0];
+        __syncthreads();
+    }
+    if (tid == 0) a.tail[t] = kept;
 }
 
 // ---------------------------------------------------------------------------
@@ -333,7 +440,7 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
     retr_sample_score_kernel<D><<<sg, 256, 0, st>>>(a);
     hipError_t e = launch_sample_stats(fin, st);
     if (e != hipSuccess) return e;
-    const size_t lds = 2 * (size_t)G::TILE + (size_t)kRetrWaves * kRetrQ * 4 + (size_t)kRetrWaves * 16 * 64 * 4;
+    const size_t lds = G::LDS;
     if (lds > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_scan_kernel<D>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -341,6 +448,11 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
     if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
     retr_scan_kernel<D><<<nsplit_pad * a.n_qgroups, kRetrWaves * 64, lds, st>>>(a);
     if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t compact_lds = (size_t)kCompactStage * 8 + ((size_t)a.n_splits + 1) * 4;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_compact_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)compact_lds);
+    retr_compact_kernel<<<a.T, 256, compact_lds, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_finalize(fin, st)) != hipSuccess) return e;
     int p2 = 1;
