@@ -106,17 +106,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Filter: the fused scan over the database
 // ---------------------------------------------------------------------------
 
+// This wave's j-th 1 KB direct load of the tile starting at row0 (16-byte
+// chunk p = 64*inst + lane holds chunk (p % CPR) ^ swz(row) of row p / CPR).
+template <int D>
+__device__ __forceinline__ void retr_load_part(const RetrArgs& a, int row0, uint8_t* st, int wave, int lane, int j) {
+    using G = RetrGeom<D>;
+    const int inst = wave + j * kRetrWaves;
+    const int p = inst * 64 + lane;
+    const int r = p / G::CPR, pc = p % G::CPR;
+    const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
+    const int row = min(row0 + r, a.N - 1);
+    lds_direct16_async(a.db + (size_t)row * G::RB + c * 16, st + inst * 1024);
+}
 template <int D>
 __device__ __forceinline__ void retr_load_tile(const RetrArgs& a, int row0, uint8_t* st, int wave, int lane) {
-    using G = RetrGeom<D>;
 #pragma unroll
-    for (int inst = wave; inst < G::NINST; inst += kRetrWaves) {
-        const int p = inst * 64 + lane;
-        const int r = p / G::CPR, pc = p % G::CPR;
-        const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
-        const int row = min(row0 + r, a.N - 1);
-        lds_direct16_async(a.db + (size_t)row * G::RB + c * 16, st + inst * 1024);
-    }
+    for (int j = 0; j < RetrGeom<D>::LPW; ++j) retr_load_part<D>(a, row0, st, wave, lane, j);
 }
 
 // Coherent (device-scope) read of a shared counter.
@@ -187,8 +192,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else if (later == 1) wait_vm<G::LPW>();
         else wait_vm<2 * G::LPW>();
         __syncthreads();   // every wave's share of tile `it` has landed; the stage of tile it-1 is free
-        if (it + LEAD < ntiles)
-            retr_load_tile<D>(a, r_lo + (it + LEAD) * kRetrRows, tiles + ((sbuf + LEAD) % G::NST) * G::TILE, wave, lane);
+        // the loads of tile it+LEAD go out spread over this tile's MFMAs (below):
+        // issued back to back they hold the wave at the memory pipe before its MFMAs
+        const bool load_next = it + LEAD < ntiles;
+        const int row_next = r_lo + (it + LEAD) * kRetrRows;
+        uint8_t* st_next = tiles + ((sbuf + LEAD) % G::NST) * G::TILE;
         const uint8_t* st = tiles + sbuf * G::TILE;
         sbuf = (sbuf + 1) % G::NST;
         const int rr = lane & 31;
@@ -208,6 +216,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         v16f acc = v16f{};
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
+            constexpr int LSTEP = G::KSTEPS / G::LPW;   // MFMAs between this wave's tile loads
+            if (s % LSTEP == 0 && s / LSTEP < G::LPW && load_next)
+                retr_load_part<D>(a, row_next, st_next, wave, lane, s / LSTEP);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf.v[s]),
                                                           __builtin_bit_cast(bf16x8, bq[s % PF]), acc, 0, 0, 0);
             if (s + PF < G::KSTEPS) bq[s % PF] = rd(s + PF);
