@@ -193,8 +193,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else wait_vm<2 * G::LPW>();
         __syncthreads();   // every wave's share of tile `it` has landed; the stage of tile it-1 is free
         // the loads of tile it+LEAD go out spread over this tile's MFMAs (below):
-        // issued back to back they hold the wave at the memory pipe before its MFMAs
-        const bool load_next = it + LEAD < ntiles;
+        // issued back to back they hold the wave at the memory pipe before its
+        // MFMAs.  They go out unconditionally (no branch between the MFMAs): past
+        // the last tile they re-read clamped rows into a stage nothing reads, and
+        // being the newest loads they never loosen the waits above.
         const int row_next = r_lo + (it + LEAD) * kRetrRows;
         uint8_t* st_next = tiles + ((sbuf + LEAD) % G::NST) * G::TILE;
         const uint8_t* st = tiles + sbuf * G::TILE;
@@ -217,8 +219,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
             constexpr int LSTEP = G::KSTEPS / G::LPW;   // MFMAs between this wave's tile loads
-            if (s % LSTEP == 0 && s / LSTEP < G::LPW && load_next)
-                retr_load_part<D>(a, row_next, st_next, wave, lane, s / LSTEP);
+            if (s % LSTEP == 0 && s / LSTEP < G::LPW) retr_load_part<D>(a, row_next, st_next, wave, lane, s / LSTEP);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf.v[s]),
                                                           __builtin_bit_cast(bf16x8, bq[s % PF]), acc, 0, 0, 0);
             if (s + PF < G::KSTEPS) bq[s % PF] = rd(s + PF);
@@ -226,11 +227,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         // gate: bit r of pm is set when the score in accumulator register r
         // reaches its query's threshold
-        const bool rv = row < r_hi;
-        uint32_t pm = 0;
+        // gate: one compare per register into a wave mask (scalar ORs); the
+        // per-lane mask of passing registers (bit r of pm) only when some pass
+        uint64_t any = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pm |= (rv && acc[r] >= tau[r]) ? (1u << r) : 0u;
-        if (__ballot(pm != 0u)) {
+        for (int r = 0; r < 16; ++r) any |= __ballot(acc[r] >= tau[r]);
+        if (any & __ballot(row < r_hi)) {
+            const bool rv = row < r_hi;
+            uint32_t pm = 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) pm |= (rv && acc[r] >= tau[r]) ? (1u << r) : 0u;
             // candidates (most tiles hold one or two): every lane walks only its
             // own passing registers, reading their scores back from a wave-private
             // LDS copy (dynamic register index), taking a slot of the query's
@@ -316,6 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     }
+    wait_vm<0>();   // loads issued past the last tile land before the workgroup ends
     // candidates this split found for each of the wave's queries (may exceed the slice)
     if (own_valid) a.seg_cnt[(size_t)(q0 + lane) * a.n_splits + split] = my_cnt[lane];
 }
