@@ -29,12 +29,17 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# HBM-side bytes per launch of the fused scan at the 1M-context workload, from
-# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings
-# (profiles/scan_kernel_prefill-1m-fp8.md).  Valid only for the kernel sources
-# with this digest; reported as null otherwise.
-SCAN_TRAFFIC = {"digest": "2b17e0a8e38ebba6", "workload": "prefill-1m-fp8", "bytes": 4.554e9 + 1.555e8}
+# HBM-side bytes per launch of each scan kernel at its workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings (FETCH x2.0, WRITE
+# x1.0; profiles/scan_kernel_prefill-1m-fp8.md, profiles/retr_scan_kernel_
+# retrieval-8m-d768-bf16.md).  Valid only for the kernel sources with the
+# recorded digest; reported as null otherwise.
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
+RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
+SCAN_TRAFFIC = {"digest": "2ccda14b383fdfde", "workload": "prefill-1m-fp8",
+                "bytes": 2223930 * 1024 * 2.0 + 151690 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "cef33f8a64b052eb", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 8856324 * 1024 * 2.0 + 1293637 * 1024 * 1.0}
 
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
@@ -64,10 +69,10 @@ def to_dev(inp, torch):
     return d
 
 
-def scan_source_digest() -> str:
+def scan_source_digest(files=KERNEL_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "indexer_topk_long_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -128,7 +133,9 @@ def bench_retrieval(args):
             "config": {"workload": f"{args.workload}: T={T} queries, N={N} rows, D={D}, bf16, k={k}, "
                                    f"sample={len(r['sample'])} random rows", "pairs": pairs},
             "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                         "traffic": (RETR_TRAFFIC["bytes"] if scan_source_digest(RETR_SOURCES) == RETR_TRAFFIC["digest"]
+                                     and args.workload == RETR_TRAFFIC["workload"] else None),
                          "kernel": "retr_scan_kernel", "kernel_ms": round(scan_ms, 4),
                          "db_read_GBps_at_kernel_time": round(N * D * 2 / (scan_ms * 1e-3) / 1e9, 1)},
             "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
