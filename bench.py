@@ -150,7 +150,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill-1m-fp8", help="indexer workload name (default: the 1M-context chunk)")
     ap.add_argument("--unfused-steps", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=12)
+    ap.add_argument("--cpu-rows", type=int, default=72)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
