@@ -143,6 +143,52 @@ def bench_retrieval(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_prefill_chunks(args):
+    """Separate line: a chunked prefill over the 1M-context keys (8,192-query chunks from
+    position 0, each chunk's sample carried from the previous chunk's result)."""
+    import torch
+    import indexer_topk_long_amd as ltk
+    from workloads import WORKLOADS, indexer_workload, prefill_queries
+
+    name = "prefill-1m-fp8"
+    c = WORKLOADS[name]
+    log(f"generating the keys of {name} ...")
+    inp = indexer_workload(name)
+    k = torch.from_numpy(inp["k"]).cuda().view(torch.float8_e4m3fn)
+    ks = torch.from_numpy(inp["k_scale"]).cuda()
+    chunk = c["T"]
+    nq = min(c["L"], args.prefill_chunks * chunk) if args.prefill_chunks > 0 else c["L"]
+    qf = prefill_queries(name, device="cuda")
+    ltk.prefill_chunked(qf, k, c["topk"], min(nq, 2 * chunk), chunk=chunk, n_sample=c["n_sample"], k_scale=ks)  # warmup
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = ltk.prefill_chunked(qf, k, c["topk"], nq, chunk=chunk, n_sample=c["n_sample"], k_scale=ks)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ch = res["chunks"]
+    pairs = sum(r["pairs"] for r in ch)
+    hits = [r["sample_hit_rate"] for r in ch if r["sample_hit_rate"] is not None]
+    sel_ms = sum(r["ms"] for r in ch)
+    line = {"metric": "scored query-key pairs/s over a chunked prefill", "value": pairs / wall, "unit": "pairs/s",
+            "n_gpus": 1, "steps": 1, "warmup": 1, "ms_per_step": round(wall * 1e3, 2), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+            "data": "synthetic (keys of prefill-1m-fp8; queries drawn on the device per chunk)",
+            "config": {"workload": f"{name} keys, {len(ch)} chunks of {chunk} queries from position 0, "
+                                   f"k={c['topk']}, sample = previous chunk's top-{c['n_sample']}",
+                       "queries": nq, "pairs": pairs},
+            "select_ms_total": round(sel_ms, 2),
+            "workspace_bytes": res["workspace_bytes"],
+            "candidates_per_query": {"first": round(ch[0]["candidates_per_query"], 1),
+                                     "last": round(ch[-1]["candidates_per_query"], 1),
+                                     "max_over_chunks": round(max(r["candidates_per_query"] for r in ch), 1)},
+            "overflow_rows": sum(r["overflow_rows"] for r in ch),
+            "sample_hit_rate": {"mean": round(float(np.mean(hits)), 4) if hits else None,
+                                "min": round(float(np.min(hits)), 4) if hits else None,
+                                "last": round(hits[-1], 4) if hits else None},
+            "chunk_ms": {"first": round(ch[0]["ms"], 3), "last": round(ch[-1]["ms"], 3)}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +197,8 @@ def main():
     ap.add_argument("--workload", default="prefill-1m-fp8", help="indexer workload name (default: the 1M-context chunk)")
     ap.add_argument("--unfused-steps", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=72)
+    ap.add_argument("--prefill-chunks", type=int, default=-1,
+                    help="time a chunked prefill over the 1M-context keys: the first N chunks (0 = all 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
@@ -176,6 +224,8 @@ def main():
     from workloads import WORKLOADS, indexer_workload
 
     cfg = WORKLOADS[args.workload]
+    if args.prefill_chunks >= 0:
+        return bench_prefill_chunks(args)
     if cfg["kind"] == "retrieval":
         return bench_retrieval(args)
     log(f"generating workload {args.workload} ...")

@@ -28,9 +28,9 @@ from ._binding import (  # noqa: F401
     unfused_score_select,
     workspace_bytes,
 )
-from .prefill import next_sample  # noqa: F401
+from .prefill import next_sample, prefill_chunked  # noqa: F401
 
 __all__ = [
     "score_select", "retrieve", "unfused_score_select", "workspace_bytes", "strerror", "device_check",
-    "Opts", "Stats", "LtkError", "next_sample", "library", "exported_symbols",
+    "Opts", "Stats", "LtkError", "next_sample", "prefill_chunked", "library", "exported_symbols",
 ]

@@ -25,3 +25,66 @@ def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
     if rc != 0:
         raise LtkError(rc, "litetopk_next_sample")
     return out
+
+
+def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_sample: int | None = None,
+                    k_scale=None, first_pos: int = 0, opts=None, keep_outputs: bool = False):
+    """Whole-prefill driver: the queries at positions first_pos .. first_pos+n_queries-1
+    in chunks of `chunk`, each chunk scored against every key at or before its
+    queries, with the previous chunk's most-selected 3k keys as its sample (the
+    LiteTopK pages, "Sampling"); the first chunk has no sample.
+
+    `queries` is either (q [n_queries, H, D], w [n_queries, H], q_scale or None)
+    or a function (c0, c1) -> that triple for the queries c0 .. c1-1, so a long
+    prefill need not hold every query at once.  One workspace, sized for a full
+    chunk over all L keys, serves every chunk.
+
+    Returns {"chunks": [per-chunk dict], "workspace_bytes": int, "last": int32
+    [rows, topk] of the last chunk, "outputs": list of every chunk's indices if
+    keep_outputs}.  Per chunk: queries, causal pairs, ms of the select call
+    (device events), candidates per query, overflow rows, and the sample hit
+    rate (fraction of the chunk's selected keys that were in its sample).
+    """
+    import torch
+    from ._binding import KIND_SCORE_SELECT, _dtype_code, score_select, workspace_bytes
+
+    L = k.shape[0]
+    n_sample = 3 * topk if n_sample is None else n_sample
+
+    def get(c0, c1):
+        if callable(queries):
+            return queries(c0, c1)
+        q, w, qs = queries
+        return q[c0:c1], w[c0:c1], None if qs is None else qs[c0:c1]
+
+    q0, _, _ = get(0, min(chunk, n_queries))
+    H, D = q0.shape[1], q0.shape[2]
+    nbytes = workspace_bytes(KIND_SCORE_SELECT, chunk, H, D, L, topk, n_sample, _dtype_code(q0), opts)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    ws_sample = torch.empty(max(4 * L, 256), dtype=torch.uint8, device=k.device)
+    records, outputs, prev = [], [], None
+    for c0 in range(0, n_queries, chunk):
+        c1 = min(n_queries, c0 + chunk)
+        q, w, qs = get(c0, c1)
+        pos = torch.arange(first_pos + c0, first_pos + c1, dtype=torch.int32, device=k.device)
+        sample = next_sample(prev, L, n_sample, workspace=ws_sample) if prev is not None else None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        idx, st = score_select(q, k, w, pos, topk, sample=sample, q_scale=qs, k_scale=k_scale, opts=opts,
+                               return_stats=True, workspace=ws)
+        e1.record()
+        e1.synchronize()
+        valid = idx >= 0
+        if sample is not None and sample.numel() > 0:
+            hit = float((torch.isin(idx, sample) & valid).sum().item()) / max(1, int(valid.sum().item()))
+        else:
+            hit = None
+        ends = torch.clamp(pos.to(torch.int64), max=L - 1) + 1
+        records.append({"chunk": c0 // chunk, "queries": c1 - c0, "pairs": int(ends.sum().item()),
+                        "ms": e0.elapsed_time(e1), "candidates_per_query": st.cand_written / (c1 - c0),
+                        "max_candidates": st.max_cand_per_query, "overflow_rows": st.overflow_rows,
+                        "sample_hit_rate": hit})
+        if keep_outputs:
+            outputs.append(idx)
+        prev = idx
+    return {"chunks": records, "workspace_bytes": nbytes, "last": prev, "outputs": outputs if keep_outputs else None}

@@ -8,6 +8,7 @@ from .gen import (  # noqa: F401
     WORKLOADS,
     indexer_workload,
     indexer_inputs,
+    prefill_queries,
     random_sample,
     retrieval_workload,
     retrieval_inputs,

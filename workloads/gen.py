@@ -190,6 +190,57 @@ def indexer_workload(name: str, chunk: int = 0, seed: int = SEED_BASE, with_prev
     return out
 
 
+_S_PREFILL = 8   # stream id of the whole-prefill queries drawn on the device
+
+
+def prefill_queries(name: str, device: str = "cuda", seed: int = SEED_BASE):
+    """Queries and head weights of a whole prefill over the named indexer
+    workload's keys, drawn with torch's generator on ``device``.
+
+    Returns a function (c0, c1) -> (q, w, q_scale) for the queries at
+    positions c0 .. c1-1: q[t, h] = q_gain * u(t) + N(0, I_D) / sqrt(D) and
+    w ~ U(w_range), as in ``indexer_inputs``, rounded to the workload's storage
+    format (fp8: per-token scale amax / 448).  Each chunk is drawn from its own
+    generator state (seeded by its start position), so chunks can be drawn in
+    any order.
+    """
+    import torch
+
+    c = WORKLOADS[name]
+    assert c["kind"] == "indexer"
+    L, H, D, dt = c["L"], c["H"], c["D"], c["dtype"]
+    u0, u1 = _direction(c["tag"], D, seed)
+    dev = torch.device(device)
+    tu0 = torch.from_numpy(u0.astype(np.float32)).to(dev)
+    tu1 = torch.from_numpy(u1.astype(np.float32)).to(dev)
+    base = int(np.random.SeedSequence([seed, c["tag"], _S_PREFILL]).generate_state(1, dtype=np.uint64)[0] >> 2)
+
+    def chunk(c0: int, c1: int):
+        g = torch.Generator(device=dev)
+        g.manual_seed(base + c0)
+        n = c1 - c0
+        p = torch.arange(c0, c1, device=dev, dtype=torch.float64)
+        if c["drift"]:
+            phi = (math.pi / 2.0) * p / float(L)
+            u = torch.cos(phi)[:, None].float() * tu0[None, :] + torch.sin(phi)[:, None].float() * tu1[None, :]
+            u = u / torch.linalg.vector_norm(u, dim=1, keepdim=True)
+        else:
+            u = tu0[None, :].expand(n, D)
+        q = torch.randn((n, H, D), generator=g, device=dev, dtype=torch.float32) / math.sqrt(D)
+        q += 0.5 * u[:, None, :]
+        w = torch.rand((n, H), generator=g, device=dev, dtype=torch.float32)
+        w = c["w_range"][0] + (c["w_range"][1] - c["w_range"][0]) * w
+        if dt == "f32":
+            return q.contiguous(), w.contiguous(), None
+        if dt == "bf16":
+            return q.to(torch.bfloat16).contiguous(), w.contiguous(), None
+        amax = q.abs().amax(dim=(1, 2))
+        scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+        return (q / scale[:, None, None]).to(torch.float8_e4m3fn).contiguous(), w.contiguous(), scale.contiguous()
+
+    return chunk
+
+
 def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, sigma: float = 0.3,
                      n_sample: int = 3072, tag: int = 4, seed: int = SEED_BASE, device: str = "cpu",
                      block: int = 1 << 20, db_dtype: str = "bf16"):
