@@ -41,6 +41,7 @@ SCAN_TRAFFIC = {"digest": "2ccda14b383fdfde", "workload": "prefill-1m-fp8",
 RETR_TRAFFIC = {"digest": "cef33f8a64b052eb", "workload": "retrieval-8m-d768-bf16",
                 "bytes": 8856324 * 1024 * 2.0 + 1293637 * 1024 * 1.0}
 
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 matrix
@@ -189,6 +190,164 @@ def bench_prefill_chunks(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_decode(args):
+    """Separate line: decode steps over the 1M-context keys.
+
+    A step scores T queries at the newest positions (T = 1: one new token;
+    T = 8: a new token and seven draft tokens verified together) against every
+    causal key and returns their exact top-k.  Its sample is the union of the
+    last three steps' results (the decode counterpart of reusing the previous
+    chunk's top-3k; duplicates are dropped on the device).  Steps advance by T
+    positions.  Timed eagerly (one library call per step) and as one HIP graph
+    of the same steps, whose results must hold the same index sets.
+    """
+    import torch
+    import indexer_topk_long_amd as ltk
+    from workloads import WORKLOADS, indexer_keys, prefill_queries, random_sample
+
+    cfg = WORKLOADS[args.workload]
+    base = cfg["keys"]
+    c = WORKLOADS[base]
+    T, L, H, D, k = cfg["T"], c["L"], c["H"], c["D"], c["topk"]
+    log(f"generating the keys of {base} ...")
+    kr, ksr = indexer_keys(base)
+    kk = torch.from_numpy(kr).cuda().view(torch.float8_e4m3fn)
+    ks = torch.from_numpy(ksr).cuda()
+    del kr, ksr
+    nw, n = max(args.warmup, 3), args.steps
+    total = 1 + nw + n                     # bootstrap, warmup, timed
+    P0 = L - total * T
+    qf = prefill_queries(base, device="cuda")
+    steps = []
+    for j in range(total):
+        q, w, qs = qf(P0 + j * T, P0 + (j + 1) * T)
+        steps.append((q, w, qs, torch.arange(P0 + j * T, P0 + (j + 1) * T, dtype=torch.int32, device="cuda")))
+    n_boot = c["n_sample"]
+    ws = torch.empty(ltk.workspace_bytes(ltk.KIND_SCORE_SELECT, T, H, D, L, k, max(3 * T * k, n_boot), 2),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(j, hist, opts=None, **kw):
+        q, w, qs, pos = steps[j]
+        sample = torch.cat([h.reshape(-1) for h in hist[-3:]])
+        return ltk.score_select(q, kk, w, pos, k, sample=sample, q_scale=qs, k_scale=ks, opts=opts,
+                                workspace=ws, **kw)
+
+    def run(j0, hist, count, opts=None):
+        outs = []
+        hist = list(hist)
+        for i in range(count):
+            o = step(j0 + i, hist, opts[i] if opts else None)
+            outs.append(o)
+            hist = (hist + [o])[-3:]
+        return outs
+
+    # bootstrap step on a seeded random sample of the visible keys, then warmup
+    boot = torch.from_numpy(random_sample(n_boot, P0, tag=c["tag"])).cuda()
+    hist = run(0, [boot], 1)
+    hist = (hist + run(1, hist, nw))[-3:]
+    hist0 = [h.clone() for h in hist]
+    torch.cuda.synchronize()
+    ev = ltk.HipEvents(n)
+    opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
+    t0 = time.perf_counter()
+    eager = run(1 + nw, hist0, n, opts)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / n
+    scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(n)]))
+    ev.close()
+    log(f"  eager: {eager_ms * 1e3:.1f} us/step, scan kernel {scan_ms * 1e3:.1f} us")
+
+    # the same n steps captured as one graph
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(1 + nw, hist0, n)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        gouts = run(1 + nw, hist0, n)
+
+    def same_sets(a, b):
+        return all(torch.equal(torch.sort(x, dim=1).values, torch.sort(y, dim=1).values) for x, y in zip(a, b))
+
+    g.replay()
+    torch.cuda.synchronize()
+    graph_same = same_sets(gouts, eager)
+    reps = 5
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / (reps * n)
+    graph_same = graph_same and same_sets(gouts, eager)
+    log(f"  graph: {graph_ms * 1e3:.1f} us/step, same as eager: {graph_same}")
+
+    # figures of the last timed step
+    jl = nw + n
+    hl = (hist0 + eager)[-4:-1]
+    _, st = step(jl, hl, return_stats=True)
+    pos_last = steps[jl][3].cpu().numpy().astype(np.int64)
+    pairs = int(np.sum(pos_last + 1))
+    visible = int(pos_last.max()) + 1
+    scan_bytes = visible * (D + 4) + T * H * D + T * H * 4 + T * 4
+    allh = hist0 + eager
+    hits = [float(torch.isin(allh[i], torch.cat([h.reshape(-1) for h in allh[i - 3:i]])).float().mean())
+            for i in range(3, len(allh))]
+    uout = ltk.unfused_score_select(steps[jl][0], kk, steps[jl][1], steps[jl][3], k, q_scale=steps[jl][2],
+                                    k_scale=ks)
+    same_unfused = same_sets([uout], [eager[-1]])
+    del uout
+    oracle = None
+    if not args.no_cpu_baseline:
+        log("  oracle on the last step's rows ...")
+        from oracle import oracle_indexer
+        q, w, qs, pos = steps[jl]
+        inp = dict(kind="indexer", T=T, L=L, H=H, D=D, dtype="fp8", topk=k, q=q.view(torch.uint8).cpu().numpy(),
+                   k=kk.view(torch.uint8).cpu().numpy(), q_scale=qs.cpu().numpy(), k_scale=ks.cpu().numpy(),
+                   w=w.cpu().numpy(), pos=pos.cpu().numpy())
+        t0 = time.perf_counter()
+        ref_idx, _ = oracle_indexer(inp, rows=np.arange(T))
+        dt = time.perf_counter() - t0
+        got = eager[-1].cpu().numpy()
+        overlap = float(np.mean([len(set(got[t].tolist()) & set(ref_idx[t].tolist())) / k for t in range(T)]))
+        oracle = {"value": pairs / dt, "unit": "pairs/s", "cores": _cores(), "kind": "oracle",
+                  "sample": f"the {T} query row(s) of the last decode step, all causal keys: {pairs} pairs in "
+                            f"{dt:.2f} s, fp64 numpy",
+                  "set_overlap_with_gpu": round(overlap, 6)}
+    value = pairs / (graph_ms * 1e-3)
+    line = {"metric": "scored query-key pairs/s per decode step at 1M context, k=2048", "value": value,
+            "unit": "pairs/s", "n_gpus": 1, "steps": n, "warmup": nw, "ms_per_step": round(graph_ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+            "data": "synthetic (keys of prefill-1m-fp8; queries drawn on the device per step)",
+            "config": {"workload": f"{args.workload}: {T} quer{'y' if T == 1 else 'ies'} per step, timed steps at "
+                                   f"positions {P0 + (1 + nw) * T}..{L - 1}, L={L} keys, H={H}, D={D}, fp8, k={k}, "
+                                   f"sample = union of the last 3 steps' results",
+                       "T": T, "L": L, "H": H, "D": D, "topk": k},
+            "tokens_per_s": T / (graph_ms * 1e-3),
+            "launch": {"graph_us_per_step": round(graph_ms * 1e3, 2), "eager_us_per_step": round(eager_ms * 1e3, 2),
+                       "graph_same_sets_as_eager": graph_same},
+            "roofline": {"bound": "hbm", "achieved": round(scan_bytes / (scan_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "scan_kernel (fused score + filter)", "kernel_us": round(scan_ms * 1e3, 2),
+                         "algorithmic_bytes_per_launch": scan_bytes},
+            "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
+            "overflow_rows": st.overflow_rows,
+            "sample_hit_rate": round(float(np.mean(hits)), 4) if hits else None,
+            "same_index_sets_as_unfused": same_unfused,
+            "cpu_baseline": oracle}
+    print(json.dumps(line), flush=True)
+
+
+def _cores() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +387,8 @@ def main():
         return bench_prefill_chunks(args)
     if cfg["kind"] == "retrieval":
         return bench_retrieval(args)
+    if cfg["kind"] == "decode":
+        return bench_decode(args)
     log(f"generating workload {args.workload} ...")
     t0 = time.perf_counter()
     inp = indexer_workload(args.workload, with_prev=True)

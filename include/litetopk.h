@@ -72,6 +72,9 @@ typedef struct {
     int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072) */
     void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan kernel */
     void* scan_event_stop;  /* optional hipEvent_t recorded just after it (profiling; NULL = none) */
+    int32_t shared_threshold; /* indexer: key splits of a query share one threshold histogram in the
+                                 workspace (decode: few queries over a long context); 0 = when the
+                                 scan has >= 16 splits, > 0 = always, < 0 = never */
 } ltk_opts;
 
 /* Optional counters (DEVICE struct, written by the call; pass NULL to skip). */
@@ -97,6 +100,9 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
  *  w        [T, H] fp32 head weights (>= 0)
  *  pos      [T] int32 query positions; keys 0..pos[t] (and < L) are valid
  *  T >= 0, 1 <= H <= 64, D in {64, 128}, 1 <= L < 2^31, 1 <= topk <= 65536
+ *           (a decode or speculative-decode step is the same call with T = 1..8
+ *           queries at the newest positions; the key range is then split over
+ *           every CU and the splits share one threshold per query)
  *  sample   [n_sample] int32 key indices reused from the previous chunk's
  *           result (the pages reuse its top-3k); may be NULL if n_sample == 0
  *  out_idx  [T, topk] int32 result; -1 padded

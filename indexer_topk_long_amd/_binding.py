@@ -17,7 +17,7 @@ _c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, c
 class _COpts(ctypes.Structure):
     _fields_ = [("nbins", _c_i32), ("refresh_every", _c_i32), ("l_splits", _c_i32),
                 ("sorted_output", _c_i32), ("cand_capacity", _c_i64),
-                ("scan_event_start", _c_p), ("scan_event_stop", _c_p)]
+                ("scan_event_start", _c_p), ("scan_event_stop", _c_p), ("shared_threshold", _c_i32)]
 
 
 @dataclass
@@ -30,10 +30,11 @@ class Opts:
     cand_capacity: int = 0
     scan_event_start: int | None = None   # raw hipEvent_t handles (profiling)
     scan_event_stop: int | None = None
+    shared_threshold: int = 0             # 0 auto (>= 16 key splits), 1 always, -1 never
 
     def c(self) -> _COpts:
         return _COpts(self.nbins, self.refresh_every, self.l_splits, int(bool(self.sorted_output)),
-                      self.cand_capacity, self.scan_event_start, self.scan_event_stop)
+                      self.cand_capacity, self.scan_event_start, self.scan_event_stop, self.shared_threshold)
 
 
 @dataclass

@@ -1,5 +1,6 @@
 // api.hip -- the C ABI declared in include/litetopk.h: argument checks,
 // workspace carving and kernel launches on the caller's stream.
+#include <algorithm>
 #include <atomic>
 #include <string.h>
 
@@ -26,8 +27,9 @@ static int device_check() {
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Opts {
-    int nbins, refresh_every, l_splits, sorted;
+    int nbins, refresh_every, l_splits, sorted, shared;
     int64_t ccap;
+    bool ccap_given;
     hipEvent_t ev0, ev1;
 };
 
@@ -36,7 +38,9 @@ static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
     r.refresh_every = 1;
     r.l_splits = 0;
     r.sorted = 0;
+    r.shared = 0;
     r.ccap = default_ccap;
+    r.ccap_given = false;
     r.ev0 = r.ev1 = nullptr;
     if (!o) return LTK_OK;
     r.ev0 = static_cast<hipEvent_t>(o->scan_event_start);
@@ -49,6 +53,8 @@ static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
     r.sorted = o->sorted_output != 0;
     if (o->cand_capacity < 0 || o->cand_capacity > (int64_t)1 << 31) return LTK_EINVAL;
     if (o->cand_capacity) r.ccap = o->cand_capacity;
+    r.ccap_given = o->cand_capacity != 0;
+    r.shared = o->shared_threshold;
     return LTK_OK;
 }
 
@@ -62,17 +68,39 @@ static int check_indexer_sizes(int32_t T, int32_t H, int32_t D, int64_t L, int32
     return LTK_OK;
 }
 
-// Key-range splits so that a launch holds at least ~2048 workgroups when the
-// context is long enough (each split keeps >= 16384 keys).
+// Key splits of the fused scan: about 2048 workgroups of at least 16K keys;
+// below one workgroup per CU (decode: a handful of queries), splits go down to
+// 4K keys so that all 256 CUs stream the context.
 static int auto_splits(int nqg, int64_t L, int requested) {
     if (requested > 0) return requested;
     int s = 1;
-    while ((int64_t)nqg * s < 2048 && L / (s * 2) >= 16384) s *= 2;
+    while ((int64_t)nqg * s < 2048 && L / (s * 2) >= ((int64_t)nqg * s < 256 ? 4096 : 16384)) s *= 2;
     return s;
 }
 
 // Queries per scan workgroup: 8 waves x 1 query.
 static int scan_qpg(int) { return 8; }
+
+// Splits from which the fused scan shares one threshold histogram per query
+// across its splits (the decode shape: few queries, hundreds of splits, no
+// split holding k passing keys on its own).
+constexpr int kSharedSplitMin = 16;
+
+// What a fused indexer call will launch, fixed by its sizes and options
+// alone, so that litetopk_workspace_bytes and the call agree.
+struct IdxPlan {
+    int n_splits;
+    bool shared;     // shared per-query histograms in the workspace
+    int64_t ccap;    // candidate slots per query
+};
+static IdxPlan indexer_plan(int32_t T, int64_t L, int32_t dtype, const Opts& o) {
+    IdxPlan p;
+    p.n_splits = auto_splits((T + scan_qpg(dtype) - 1) / scan_qpg(dtype), L, o.l_splits);
+    p.shared = o.shared > 0 || (o.shared == 0 && p.n_splits >= kSharedSplitMin);
+    // every split may write a few batches before the shared counts reach k
+    p.ccap = (p.shared && !o.ccap_given) ? std::max<int64_t>(o.ccap, (int64_t)p.n_splits * 256) : o.ccap;
+    return p;
+}
 
 // Shared retrieval histograms: nbins fine counters + one per 16-bin super-bin, per query.
 // Retrieval database splits: the caller's count, else about 2048 workgroups
@@ -116,11 +144,13 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
         return align_up((size_t)T * (size_t)L * 4, 256);
     }
     if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
-    (void)H; (void)D; (void)dtype;
+    (void)H; (void)D;
     Opts o;
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? kDefaultCcapRetrieve : kDefaultCcap, o) != LTK_OK) return 0;
-    return ws_layout(T, L, n_sample, o.ccap,
-                     kind == LTK_KIND_RETRIEVE ? retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits)) : 0).total;
+    if (kind == LTK_KIND_RETRIEVE)
+        return ws_layout(T, L, n_sample, o.ccap, retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
+    const IdxPlan p = indexer_plan(T, L, dtype, o);
+    return ws_layout(T, L, n_sample, p.ccap, p.shared ? (size_t)T * o.nbins : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -138,7 +168,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     Opts o;
     if ((st = resolve_opts(opts, kDefaultCcap, o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
-    const WsLayout lay = ws_layout(T, L, n_sample, o.ccap);
+    const IdxPlan plan = indexer_plan(T, L, dtype, o);
+    const WsLayout lay = ws_layout(T, L, n_sample, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0);
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -158,16 +189,17 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.nbins = o.nbins;
     a.n_sample = n_sample > 0 ? n_sample : 1;
     const int nqg = (T + kQPG - 1) / kQPG;
-    a.n_splits = auto_splits((T + scan_qpg(dtype) - 1) / scan_qpg(dtype), L, o.l_splits);
+    a.n_splits = plan.n_splits;
     a.s_splits = 1;
     while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= 8) a.s_splits *= 2;
     a.refresh_every = o.refresh_every;
     a.sorted = o.sorted;
-    a.ccap = o.ccap;
+    a.ccap = plan.ccap;
     a.tail = reinterpret_cast<uint32_t*>(wsb + lay.tail);
     a.flags = reinterpret_cast<uint32_t*>(wsb + lay.flags);
     a.nu = reinterpret_cast<uint32_t*>(wsb + lay.nu);
     a.bitmap = reinterpret_cast<uint32_t*>(wsb + lay.bitmap);
+    a.hist_g = plan.shared ? reinterpret_cast<uint32_t*>(wsb + lay.hist) : nullptr;
     a.meta = wsb + lay.meta;
     a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
     a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     Meta m{0.0f, 1.0f, 0, 0};
     if (tv) m = reinterpret_cast<const Meta*>(a.meta)[t];
     int thr = m.thr0;
-    float tau = tau_of(thr, m.smin, m.delta, nbins);
+    float tau = tv ? initial_gate(thr, m, nbins, a.topk) : -INFINITY;
 
     QueryRegs<DT, D, HB> ra, rb;
     load_query<DT, D, HB>(ra, a, s0);
@@ -368,10 +368,30 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         if (lane < rem) st[lane] = r;
         cnt[s] = rem;
         ++fl[s];
+        uint32_t* hl = hist + lq * nbins;
+        uint32_t* hg = a.hist_g ? a.hist_g + (size_t)tq * nbins : nullptr;
+        if (hg) {
+            // shared threshold: move the counts gathered since the last flush
+            // into the query's histogram in device memory (the LDS copy then
+            // holds only what this wave has not yet added there)
+            for (int b = lane; b < nbins; b += 64) {
+                const uint32_t v = hl[b];
+                if (v) {
+                    atomicAdd(&hg[b], v);
+                    hl[b] = 0u;
+                }
+            }
+        }
         wait_vm<0>();   // keep the in-flight vector-memory ops to tile loads only
         if (a.refresh_every > 0 && fl[s] % a.refresh_every == 0) {
-            // top-down recount; a plain overwrite that can only raise the threshold
-            const SuffixPick p = suffix_pick(hist + lq * nbins, nbins, k);
+            // top-down recount (of every split's counts, when shared); a plain
+            // overwrite that can only raise the threshold.  Counts cover real
+            // causal keys only, so the new bin is at most the true one.
+            if (hg)
+                for (int b = lane; b < nbins; b += 64) hl[b] = __hip_atomic_load(&hg[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const SuffixPick p = suffix_pick(hl, nbins, k);
+            if (hg)
+                for (int b = lane; b < nbins; b += 64) hl[b] = 0u;
             if (QPW == 1 || half == s) {
                 if (p.bin > thr) {
                     thr = p.bin;

@@ -29,7 +29,8 @@ struct WsLayout {
 };
 
 // hist_words: 32-bit counters of the histograms shared across workgroups
-// (retrieval: T x (nbins + super-bins)); 0 for the indexer.
+// (retrieval: T x (nbins + super-bins) + T x splits; indexer: T x nbins when
+// its splits share thresholds, else 0).
 inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0) {
     WsLayout w{};
     size_t o = 0;
@@ -68,6 +69,7 @@ struct IdxArgs {
     uint32_t* flags;
     uint32_t* nu;
     uint32_t* bitmap;
+    uint32_t* hist_g;        // [T][nbins] threshold histograms shared by the key splits, or null
     void* meta;              // Meta[T]
     int32_t* sample_u;
     float* sscore;

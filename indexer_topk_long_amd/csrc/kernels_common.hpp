@@ -76,6 +76,16 @@ __device__ __forceinline__ float tau_of(int thr, float smin, float delta, int nb
     return unord_f32(hi);
 }
 
+// Initial gate of a query: the gate of its threshold bin, except that bin 0
+// also counts every score below the sample's minimum (the bin map clamps them
+// for counting).  When at least k valid sample keys scored >= smin, no key
+// scoring below smin can be in the top-k, so bin 0 gates at smin itself.
+// Sample and scan score a key bit-identically, so the sample's own keys pass.
+__device__ __forceinline__ float initial_gate(int thr, const Meta& m, int nbins, int k) {
+    if (thr <= 0) return (m.nvalid >= k) ? m.smin : -INFINITY;
+    return tau_of(thr, m.smin, m.delta, nbins);
+}
+
 // Block-wide bitonic sort (descending) of n <= cap 64-bit keys in LDS.
 __device__ inline void block_sort_desc(uint64_t* keys, int n) {
     int p2 = 1;

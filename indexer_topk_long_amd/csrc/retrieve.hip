@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float* my_tau = tau_l + wave * kRetrQ;
     uint32_t* my_cnt = cnt_l + wave * kRetrQ;
     if (lane < 32) {
-        my_tau[lane] = own_valid ? tau_of(thr_own, m_own.smin, m_own.delta, a.nbins) : INFINITY;
+        my_tau[lane] = own_valid ? initial_gate(thr_own, m_own, a.nbins, a.topk) : INFINITY;
         my_cnt[lane] = 0u;
         smin_l[wave * kRetrQ + lane] = m_own.smin;
         delta_l[wave * kRetrQ + lane] = m_own.delta;

@@ -36,7 +36,8 @@ def test_header_is_c_and_matches_binding_layout(tmp_path):
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "litetopk.h"\n'
         'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(ltk_opts), offsetof(ltk_opts, cand_capacity),'
-        ' offsetof(ltk_opts, scan_event_stop), sizeof(ltk_stats), offsetof(ltk_stats, overflow_rows)); return 0;}\n')
+        ' offsetof(ltk_opts, scan_event_stop), sizeof(ltk_stats), offsetof(ltk_stats, overflow_rows));'
+        ' printf("%zu\\n", offsetof(ltk_opts, shared_threshold)); return 0;}\n')
     exe = tmp_path / "probe"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", B.INCLUDE, str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
@@ -44,12 +45,29 @@ def test_header_is_c_and_matches_binding_layout(tmp_path):
     assert got[0] == ctypes.sizeof(_COpts)
     assert got[1] == _COpts.cand_capacity.offset and got[2] == _COpts.scan_event_stop.offset
     assert got[3] == 16 and got[4] == 12     # Stats: u64 + u32 + u32, read as two int64 by the binding
+    assert got[5] == _COpts.shared_threshold.offset
 
 
 def test_strerror(L):
     for code in (OK, EINVAL, EUNSUP, EWS, EHIP):
         assert len(ltk.strerror(code)) >= 2 and ltk.strerror(code) != "unknown status"
     assert ltk.strerror(12345) == "unknown status"
+
+
+def test_workspace_decode_shape_reserves_shared_histograms(L):
+    # one fp8 query over 128K keys: 32 splits of 4K keys share T x nbins counters
+    # and get at least 256 candidate slots per split
+    ws = lambda o=None: ltk.workspace_bytes(0, 1, 64, 128, 131072, 2048, 2048, 2, o)
+    on, off = ws(), ws(ltk.Opts(shared_threshold=-1))
+    assert on - off >= 32 * 256 * 8 - 16384 * 8 + 256 * 4 - 256
+    assert ws(ltk.Opts(shared_threshold=1)) == on
+    # an explicit capacity is kept; sharing then adds only the histograms
+    c_on = ws(ltk.Opts(cand_capacity=4096))
+    c_off = ws(ltk.Opts(cand_capacity=4096, shared_threshold=-1))
+    assert 0 < c_on - c_off <= 1024 + 256
+    # a prefill chunk (2 splits) does not share
+    p = lambda o=None: ltk.workspace_bytes(0, 8192, 64, 128, 1 << 20, 2048, 6144, 2, o)
+    assert p() == p(ltk.Opts(shared_threshold=-1)) < p(ltk.Opts(shared_threshold=1))
 
 
 def test_workspace_sizes(L):

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle import decode, indexer_row_scores, oracle_indexer
-from workloads import WORKLOADS, indexer_inputs, indexer_workload, retrieval_inputs, to_storage
+from workloads import WORKLOADS, indexer_inputs, indexer_keys, indexer_workload, retrieval_inputs, to_storage
 
 
 def test_tiny_workload_shapes():
@@ -81,3 +81,10 @@ def test_retrieval_generator_small():
     assert len(np.unique(r["sample"])) == 30
     r2 = retrieval_inputs(T=16, N=5000, D=64, topk=10, n_centres=20, sigma=0.3, n_sample=30, block=1000)
     assert (r2["db"] == r["db"]).all()
+
+
+def test_indexer_keys_match_the_workload():
+    k, ks = indexer_keys("tiny-4k-fp32")
+    full = indexer_workload("tiny-4k-fp32")
+    assert np.array_equal(k, full["k"]) and ks is None
+    assert all(WORKLOADS[c["keys"]]["kind"] == "indexer" for c in WORKLOADS.values() if c["kind"] == "decode")

@@ -1,0 +1,151 @@
+"""Decode and speculative-decode steps (LiteTopK pages, "Significance": the
+method is said to extend to decode and speculative decoding).
+
+A step is T = 1..8 queries at the newest positions of a long context.  Its
+key range is split over many workgroups whose per-query threshold
+histograms are shared in device memory.  Every row is checked against the
+oracle and the index sets are checked against the unfused path bit for bit.
+This is done with a good sample (the previous step's result), with a poor
+one (seeded random keys), with sharing forced on and off, over a chain of
+steps, and under HIP graph capture.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import canon, check_rows, say, to_dev
+from workloads import indexer_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _step_inputs(T, L, H, D, dt, k, nh, step, keys=None, tag=61):
+    """Queries of decode step `step` (0 = the newest T positions, -1 the T before, ...)."""
+    return indexer_inputs(T, L, H, D, dt, k, nh, drift=True, tag=tag, chunk=step, keys=keys, n_sample=6144)
+
+
+def _keys(inp):
+    return (inp["k"], inp["k_scale"], inp["hot"])
+
+
+CASES = [
+    # (T, L, H, D, dtype, k, n_hot, sample) -- 32 splits of 4K keys for L = 128K
+    (1, 131072, 64, 128, "fp8", 2048, 8192, "prev"),
+    (3, 131072, 64, 128, "fp8", 2048, 8192, "random"),
+    (8, 131072, 64, 128, "bf16", 512, 8192, "prev"),
+    (1, 70001, 20, 64, "f32", 100, 1000, "random"),    # 16 splits, ragged last split and tile
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"T{c[0]}_L{c[1]}_H{c[2]}_D{c[3]}_{c[4]}_k{c[5]}_{c[7]}")
+def test_decode_step_vs_oracle_and_unfused(lib, case):
+    import torch
+    T, L, H, D, dt, k, nh, smp = case
+    say("decode", case)
+    inp = _step_inputs(T, L, H, D, dt, k, nh, 0)
+    d = to_dev(inp)
+    if smp == "prev":
+        prev = _step_inputs(T, L, H, D, dt, k, nh, -1, keys=_keys(inp))
+        pd = to_dev(prev)
+        sample = lib.score_select(pd["q"], d["k"], pd["w"], pd["pos"], k, sample=pd["sample"], q_scale=pd["q_scale"],
+                                  k_scale=d["k_scale"]).reshape(-1)
+    else:
+        sample = d["sample"]
+    idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                   k_scale=d["k_scale"], return_scores=True, return_stats=True)
+    say("  candidates/query", st.cand_written / T, "max", st.max_cand_per_query, "overflow rows", st.overflow_rows)
+    if smp == "prev":
+        # k sample keys score >= the sample's minimum: the gate starts there, not at -inf
+        assert st.overflow_rows == 0
+    check_rows(inp, idx.cpu().numpy(), sc.cpu().numpy(), range(T), f"decode {case}")
+    uidx, usc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                         k_scale=d["k_scale"], return_scores=True)
+    gi, gs = canon(idx.cpu().numpy(), sc.cpu().numpy())
+    ui, us = canon(uidx.cpu().numpy(), usc.cpu().numpy())
+    assert np.array_equal(gi, ui)
+    assert np.array_equal(gs.view(np.uint32), us.view(np.uint32))   # bit-identical scores
+    # sharing the threshold changes the work, never the result
+    for shared in (1, -1):
+        o = lib.Opts(shared_threshold=shared)
+        idx2, st2 = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                     k_scale=d["k_scale"], opts=o, return_stats=True)
+        say(f"  shared={shared}: candidates/query", st2.cand_written / T, "overflow rows", st2.overflow_rows)
+        assert np.array_equal(canon(idx2.cpu().numpy()), gi)
+
+
+def test_decode_shared_threshold_small_splits(lib):
+    """Sharing forced on with a handful of uneven splits and a tiny k: every split
+    flushes and refreshes from the shared counts many times."""
+    T, L, H, D, dt, k = 3, 5000, 20, 64, "f32", 64
+    inp = indexer_inputs(T, L, H, D, dt, k, 300, drift=True, tag=62, n_sample=96)
+    d = to_dev(inp)
+    o = lib.Opts(shared_threshold=1, l_splits=7)
+    idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=d["sample"], opts=o,
+                                   return_scores=True, return_stats=True)
+    check_rows(inp, idx.cpu().numpy(), sc.cpu().numpy(), range(T), "shared 7 splits")
+    o2 = lib.Opts(shared_threshold=-1, l_splits=7)
+    idx2, st2 = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=d["sample"], opts=o2,
+                                 return_stats=True)
+    assert np.array_equal(canon(idx.cpu().numpy()), canon(idx2.cpu().numpy()))
+    say("  shared", st.cand_written, "unshared", st2.cand_written)
+
+
+def test_decode_chain_of_steps(lib):
+    """Four speculative-decode steps of T = 4: each step's sample is the previous step's result."""
+    T, L, H, D, dt, k, nh = 4, 65536, 64, 128, "fp8", 1024, 4096
+    first = _step_inputs(T, L, H, D, dt, k, nh, -4, tag=63)
+    keys = _keys(first)
+    inp = first
+    sample = to_dev(first)["sample"]
+    for s in range(-4, 0):
+        if s > -4:
+            inp = _step_inputs(T, L, H, D, dt, k, nh, s, keys=keys, tag=63)
+        d = to_dev(inp)
+        idx = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                               k_scale=d["k_scale"])
+        check_rows(inp, idx.cpu().numpy(), None, range(T), f"chain step {s}")
+        sample = idx.reshape(-1)
+
+
+def test_decode_graph_capture_replays(lib):
+    """Three decode steps captured as one HIP graph: every replay, with eager work
+    and synchronisations in between, equals the eager chain."""
+    import torch
+    T, L, H, D, dt, k, nh = 2, 65536, 64, 128, "fp8", 512, 4096
+    ins = [_step_inputs(T, L, H, D, dt, k, nh, -3, tag=64)]
+    keys = _keys(ins[0])
+    ins += [_step_inputs(T, L, H, D, dt, k, nh, s, keys=keys, tag=64) for s in (-2, -1)]
+    ds = [to_dev(x) for x in ins]
+    kk, ks = ds[0]["k"], ds[0]["k_scale"]
+    ws = torch.empty(lib.workspace_bytes(lib.KIND_SCORE_SELECT, T, H, D, L, k, 6144, 2), dtype=torch.uint8,
+                     device="cuda")
+
+    def chain(sample):
+        outs = []
+        for d in ds:
+            sample = lib.score_select(d["q"], kk, d["w"], d["pos"], k, sample=sample.reshape(-1),
+                                      q_scale=d["q_scale"], k_scale=ks, workspace=ws)
+            outs.append(sample)
+        return outs
+
+    s0 = ds[0]["sample"].clone()
+    eager = [o.clone() for o in chain(s0)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain(s0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gouts = chain(s0)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(gouts, eager):   # row order follows atomic order: compare the sets
+            assert np.array_equal(canon(a.cpu().numpy()), canon(b.cpu().numpy())), f"replay {rep}"
+        # eager work on the same workspace between replays
+        lib.score_select(ds[1]["q"], kk, ds[1]["w"], ds[1]["pos"], k, sample=s0, q_scale=ds[1]["q_scale"],
+                         k_scale=ks, workspace=ws)
+        torch.cuda.synchronize()
+    check_rows(ins[2], gouts[2].cpu().numpy(), None, range(T), "graph replay, last step")

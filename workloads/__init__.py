@@ -6,6 +6,7 @@ rounds them to the storage formats the kernels read.
 from .gen import (  # noqa: F401
     INDEXER_WORKLOADS,
     WORKLOADS,
+    indexer_keys,
     indexer_workload,
     indexer_inputs,
     prefill_queries,

@@ -43,6 +43,11 @@ WORKLOADS = {
                            topk=2048, n_hot=65536, drift=True, w_range=(0.0, 1.0), n_sample=6144),
     "retrieval-8m-d768-bf16": dict(kind="retrieval", tag=4, T=1024, N=8_000_000, D=768,
                                    dtype="bf16", topk=1024, n_centres=1000, sigma=0.3, n_sample=3072),
+    # Decode over the 1M-context keys: T queries at the newest positions per
+    # step (one new token, or one plus seven draft tokens verified together),
+    # each step's sample being the previous step's result.
+    "decode-1m-fp8": dict(kind="decode", keys="prefill-1m-fp8", T=1),
+    "specdecode-1m-fp8": dict(kind="decode", keys="prefill-1m-fp8", T=8),
 }
 INDEXER_WORKLOADS = [n for n, c in WORKLOADS.items() if c["kind"] == "indexer"]
 
@@ -188,6 +193,16 @@ def indexer_workload(name: str, chunk: int = 0, seed: int = SEED_BASE, with_prev
                            n_sample=c["n_sample"], keys=(out["k"], out["k_scale"], out["hot"]))
         out["prev"] = p
     return out
+
+
+def indexer_keys(name: str, seed: int = SEED_BASE):
+    """Keys of the named indexer workload alone (raw storage, per-key scales
+    or None), the same as ``indexer_workload(name)["k"]``."""
+    c = WORKLOADS[name]
+    assert c["kind"] == "indexer"
+    out = indexer_inputs(0, c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"], drift=c["drift"],
+                         w_range=c["w_range"], tag=c["tag"], seed=seed)
+    return out["k"], out["k_scale"]
 
 
 _S_PREFILL = 8   # stream id of the whole-prefill queries drawn on the device
