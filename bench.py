@@ -214,7 +214,7 @@ def bench_decode(args):
     kk = torch.from_numpy(kr).cuda().view(torch.float8_e4m3fn)
     ks = torch.from_numpy(ksr).cuda()
     del kr, ksr
-    nw, n = max(args.warmup, 3), args.steps
+    nw, n = args.warmup, args.steps
     total = 1 + nw + n                     # bootstrap, warmup, timed
     P0 = L - total * T
     qf = prefill_queries(base, device="cuda")
@@ -225,73 +225,84 @@ def bench_decode(args):
     n_boot = c["n_sample"]
     ws = torch.empty(ltk.workspace_bytes(ltk.KIND_SCORE_SELECT, T, H, D, L, k, max(3 * T * k, n_boot), 2),
                      dtype=torch.uint8, device="cuda")
+    # the last three results live in one ring [3, T, k]: step j writes slot j % 3
+    # and samples the whole ring (the call consumes its sample before it writes)
+    ring = torch.empty((3, T, k), dtype=torch.int32, device="cuda")
 
-    def step(j, hist, opts=None, **kw):
+    def step(j, sample, out, opts=None, **kw):
         q, w, qs, pos = steps[j]
-        sample = torch.cat([h.reshape(-1) for h in hist[-3:]])
-        return ltk.score_select(q, kk, w, pos, k, sample=sample, q_scale=qs, k_scale=ks, opts=opts,
-                                workspace=ws, **kw)
+        return ltk.score_select(q, kk, w, pos, k, sample=sample.reshape(-1), q_scale=qs, k_scale=ks, opts=opts,
+                                workspace=ws, out=out, **kw)
 
-    def run(j0, hist, count, opts=None):
+    def run(j0, count, opts=None, keep=True):
         outs = []
-        hist = list(hist)
         for i in range(count):
-            o = step(j0 + i, hist, opts[i] if opts else None)
-            outs.append(o)
-            hist = (hist + [o])[-3:]
+            j = j0 + i
+            o = step(j, ring, ring[j % 3], opts[i] if opts else None)
+            if keep:
+                outs.append(o.clone())
         return outs
 
-    # bootstrap step on a seeded random sample of the visible keys, then warmup
+    # bootstrap step on a seeded random sample of the visible keys fills every
+    # slot of the ring, then warmup
     boot = torch.from_numpy(random_sample(n_boot, P0, tag=c["tag"])).cuda()
-    hist = run(0, [boot], 1)
-    hist = (hist + run(1, hist, nw))[-3:]
-    hist0 = [h.clone() for h in hist]
+    first = step(0, boot, None)
+    ring.copy_(first.unsqueeze(0).expand(3, T, k))
+    run(1, nw, keep=False)
+    ring0 = ring.clone()
     torch.cuda.synchronize()
     ev = ltk.HipEvents(n)
     opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
     t0 = time.perf_counter()
-    eager = run(1 + nw, hist0, n, opts)
+    for i in range(n):
+        step(1 + nw + i, ring, ring[(1 + nw + i) % 3], opts[i])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / n
     scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(n)]))
     ev.close()
+    ring_eager = ring.clone()
     log(f"  eager: {eager_ms * 1e3:.1f} us/step, scan kernel {scan_ms * 1e3:.1f} us")
 
-    # the same n steps captured as one graph
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        run(1 + nw, hist0, n)
-    torch.cuda.current_stream().wait_stream(side)
+    # the results of every timed step, kept step by step (untimed), for the checks
+    ring.copy_(ring0)
+    eager = run(1 + nw, n)
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        gouts = run(1 + nw, hist0, n)
 
     def same_sets(a, b):
         return all(torch.equal(torch.sort(x, dim=1).values, torch.sort(y, dim=1).values) for x, y in zip(a, b))
 
+    # the same n steps captured as one graph (it starts from the ring the timed steps started from)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ring.copy_(ring0)
+        run(1 + nw, n, keep=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run(1 + nw, n, keep=False)
+    ring.copy_(ring0)
     g.replay()
     torch.cuda.synchronize()
-    graph_same = same_sets(gouts, eager)
+    graph_same = same_sets(ring, ring_eager)
     reps = 5
     t0 = time.perf_counter()
     for _ in range(reps):
-        g.replay()
+        g.replay()   # each replay continues from the ring the previous one left (steps of the same positions)
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t0) * 1e3 / (reps * n)
-    graph_same = graph_same and same_sets(gouts, eager)
     log(f"  graph: {graph_ms * 1e3:.1f} us/step, same as eager: {graph_same}")
 
     # figures of the last timed step
     jl = nw + n
-    hl = (hist0 + eager)[-4:-1]
-    _, st = step(jl, hl, return_stats=True)
+    allh = [ring0[(1 + nw + i) % 3] for i in range(-3, 0)] + eager   # results, oldest first
+    _, st = step(jl, torch.stack(allh[-4:-1]), torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                 return_stats=True)
     pos_last = steps[jl][3].cpu().numpy().astype(np.int64)
     pairs = int(np.sum(pos_last + 1))
     visible = int(pos_last.max()) + 1
     scan_bytes = visible * (D + 4) + T * H * D + T * H * 4 + T * 4
-    allh = hist0 + eager
     hits = [float(torch.isin(allh[i], torch.cat([h.reshape(-1) for h in allh[i - 3:i]])).float().mean())
             for i in range(3, len(allh))]
     uout = ltk.unfused_score_select(steps[jl][0], kk, steps[jl][1], steps[jl][3], k, q_scale=steps[jl][2],

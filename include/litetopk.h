@@ -69,7 +69,8 @@ typedef struct {
     int32_t refresh_every;  /* threshold refresh after every N candidate batches; default 1; <0 = never */
     int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
     int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
-    int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072) */
+    int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072;
+                               shared thresholds: L when T x L x 8 B <= 512 MiB, else >= 256 per split) */
     void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan kernel */
     void* scan_event_stop;  /* optional hipEvent_t recorded just after it (profiling; NULL = none) */
     int32_t shared_threshold; /* indexer: key splits of a query share one threshold histogram in the
@@ -104,7 +105,9 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
  *           queries at the newest positions; the key range is then split over
  *           every CU and the splits share one threshold per query)
  *  sample   [n_sample] int32 key indices reused from the previous chunk's
- *           result (the pages reuse its top-3k); may be NULL if n_sample == 0
+ *           result (the pages reuse its top-3k); may be NULL if n_sample == 0.
+ *           The first kernels of the call consume it, so it may overlap
+ *           out_idx (a decode loop can keep its last results in one ring)
  *  out_idx  [T, topk] int32 result; -1 padded
  *  out_score[T, topk] fp32 scores of out_idx (NaN where padded), or NULL
  *  ws       workspace of ws_bytes >= litetopk_workspace_bytes(LTK_KIND_SCORE_SELECT, ...)

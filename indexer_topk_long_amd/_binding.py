@@ -154,13 +154,14 @@ def _read_stats(buf) -> Stats:
 
 
 def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=None, opts: Opts | None = None,
-                 return_scores: bool = False, return_stats: bool = False, workspace=None):
+                 return_scores: bool = False, return_stats: bool = False, workspace=None, out=None):
     """Fused indexer top-k (litetopk_score_select).
 
     q [T, H, D] and k [L, D] in float32 / bfloat16 / float8_e4m3fn (fp8 needs
     q_scale [T] and k_scale [L] fp32); w [T, H] fp32; pos [T] int32; sample
     int32 key indices (the previous chunk's top-3k).  Returns int32 [T, topk]
-    (-1 padded), plus fp32 scores and/or Stats when asked.
+    (-1 padded; written into ``out`` when given, which may overlap the
+    sample), plus fp32 scores and/or Stats when asked.
     """
     import torch
     _dev(q, "q"), _dev(k, "k"), _dev(w, "w", torch.float32), _dev(pos, "pos", torch.int32)
@@ -180,7 +181,12 @@ def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=Non
     if nbytes == 0:
         raise LtkError(-1, "litetopk_workspace_bytes")
     ws = _workspace(nbytes, q.device, workspace)
-    out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    if out is None:
+        out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    elif tuple(out.shape) != (T, topk):
+        raise ValueError(f"out must be [{T}, {topk}]")
+    else:
+        _dev(out, "out", torch.int32)
     osc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
     st = _stats_buf(q.device) if return_stats else None
     rc = lib.litetopk_score_select(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(pos), T, H, D, L,

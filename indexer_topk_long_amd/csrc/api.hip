@@ -97,8 +97,13 @@ static IdxPlan indexer_plan(int32_t T, int64_t L, int32_t dtype, const Opts& o) 
     IdxPlan p;
     p.n_splits = auto_splits((T + scan_qpg(dtype) - 1) / scan_qpg(dtype), L, o.l_splits);
     p.shared = o.shared > 0 || (o.shared == 0 && p.n_splits >= kSharedSplitMin);
-    // every split may write a few batches before the shared counts reach k
-    p.ccap = (p.shared && !o.ccap_given) ? std::max<int64_t>(o.ccap, (int64_t)p.n_splits * 256) : o.ccap;
+    // every split may write a few batches before the shared counts reach k; a
+    // few queries over a context whose every key fits (T x L x 8 B <= 512 MiB)
+    // get room for all of them, so no decode step ever overflows
+    p.ccap = o.ccap;
+    if (p.shared && !o.ccap_given)
+        p.ccap = ((int64_t)T * L * 8 <= ((int64_t)512 << 20)) ? std::max<int64_t>(o.ccap, L)
+                                                            : std::max<int64_t>(o.ccap, (int64_t)p.n_splits * 256);
     return p;
 }
 
@@ -191,7 +196,10 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     const int nqg = (T + kQPG - 1) / kQPG;
     a.n_splits = plan.n_splits;
     a.s_splits = 1;
-    while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= 8) a.s_splits *= 2;
+    // sample splits: about 512 workgroups of >= 8 key blocks, down to one block
+    // each while the queries alone fill fewer than 128 workgroups (decode)
+    while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= (nqg * a.s_splits < 128 ? 1 : 8))
+        a.s_splits *= 2;
     a.refresh_every = o.refresh_every;
     a.sorted = o.sorted;
     a.ccap = plan.ccap;

@@ -50,44 +50,113 @@ __global__ void sample_mark_kernel(const int32_t* sample, int n, int L, uint32_t
     }
 }
 
-// One workgroup of 1024 threads turns the bitmap into the sorted list of
-// distinct sample keys.
-__global__ __launch_bounds__(1024) void sample_compact_kernel(const uint32_t* bitmap, int nwords, int32_t* out,
-                                                              uint32_t* nu) {
-    __shared__ uint32_t wsum[16];
-    __shared__ uint32_t s_base;
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    if (tid == 0) s_base = 0;
+// Small samples: workgroup 0 (1024 threads) de-duplicates the sample through
+// an LDS hash table (open addressing, at least twice as many slots as
+// entries) into the list of distinct in-range keys, in no particular order;
+// the other workgroups clear [zero_begin, zero_end) of the workspace.
+constexpr uint32_t kHashEmpty = 0xffffffffu;
+
+__global__ __launch_bounds__(1024) void sample_prep_kernel(const int32_t* sample, int n, int L, int log2_slots,
+                                                           uint32_t* zero, size_t n_zero, ltk_stats* stats,
+                                                           int32_t* out, uint32_t* nu) {
+    const int tid = threadIdx.x;
+    if (blockIdx.x > 0) {
+        const size_t i0 = (size_t)(blockIdx.x - 1) * 1024 + tid;
+        for (size_t i = i0; i < n_zero; i += (size_t)(gridDim.x - 1) * 1024) zero[i] = 0u;
+        if (stats && i0 == 0) {
+            stats->cand_written = 0;
+            stats->max_cand_per_query = 0;
+            stats->overflow_rows = 0;
+        }
+        return;
+    }
+    extern __shared__ uint32_t tab[];   // [1 << log2_slots]
+    __shared__ uint32_t s_n;
+    const int slots = 1 << log2_slots, lane = lane_id();
+    for (int i = tid; i < slots; i += 1024) tab[i] = kHashEmpty;
+    if (tid == 0) s_n = 0u;
     __syncthreads();
-    for (int w0 = 0; w0 < nwords; w0 += 1024) {
-        const int i = w0 + tid;
-        uint32_t word = (i < nwords) ? bitmap[i] : 0u;
-        const uint32_t c = __popc(word);
-        uint32_t incl = c;
+    for (int i0 = 0; i0 < n; i0 += 1024) {
+        const int i = i0 + tid;
+        bool fresh = false;
+        uint32_t key = 0u;
+        if (i < n) {
+            const int s = sample[i];
+            if (s >= 0 && s < L) {
+                key = (uint32_t)s;
+                uint32_t h = (key * 2654435761u) >> (32 - log2_slots);
+                while (true) {   // terminates: fewer entries than slots
+                    const uint32_t old = atomicCAS(&tab[h], kHashEmpty, key);
+                    if (old == kHashEmpty) { fresh = true; break; }
+                    if (old == key) break;
+                    h = (h + 1u) & (uint32_t)(slots - 1);
+                }
+            }
+        }
+        const uint64_t m = __ballot(fresh);
+        uint32_t base = 0u;
+        if (lane == 0 && m) base = atomicAdd(&s_n, (uint32_t)__popcll(m));
+        base = __shfl(base, 0);
+        if (fresh) out[base + mbcnt(m)] = (int32_t)key;
+    }
+    __syncthreads();
+    if (tid == 0) *nu = s_n;
+}
+
+// Keys marked in each bitmap chunk (one workgroup per chunk).
+__global__ __launch_bounds__(256) void sample_count_kernel(const uint32_t* bitmap, int nwords, int chunk_log2,
+                                                           uint32_t* ccount) {
+    __shared__ uint32_t s_red[4];
+    const int c = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int w_end = min(nwords, (c + 1) << chunk_log2);
+    uint32_t cnt = 0;
+    for (int w = (c << chunk_log2) + tid; w < w_end; w += 256) cnt += __popc(bitmap[w]);
+    cnt = wave_sum_u32(cnt);
+    if (lane == 0) s_red[wave] = cnt;
+    __syncthreads();
+    if (tid == 0) ccount[c] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+// One workgroup per bitmap chunk writes the chunk's keys, in order, after the
+// keys of all earlier chunks: the sorted list of distinct sample keys.  The
+// last chunk's workgroup writes the total.
+__global__ __launch_bounds__(256) void sample_compact_kernel(const uint32_t* bitmap, int nwords, int chunk_log2,
+                                                             const uint32_t* ccount, int32_t* out, uint32_t* nu) {
+    __shared__ uint32_t s_red[4], s_wsum[4];
+    const int c = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    uint32_t part = 0;
+    for (int i = tid; i < c; i += 256) part += ccount[i];
+    part = wave_sum_u32(part);
+    if (lane == 0) s_red[wave] = part;
+    __syncthreads();
+    const uint32_t off = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const uint32_t mine = ccount[c];
+    if (c == (int)gridDim.x - 1 && tid == 0) *nu = off + mine;
+    if (mine == 0) return;
+    const int wpt = (1 << chunk_log2) >> 8;   // words per thread (>= 4)
+    const int w0 = (c << chunk_log2) + tid * wpt;
+    uint32_t cnt = 0;
+    for (int j = 0; j < wpt; ++j)
+        if (w0 + j < nwords) cnt += __popc(bitmap[w0 + j]);
+    uint32_t incl = cnt;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        if (lane == 63) wsum[wave] = incl;
-        __syncthreads();
-        uint32_t before = s_base;
-        uint32_t total = 0;
-        for (int w = 0; w < 16; ++w) {
-            if (w < wave) before += wsum[w];
-            total += wsum[w];
-        }
-        uint32_t o = before + incl - c;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t o = off + incl - cnt;
+    for (int w = 0; w < wave; ++w) o += s_wsum[w];
+    for (int j = 0; j < wpt; ++j) {
+        if (w0 + j >= nwords) break;
+        uint32_t word = bitmap[w0 + j];
         while (word) {
             const int b = __ffs(word) - 1;
-            out[o++] = i * 32 + b;
+            out[o++] = (w0 + j) * 32 + b;
             word &= word - 1;
         }
-        __syncthreads();
-        if (tid == 0) s_base += total;
-        __syncthreads();
     }
-    if (tid == 0) *nu = s_base;
 }
 
 // ---------------------------------------------------------------------------
@@ -183,38 +252,54 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
 __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];  // [nbins]
     __shared__ float s_min[4], s_max[4];
-    __shared__ int s_nvalid;
     const int t = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int nu = (int)*a.nu;
+    __shared__ uint32_t s_nv[4];
     const int pos_t = a.pos ? min(a.pos[t], a.L - 1) : a.L - 1;   // no positions: every key is valid
-    if (tid == 0) {  // number of sorted sample keys <= pos_t
-        int lo = 0, hi = nu;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (a.sample_u[mid] <= pos_t) lo = mid + 1; else hi = mid;
-        }
-        s_nvalid = lo;
-    }
-    for (int i = tid; i < a.nbins; i += 256) sh[i] = 0u;
-    __syncthreads();
-    const int nv = s_nvalid;
     const float* S = a.sscore + (size_t)t * a.n_sample;
+    // one pass: valid sample keys (<= pos_t; the list may be in any order)
+    // and their score range; up to kStatsRegs scores per thread stay in
+    // registers (NaN when invalid) for the histogram
+    constexpr int kStatsRegs = 16;
+    const bool in_regs = nu <= 256 * kStatsRegs;
+    float v[kStatsRegs];
+    uint32_t c = 0;
     float mn = INFINITY, mx = -INFINITY;
-    for (int j = tid; j < nv; j += 256) {
-        const float v = S[j];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kStatsRegs; ++i) {
+            const int j = tid + 256 * i;
+            const bool ok = j < nu && a.sample_u[j] <= pos_t;
+            v[i] = ok ? S[j] : NAN;
+            if (ok) {
+                ++c;
+                mn = fminf(mn, v[i]);
+                mx = fmaxf(mx, v[i]);
+            }
+        }
+    } else {
+        for (int j = tid; j < nu; j += 256) {
+            if (a.sample_u[j] <= pos_t) {
+                ++c;
+                mn = fminf(mn, S[j]);
+                mx = fmaxf(mx, S[j]);
+            }
+        }
     }
+    c = wave_sum_u32(c);
+    for (int i = tid; i < a.nbins; i += 256) sh[i] = 0u;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         mn = fminf(mn, __shfl_xor(mn, off));
         mx = fmaxf(mx, __shfl_xor(mx, off));
     }
     if (lane == 0) {
+        s_nv[wave] = c;
         s_min[wave] = mn;
         s_max[wave] = mx;
     }
     __syncthreads();
+    const int nv = (int)(s_nv[0] + s_nv[1] + s_nv[2] + s_nv[3]);
     float smin = fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3]));
     float smax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     if (nv == 0) {
@@ -225,7 +310,14 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
     const float floor_w = 1e-6f * fmaxf(1.0f, fabsf(smax));
     if (!(width >= floor_w)) width = floor_w;
     const float delta = (float)a.nbins / width;
-    for (int j = tid; j < nv; j += 256) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
+    if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kStatsRegs; ++i)
+            if (!__builtin_isnan(v[i])) atomicAdd(&sh[bin_of(v[i], smin, delta, a.nbins)], 1u);
+    } else {
+        for (int j = tid; j < nu; j += 256)
+            if (a.sample_u[j] <= pos_t) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
+    }
     __syncthreads();
     if (wave == 0) {
         int thr0 = 0;
@@ -246,17 +338,16 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 // ---------------------------------------------------------------------------
 //
 // One workgroup = 8 waves sharing K tiles that are streamed into LDS with
-// direct global->LDS loads (three 32 KB stages: one computed, two loading), so the
-// eight waves read each key from device memory once.  fp8 waves own two
-// queries (one per 32-lane half, both scored against the same 32 keys);
-// bf16/fp32 waves own one query scored against two 32-key blocks.  Two waves
-// per SIMD let one wave's VALU epilogue overlap the other's MFMAs.
+// direct global->LDS loads (32 KB tiles in three stages, four at decode
+// shape: one scored while the others load), so the eight waves read each key
+// from device memory once.  Each wave owns one query (at decode shape two or
+// four waves share one) and scores it against 32-key slots.  Two waves per
+// SIMD let one wave's VALU epilogue overlap the other's MFMAs.
 
 constexpr int kScanWaves = 8;
 constexpr int kTileBytes = 32768;
-constexpr int kScanStages = 3;     // tiles in flight: compute one, two loading
-
-template <int DT> struct ScanShape { static constexpr int QPW = 1; };
+constexpr int kScanStages = 3;     // tile stages at prefill shape: compute one, two loading
+constexpr int kScanStagesFew = 4;  // at decode shape (R > 1), where the key stream bounds the scan
 
 template <int DT, int D>
 struct TileGeom {
@@ -274,7 +365,9 @@ struct TileGeom {
 };
 
 // Issue this wave's share of the direct loads of the tile starting at key0.
-template <int DT, int D>
+// ASYNC: issued as inline assembly, ordered by the caller's own vmcnt waits
+// (the builtin form makes the compiler drain every load before each barrier).
+template <int DT, int D, bool ASYNC = false>
 __device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* st, int wave, int lane) {
     using G = TileGeom<DT, D>;
 #pragma unroll
@@ -284,14 +377,16 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* s
         const int r = p / G::CPR, pc = p % G::CPR;
         const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
         const int key = min(key0 + r, a.L - 1);
-        lds_direct16(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
+        if constexpr (ASYNC) lds_direct16_async(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
+        else lds_direct16(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
     }
     if constexpr (DT == DT_FP8) {
         // one per-key scale per lane (keys past the context re-read the last one)
 #pragma unroll
         for (int j = wave; j < G::TK / 64; j += kScanWaves) {
             const int key = min(key0 + j * 64 + lane, a.L - 1);
-            lds_direct4(a.k_scale + key, st + kTileBytes + j * 256);
+            if constexpr (ASYNC) lds_direct4_async(a.k_scale + key, st + kTileBytes + j * 256);
+            else lds_direct4(a.k_scale + key, st + kTileBytes + j * 256);
         }
     }
 }
@@ -307,25 +402,33 @@ __device__ __forceinline__ void read_frag(HalfRow<DT, D>& f, const uint8_t* st, 
     }
 }
 
-template <int DT, int D, int HB>
+// R waves per query: a workgroup holds kScanWaves / R queries, and the R
+// waves of a query take every R-th 64-key block of each tile.  R = 1 at
+// prefill shape; a decode step of one to four queries uses R = 4 or 2, so
+// that the waves score real queries instead of empty slots.
+template <int DT, int D, int HB, int R>
 __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     using G = TileGeom<DT, D>;
-    constexpr int QPW = ScanShape<DT>::QPW;
-    constexpr int QPG = kScanWaves * QPW;
+    constexpr int NST = (R > 1) ? kScanStagesFew : kScanStages;            // tile stages
+    constexpr bool ASYNC = R > 1;
+    constexpr int QPG = kScanWaves / R;
+    constexpr int NB = G::TK / 64;                                         // 64-key blocks per tile
+    static_assert(R >= 1 && NB % R == 0, "a tile's blocks split evenly over a query's waves");
     extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
     const int nbins = a.nbins;
-    uint8_t* tiles = shm;                                                  // kScanStages stages
-    uint32_t* hist = reinterpret_cast<uint32_t*>(shm + kScanStages * G::STAGE_BYTES);  // [QPG][nbins]
-    uint2* stage = reinterpret_cast<uint2*>(hist + QPG * nbins);           // [QPG][kStage]
-    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
+    uint8_t* tiles = shm;                                                  // NST stages
+    uint32_t* hist = reinterpret_cast<uint32_t*>(shm + NST * G::STAGE_BYTES);  // [waves][nbins]
+    uint2* stage = reinterpret_cast<uint2*>(hist + kScanWaves * nbins);    // [waves][kStage]
+    const int wave = threadIdx.x >> 6, lane = lane_id();
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int t0 = qg * QPG;
-    const int s0 = t0 + QPW * wave, s1 = s0 + (QPW - 1);                  // the wave's queries
-    const int t = (QPW == 2 && half) ? s1 : s0;                           // this lane's query
-    const int qi = QPW * wave + ((QPW == 2) ? half : 0);                  // its local index
+    const int t = t0 + wave / R;                                           // the wave's query
+    const int sub = wave % R;                                              // its blocks: sub, sub + R, ...
     const uint32_t k = (uint32_t)a.topk;
+    uint32_t* hl = hist + wave * nbins;                                    // the wave's own counts
+    uint2* stg = stage + wave * kStage;                                    // and staging list
 
-    for (int i = lane; i < QPW * nbins; i += 64) hist[QPW * wave * nbins + i] = 0u;
+    for (int i = lane; i < nbins; i += 64) hl[i] = 0u;
 
     // keys any query of the group can see, split into tile-aligned ranges
     int e = 0;
@@ -339,37 +442,32 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
 
     const bool tv = t < a.T;
     const int my_pos = tv ? min(a.pos[t], a.L - 1) : -1;
-    const int wave_end = min(k_hi, wave_max_i32(my_pos) + 1);
+    const int wave_end = min(k_hi, my_pos + 1);
     Meta m{0.0f, 1.0f, 0, 0};
     if (tv) m = reinterpret_cast<const Meta*>(a.meta)[t];
     int thr = m.thr0;
     float tau = tv ? initial_gate(thr, m, nbins, a.topk) : -INFINITY;
 
-    QueryRegs<DT, D, HB> ra, rb;
-    load_query<DT, D, HB>(ra, a, s0);
-    if constexpr (QPW == 2) load_query<DT, D, HB>(rb, a, s1);
+    QueryRegs<DT, D, HB> ra;
+    load_query<DT, D, HB>(ra, a, t);
+    if constexpr (ASYNC) drain_vm_loads();   // the loop's waits then cover tile loads only
 
-    int cnt[QPW] = {};   // staged entries per query (wave-uniform)
-    int fl[QPW] = {};    // batches written back per query
-    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    int cnt = 0;   // staged entries (wave-uniform)
+    int fl = 0;    // batches written back
 
-    auto flush = [&](int s) {
-        const int tq = s0 + s;
-        const int lq = QPW * wave + s;
-        uint2* st = stage + lq * kStage;
+    auto flush = [&]() {
         uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)kFlush);
+        if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)kFlush);
         base = __shfl(base, 0);
-        const uint2 en = st[lane];
-        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = en;
-        const int rem = cnt[s] - kFlush;
+        const uint2 en = stg[lane];
+        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
+        const int rem = cnt - kFlush;
         uint2 r{0u, 0u};
-        if (lane < rem) r = st[kFlush + lane];
-        if (lane < rem) st[lane] = r;
-        cnt[s] = rem;
-        ++fl[s];
-        uint32_t* hl = hist + lq * nbins;
-        uint32_t* hg = a.hist_g ? a.hist_g + (size_t)tq * nbins : nullptr;
+        if (lane < rem) r = stg[kFlush + lane];
+        if (lane < rem) stg[lane] = r;
+        cnt = rem;
+        ++fl;
+        uint32_t* hg = a.hist_g ? a.hist_g + (size_t)t * nbins : nullptr;
         if (hg) {
             // shared threshold: move the counts gathered since the last flush
             // into the query's histogram in device memory (the LDS copy then
@@ -383,7 +481,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
             }
         }
         wait_vm<0>();   // keep the in-flight vector-memory ops to tile loads only
-        if (a.refresh_every > 0 && fl[s] % a.refresh_every == 0) {
+        if (a.refresh_every > 0 && fl % a.refresh_every == 0) {
             // top-down recount (of every split's counts, when shared); a plain
             // overwrite that can only raise the threshold.  Counts cover real
             // causal keys only, so the new bin is at most the true one.
@@ -392,11 +490,9 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
             const SuffixPick p = suffix_pick(hl, nbins, k);
             if (hg)
                 for (int b = lane; b < nbins; b += 64) hl[b] = 0u;
-            if (QPW == 1 || half == s) {
-                if (p.bin > thr) {
-                    thr = p.bin;
-                    tau = tau_of(thr, m.smin, m.delta, nbins);
-                }
+            if (p.bin > thr) {
+                thr = p.bin;
+                tau = tau_of(thr, m.smin, m.delta, nbins);
             }
         }
     };
@@ -405,62 +501,47 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         const bool pass = (key <= my_pos) && (I >= tau);
         const uint64_t mask = __ballot(pass);
         if (mask) {
-            if (pass) atomicAdd(&hist[qi * nbins + bin_of(I, m.smin, m.delta, nbins)], 1u);
-            if constexpr (QPW == 2) {
-                const uint32_t ma = (uint32_t)mask, mb = (uint32_t)(mask >> 32);
-                if (pass) {
-                    const int rank = __popcll(mask & lt_mask & (half ? 0xffffffff00000000ull : 0xffffffffull));
-                    stage[qi * kStage + (half ? cnt[1] : cnt[0]) + rank] = make_uint2((uint32_t)key, __float_as_uint(I));
-                }
-                cnt[0] += __popc(ma);
-                cnt[1] += __popc(mb);
-                if (cnt[0] >= kFlush) flush(0);
-                if (cnt[1] >= kFlush) flush(1);
-            } else {
-                if (pass) stage[qi * kStage + cnt[0] + mbcnt(mask)] = make_uint2((uint32_t)key, __float_as_uint(I));
-                cnt[0] += __popcll(mask);
-                if (cnt[0] >= kFlush) flush(0);
+            if (pass) {
+                atomicAdd(&hl[bin_of(I, m.smin, m.delta, nbins)], 1u);
+                stg[cnt + mbcnt(mask)] = make_uint2((uint32_t)key, __float_as_uint(I));
             }
+            cnt += __popcll(mask);
+            if (cnt >= kFlush) flush();
         }
     };
 
     const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
     constexpr int LPW_HI = G::PER_WAVE + (G::SCALE_INST > 0 ? 1 : 0);   // loads per tile, waves < SCALE_INST
     constexpr int LPW_LO = G::PER_WAVE;                                  // loads per tile, other waves
-    if (ntiles > 0) load_tile<DT, D>(a, k_lo, tiles, wave, lane);
-    if (ntiles > 1) load_tile<DT, D>(a, k_lo + G::TK, tiles + G::STAGE_BYTES, wave, lane);
+    static_assert(NST == 3 || NST == 4, "two or three tiles load while one is scored");
+#pragma unroll
+    for (int j = 0; j < NST - 1; ++j)
+        if (j < ntiles) load_tile<DT, D, ASYNC>(a, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
     int sbuf = 0;   // stage holding tile `it`
     for (int it = 0; it < ntiles; ++it) {
-        if (it + 1 < ntiles) {   // tile it+1 may still be loading
-            if (wave < G::SCALE_INST) wait_vm<LPW_HI>(); else wait_vm<LPW_LO>();
+        // tile `it` has landed once at most the loads of the later tiles in
+        // flight remain (vector-memory operations complete in issue order)
+        const int later = min(NST - 2, ntiles - 1 - it);
+        if (wave < G::SCALE_INST) {
+            if (NST == 4 && later >= 2) wait_vm<2 * LPW_HI>(); else if (later >= 1) wait_vm<LPW_HI>(); else wait_vm<0>();
         } else {
-            wait_vm<0>();
+            if (NST == 4 && later >= 2) wait_vm<2 * LPW_LO>(); else if (later >= 1) wait_vm<LPW_LO>(); else wait_vm<0>();
         }
         __syncthreads();
-        if (it + 2 < ntiles) {
-            const int nb = (sbuf + 2) % kScanStages;
-            load_tile<DT, D>(a, k_lo + (it + 2) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
+        if (it + NST - 1 < ntiles) {   // into the stage every wave finished scoring before the barrier
+            const int nb = (sbuf + NST - 1) % NST;
+            load_tile<DT, D, ASYNC>(a, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
         }
         const int key0 = k_lo + it * G::TK;
         const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
-        sbuf = (sbuf + 1) % kScanStages;
+        sbuf = (sbuf + 1) % NST;
         const float* sks = reinterpret_cast<const float*>(st + kTileBytes);
-        if constexpr (QPW == 2) {
-#pragma unroll 1
-            for (int blk = 0; blk < G::TK / 32; ++blk) {
-                const int kb = key0 + 32 * blk;
-                if (kb >= wave_end) break;
-                HalfRow<DT, D> kf;
-                read_frag<DT, D>(kf, st, 32 * blk, lane);
-                float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-                if constexpr (DT == DT_FP8) I = I * sks[32 * blk + (lane & 31)];
-                process(I, kb + (lane & 31));
-            }
-        } else if constexpr (HalfRow<DT, D>::NV > 4) {
+        if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
+        if constexpr (HalfRow<DT, D>::NV > 4) {
             // wide fragments (bf16/fp32 at D = 128): the two 32-key slots of a
             // block one after the other, keeping one slot's registers live
 #pragma unroll 1
-            for (int blk = 0; blk < G::TK / 64; ++blk) {
+            for (int blk = sub; blk < NB; blk += R) {
                 const int kb = key0 + 64 * blk;
                 if (kb >= wave_end) break;
                 HalfRow<DT, D> kf;
@@ -478,46 +559,45 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         } else {
             // 32-key slots, software-pipelined: the MFMAs of slot s+1 are issued
             // before the ReLU*w reduction of slot s, so the matrix core and the
-            // VALU of one wave overlap; two slots make one 64-key block.
-            constexpr int NS = G::TK / 32;
+            // VALU of one wave overlap; two slots make one 64-key block.  The
+            // wave's slot j is half (j & 1) of block sub + R * (j / 2).
+            constexpr int NS = G::TK / 32 / R;
+            auto row0 = [&](int j) { return 64 * (sub + R * (j >> 1)) + 32 * (j & 1); };
             HalfRow<DT, D> kf;
             v16f accC[HB], accN[HB];
-            read_frag<DT, D>(kf, st, 0, lane);
+            read_frag<DT, D>(kf, st, row0(0), lane);
             mfma_1slot<DT, D, HB>(ra.q, kf, accC);
             float pprev = 0.0f;
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl) {
                 if (sl + 1 < NS) {
-                    read_frag<DT, D>(kf, st, 32 * (sl + 1), lane);
+                    read_frag<DT, D>(kf, st, row0(sl + 1), lane);
                     mfma_1slot<DT, D, HB>(ra.q, kf, accN);
                 }
                 const float p = relu_wsum<HB>(accC, ra.w);
                 if (sl & 1) {
+                    const int r0 = row0(sl - 1);
                     float I = combine_halves(pprev, p);
-                    if constexpr (DT == DT_FP8) I = I * sks[32 * (sl - 1) + lane];
-                    process(I, key0 + 32 * (sl - 1) + lane);
+                    if constexpr (DT == DT_FP8) I = I * sks[r0 + lane];
+                    process(I, key0 + r0 + lane);
                 } else {
                     pprev = p;
                 }
                 if (sl + 1 < NS) {
 #pragma unroll
-                    for (int m = 0; m < HB; ++m) accC[m] = accN[m];
+                    for (int mm = 0; mm < HB; ++mm) accC[mm] = accN[mm];
                 }
             }
         }
     }
-    // final partial batches
-#pragma unroll
-    for (int s = 0; s < QPW; ++s) {
-        if (cnt[s] > 0) {
-            const int tq = s0 + s;
-            uint32_t base = 0;
-            if (lane == 0) base = atomicAdd(&a.tail[tq], (uint32_t)cnt[s]);
-            base = __shfl(base, 0);
-            if (lane < cnt[s]) {
-                const uint2 en = stage[(QPW * wave + s) * kStage + lane];
-                if ((int64_t)base + lane < a.ccap) a.cand[(size_t)tq * a.ccap + base + lane] = en;
-            }
+    // final partial batch
+    if (cnt > 0) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)cnt);
+        base = __shfl(base, 0);
+        if (lane < cnt) {
+            const uint2 en = stg[lane];
+            if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
         }
     }
 }
@@ -526,16 +606,26 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
 // Select: finalize
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
-    extern __shared__ uint32_t sh[];   // [max(nbins, 256)] then (sorted) keys
+constexpr int kRankMax = 512;   // threshold-bin entries ranked in LDS by counting
+
+// 32-bit LDS words of the select's counters: max(nbins, 256), rounded up to even.
+__host__ __device__ inline int fin_words(int nbins) { return ((nbins > 256 ? nbins : 256) + 1) & ~1; }
+
+// Select of one row (LiteTopK pages, "Selection").  Returns true, with the
+// row's overflow flag set, when the candidate buffer overflowed and the row
+// must be recomputed.  LDS (sh): fin_words(nbins) counters, then kRankMax
+// rank keys and candidate entries, then the sort keys of a sorted output.
+__device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
     __shared__ int s_pick;
-    __shared__ uint32_t s_above, s_cnt, s_ocnt;
+    __shared__ uint32_t s_above, s_cnt, s_ocnt, s_mcnt;
     const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
     const int k = a.topk;
     const uint32_t n = a.tail[t];
     int32_t* out = a.out_idx + (size_t)t * k;
     float* osc = a.out_score ? a.out_score + (size_t)t * k : nullptr;
-    uint64_t* sort_keys = reinterpret_cast<uint64_t*>(sh + ((max(a.nbins, 256) + 1) & ~1));
+    uint64_t* rk = reinterpret_cast<uint64_t*>(sh + fin_words(a.nbins));        // [kRankMax]
+    uint2* rent = reinterpret_cast<uint2*>(rk + kRankMax);                        // [kRankMax]
+    uint64_t* sort_keys = reinterpret_cast<uint64_t*>(rent + kRankMax);
     if (tid == 0 && a.stats) {
         atomicAdd((unsigned long long*)&a.stats->cand_written, (unsigned long long)n);
         atomicMax(&a.stats->max_cand_per_query, n);
@@ -545,7 +635,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
             a.flags[t] = 1u;
             if (a.stats) atomicAdd(&a.stats->overflow_rows, 1u);
         }
-        return;
+        return true;
     }
     const uint2* c = a.cand + (size_t)t * a.ccap;
     if (n <= (uint32_t)k) {      // only when the row has at most k valid keys: keep them all
@@ -558,39 +648,98 @@ __global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
             if (osc) osc[i] = __builtin_nanf("");
         }
         if (a.sorted) sort_row_output(out, osc, k, sort_keys);
-        return;
+        return false;
     }
     const Meta m = reinterpret_cast<const Meta*>(a.meta)[t];
     const int nbins = a.nbins;
+    // up to kSelRegs candidates per thread are read once and kept in registers
+    constexpr int kSelRegs = 16;
+    const bool in_regs = n <= 256u * kSelRegs;
+    uint2 ce[kSelRegs];
+    if (in_regs) {
+#pragma unroll
+        for (int r = 0; r < kSelRegs; ++r) {
+            const uint32_t i = tid + 256u * r;
+            ce[r] = (i < n) ? c[i] : make_uint2(0u, 0u);
+        }
+    }
     uint32_t* hist = sh;
     for (int i = tid; i < nbins; i += 256) hist[i] = 0u;
-    if (tid == 0) s_ocnt = 0u;
+    if (tid == 0) {
+        s_ocnt = 0u;
+        s_mcnt = 0u;
+    }
     __syncthreads();
-    for (uint32_t i = tid; i < n; i += 256) atomicAdd(&hist[bin_of(__uint_as_float(c[i].y), m.smin, m.delta, nbins)], 1u);
+    if (in_regs) {
+#pragma unroll
+        for (int r = 0; r < kSelRegs; ++r)
+            if (tid + 256u * r < n) atomicAdd(&hist[bin_of(__uint_as_float(ce[r].y), m.smin, m.delta, nbins)], 1u);
+    } else {
+        for (uint32_t i = tid; i < n; i += 256)
+            atomicAdd(&hist[bin_of(__uint_as_float(c[i].y), m.smin, m.delta, nbins)], 1u);
+    }
     __syncthreads();
     if (wave == 0) {   // final threshold bin: top-down recount of the candidates' bins
         const SuffixPick p = suffix_pick(hist, nbins, (uint32_t)k);
         if (lane == 0) {
             s_pick = p.bin;
             s_above = p.above;
+            s_cnt = hist[p.bin];
         }
     }
     __syncthreads();
     const int bstar = s_pick;
     const uint32_t above = s_above;
-    // bins strictly above the final threshold bin go straight to the output
-    for (uint32_t i = tid; i < n; i += 256) {
-        const uint2 e = c[i];
+    const bool ranked = s_cnt <= (uint32_t)kRankMax;   // the threshold bin fits the LDS ranking
+    // bins strictly above the final threshold bin go straight to the output;
+    // a small threshold bin is gathered into LDS
+    auto emit = [&](const uint2 e) {
         const float I = __uint_as_float(e.y);
-        if (bin_of(I, m.smin, m.delta, nbins) > bstar) {
+        const int b = bin_of(I, m.smin, m.delta, nbins);
+        if (b > bstar) {
             const uint32_t p = atomicAdd(&s_ocnt, 1u);
             if (p < (uint32_t)k) {
                 out[p] = (int32_t)e.x;
                 if (osc) osc[p] = I;
             }
+        } else if (ranked && b == bstar) {
+            const uint32_t p = atomicAdd(&s_mcnt, 1u);   // < kRankMax: the bin holds s_cnt entries
+            if (p < (uint32_t)kRankMax) {
+                rk[p] = rank_key(I, (int)e.x);
+                rent[p] = e;
+            }
         }
+    };
+    if (in_regs) {
+#pragma unroll
+        for (int r = 0; r < kSelRegs; ++r)
+            if (tid + 256u * r < n) emit(ce[r]);
+    } else {
+        for (uint32_t i = tid; i < n; i += 256) emit(c[i]);
     }
-    // exact top-(k - above) inside the threshold bin: radix select on (score desc, index asc)
+    if (ranked) {
+        // exact top-(k - above) inside the threshold bin: an entry is taken when
+        // fewer than k - above entries of the bin rank before it (score desc,
+        // index asc; the keys are distinct)
+        __syncthreads();
+        const uint32_t mm = min(s_mcnt, (uint32_t)kRankMax), need = (uint32_t)k - above;
+        for (uint32_t i = tid; i < mm; i += 256) {
+            const uint64_t key = rk[i];
+            uint32_t r = 0;
+            for (uint32_t j = 0; j < mm; ++j) r += (rk[j] > key) ? 1u : 0u;
+            if (r < need) {
+                const uint2 e = rent[i];
+                const uint32_t p = atomicAdd(&s_ocnt, 1u);
+                if (p < (uint32_t)k) {
+                    out[p] = (int32_t)e.x;
+                    if (osc) osc[p] = __uint_as_float(e.y);
+                }
+            }
+        }
+        if (a.sorted) sort_row_output(out, osc, k, sort_keys);
+        return false;
+    }
+    // larger threshold bins: radix select on (score desc, index asc)
     uint64_t P = 0ull, mask = 0ull;
     uint32_t need = (uint32_t)k - above;
     uint32_t* h256 = sh;   // reuses the histogram space (nbins is no longer needed)
@@ -634,6 +783,13 @@ __global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
         }
     }
     if (a.sorted) sort_row_output(out, osc, k, sort_keys);
+    return false;
+}
+
+// Retrieval select (its own fallback kernel re-scores overflowed rows).
+__global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];
+    finalize_row(a, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -662,11 +818,14 @@ struct RescoreSource {
     }
 };
 
+// Indexer select: finalize, and for a row whose candidate buffer overflowed,
+// the exact select over re-computed scores in the same workgroup.
 template <int DT, int D, int HB>
-__global__ __launch_bounds__(256) void fallback_kernel(IdxArgs a) {
+__global__ __launch_bounds__(256) void select_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];
+    if (!finalize_row(a, sh)) return;
+    __syncthreads();
     const int t = blockIdx.x;
-    if (a.flags[t] == 0u) return;
     RescoreSource<DT, D, HB> src;
     load_query<DT, D, HB>(src.r, a, t);
     src.k = a.k;
@@ -757,6 +916,13 @@ static bool dispatch(int dt, int D, int HB, F&& f) {
     return false;
 }
 
+// Waves per query of the fused scan: 4 for one or two queries, 2 for three or
+// four, else 1; at most the number of 64-key blocks in a tile.
+static int scan_waves_per_query(int T, int nb) {
+    const int r = (T <= 2) ? 4 : (T <= 4) ? 2 : 1;
+    return std::min(r, nb);
+}
+
 static size_t sort_lds(const IdxArgs& a) {
     if (!a.sorted) return 0;
     int p2 = 1;
@@ -764,15 +930,9 @@ static size_t sort_lds(const IdxArgs& a) {
     return (size_t)p2 * 8;
 }
 
-hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
-                                 uint8_t* ws, hipStream_t st) {
-    const size_t nz = (lay.zero_end - lay.zero_begin) / 4;
-    const int zb = (int)std::min<size_t>((nz + 255) / 256, 2048);
-    zero_kernel<<<std::max(zb, 1), 256, 0, st>>>(reinterpret_cast<uint32_t*>(ws + lay.zero_begin), nz, a.stats);
-    if (n_sample > 0)
-        sample_mark_kernel<<<(n_sample + 255) / 256, 256, 0, st>>>(sample, n_sample, a.L, a.bitmap);
-    sample_compact_kernel<<<1, 1024, 0, st>>>(a.bitmap, (a.L + 31) / 32, a.sample_u, a.nu);
-    return hipGetLastError();
+// finalize_row's LDS: counters, the threshold bin's rank keys and positions, sort keys
+static size_t fin_lds_bytes(const IdxArgs& a) {
+    return (size_t)fin_words(a.nbins) * 4 + (size_t)kRankMax * 16 + sort_lds(a);
 }
 
 template <class K>
@@ -782,6 +942,35 @@ static void allow_lds(K kernel, size_t bytes) {
                                   (int)bytes);
 }
 
+hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
+                                 uint8_t* ws, hipStream_t st) {
+    if (n_sample <= kHashSampleMax) {
+        int lg = 10;
+        while ((1 << lg) < 2 * n_sample) ++lg;
+        const size_t nz = (lay.bitmap - lay.zero_begin) / 4;   // the bitmap is not used
+        const int zb = (int)std::min<size_t>((nz + 1023) / 1024, 512);
+        const size_t lds = (size_t)4 << lg;
+        allow_lds(sample_prep_kernel, lds);
+        sample_prep_kernel<<<1 + std::max(zb, 1), 1024, lds, st>>>(sample, n_sample, a.L, lg,
+                                                                     reinterpret_cast<uint32_t*>(ws + lay.zero_begin),
+                                                                     nz, a.stats, a.sample_u, a.nu);
+        return hipGetLastError();
+    }
+    const size_t nz = (lay.zero_end - lay.zero_begin) / 4;
+    const int zb = (int)std::min<size_t>((nz + 255) / 256, 2048);
+    zero_kernel<<<std::max(zb, 1), 256, 0, st>>>(reinterpret_cast<uint32_t*>(ws + lay.zero_begin), nz, a.stats);
+    const int lg = sample_chunk_log2(a.L);
+    uint32_t* ccount = reinterpret_cast<uint32_t*>(ws + lay.ccount);
+    const int nwords = (a.L + 31) / 32;
+    if (n_sample > 0) {
+        sample_mark_kernel<<<(n_sample + 255) / 256, 256, 0, st>>>(sample, n_sample, a.L, a.bitmap);
+        sample_count_kernel<<<sample_chunks(a.L), 256, 0, st>>>(a.bitmap, nwords, lg, ccount);
+    }
+    sample_compact_kernel<<<sample_chunks(a.L), 256, 0, st>>>(a.bitmap, nwords, lg, ccount, a.sample_u, a.nu);
+    return hipGetLastError();
+}
+
+
 hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
     const int nqg = (a.T + kQPG - 1) / kQPG;
     hipError_t err = hipSuccess;
@@ -789,19 +978,31 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
-        constexpr int QPG = kScanWaves * ScanShape<DT_>::QPW;
-        const size_t scan_lds = kScanStages * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + (size_t)QPG * a.nbins * 4 +
-                                (size_t)QPG * kStage * 8;
-        allow_lds(scan_kernel<DT_, D_, HB_>, scan_lds);
-        if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-        scan_kernel<DT_, D_, HB_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
-        if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
-        const size_t fin_lds = (size_t)((std::max(a.nbins, 256) + 1) & ~1) * 4 + sort_lds(a);
-        allow_lds(finalize_kernel, fin_lds);
-        finalize_kernel<<<a.T, 256, fin_lds, st>>>(a);
-        const size_t fb_lds = 256 * 4 + sort_lds(a);
-        allow_lds(fallback_kernel<DT_, D_, HB_>, fb_lds);
-        fallback_kernel<DT_, D_, HB_><<<a.T, 256, fb_lds, st>>>(a);
+        const size_t scan_fixed = (size_t)kScanWaves * a.nbins * 4 + (size_t)kScanWaves * kStage * 8;
+        constexpr int NB = TileGeom<DT_, D_>::TK / 64;
+        auto launch_scan = [&](auto Rc) {
+            constexpr int R_ = decltype(Rc)::value;
+            constexpr int QPG = kScanWaves / R_;
+            const size_t scan_lds = (R_ > 1 ? kScanStagesFew : kScanStages) * (size_t)TileGeom<DT_, D_>::STAGE_BYTES +
+                                    scan_fixed;
+            allow_lds(scan_kernel<DT_, D_, HB_, R_>, scan_lds);
+            if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
+            scan_kernel<DT_, D_, HB_, R_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
+            if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
+        };
+        // the decode-shape variants need room for four tile stages
+        const bool few_fits = kScanStagesFew * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + scan_fixed <= kMaxLds;
+        const int R = few_fits ? scan_waves_per_query(a.T, NB) : 1;
+        if constexpr (NB % 4 == 0) {
+            if (R == 4) launch_scan(ic<4>{});
+        }
+        if constexpr (NB % 2 == 0) {
+            if (R == 2) launch_scan(ic<2>{});
+        }
+        if (R == 1) launch_scan(ic<1>{});
+        const size_t sel_lds = std::max(fin_lds_bytes(a), 256 * 4 + sort_lds(a));
+        allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
+        select_kernel<DT_, D_, HB_><<<a.T, 256, sel_lds, st>>>(a);
         err = hipGetLastError();
     });
     return ok ? err : hipErrorInvalidValue;
@@ -813,7 +1014,7 @@ hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_finalize(const IdxArgs& a, hipStream_t st) {
-    const size_t fin_lds = (size_t)((std::max(a.nbins, 256) + 1) & ~1) * 4 + sort_lds(a);
+    const size_t fin_lds = fin_lds_bytes(a);
     allow_lds(finalize_kernel, fin_lds);
     finalize_kernel<<<a.T, 256, fin_lds, st>>>(a);
     return hipGetLastError();

@@ -21,12 +21,32 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS one gfx950 workgroup may allocat
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Sample de-duplication: a bitmap over the keys, cut into chunks of
+// 2^chunk_log2 words (at least 1024, doubled until there are at most 2048
+// chunks); a counting pass popcounts every chunk so that the chunks compact
+// in parallel.
+inline int sample_chunk_log2(int64_t L) {
+    const int64_t nw = (L + 31) / 32;
+    int lg = 10;
+    while ((nw + ((int64_t)1 << lg) - 1) >> lg > 2048) ++lg;
+    return lg;
+}
+inline int sample_chunks(int64_t L) {
+    const int lg = sample_chunk_log2(L);
+    return (int)(((L + 31) / 32 + ((int64_t)1 << lg) - 1) >> lg);
+}
+
 // Workspace of one fused call.  The [zero_begin, zero_end) range is cleared
 // by the first kernel of every call.
 struct WsLayout {
-    size_t tail, flags, nu, bitmap, hist, zero_begin, zero_end;
+    size_t tail, flags, nu, hist, bitmap, ccount, zero_begin, zero_end;
     size_t meta, sample_u, sscore, cand, total;
 };
+
+// Samples of at most this many entries are de-duplicated in one workgroup's
+// LDS hash table, with no key bitmap (the bitmap and its chunk counts, the
+// tail of the cleared range, then stay untouched).
+constexpr int kHashSampleMax = 16384;
 
 // hist_words: 32-bit counters of the histograms shared across workgroups
 // (retrieval: T x (nbins + super-bins) + T x splits; indexer: T x nbins when
@@ -38,8 +58,9 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, 
     w.tail = o;   o = align_up(o + (size_t)T * 4, 256);
     w.flags = o;  o = align_up(o + (size_t)T * 4, 256);
     w.nu = o;     o = align_up(o + 64, 256);
-    w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
     w.hist = o;   o = align_up(o + hist_words * 4, 256);
+    w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
+    w.ccount = o; o = align_up(o + (size_t)sample_chunks(L) * 4, 256);
     w.zero_end = o;
     w.meta = o;     o = align_up(o + (size_t)T * sizeof(int32_t) * 4, 256);
     w.sample_u = o; o = align_up(o + (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);

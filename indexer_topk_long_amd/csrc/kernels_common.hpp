@@ -61,6 +61,11 @@ __device__ __forceinline__ void lds_direct16_async(const void* g, void* lds) {
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(off) : "memory", "m0");
 }
+__device__ __forceinline__ void lds_direct4_async(const void* g, void* lds) {
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(off) : "memory", "m0");
+}
 
 // Smallest fp32 score whose bin is >= thr (bin_of is monotone), found by
 // bisection over the ordered float encoding: the gate I >= tau is then

@@ -89,21 +89,55 @@ def test_decode_shared_threshold_small_splits(lib):
     say("  shared", st.cand_written, "unshared", st2.cand_written)
 
 
+VARIANTS = [
+    # (T, H, D, dtype, k, opts) -- 2 or 4 waves per query, every tile geometry
+    (1, 64, 64, "bf16", 128, {}),
+    (2, 20, 64, "fp8", 200, {}),
+    (3, 64, 128, "bf16", 64, {}),
+    (1, 20, 128, "f32", 100, {}),                 # one 64-key block per tile: one wave per query
+    (1, 64, 128, "fp8", 256, {"nbins": 1024}),    # four tile stages do not fit: one wave per query
+    (4, 33, 128, "fp8", 300, {"l_splits": 5}),
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS, ids=lambda c: f"T{c[0]}_H{c[1]}_D{c[2]}_{c[3]}_k{c[4]}_{len(c[5])}")
+def test_decode_waves_per_query_variants(lib, case):
+    T, H, D, dt, k, ok = case
+    L = 20011
+    inp = indexer_inputs(T, L, H, D, dt, k, 600, drift=True, tag=65, n_sample=3 * k)
+    d = to_dev(inp)
+    idx, sc = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=d["sample"], q_scale=d["q_scale"],
+                               k_scale=d["k_scale"], opts=lib.Opts(**ok), return_scores=True)
+    check_rows(inp, idx.cpu().numpy(), sc.cpu().numpy(), range(T), f"variant {case}")
+    uidx = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"], k_scale=d["k_scale"])
+    assert np.array_equal(canon(idx.cpu().numpy()), canon(uidx.cpu().numpy()))
+
+
 def test_decode_chain_of_steps(lib):
-    """Four speculative-decode steps of T = 4: each step's sample is the previous step's result."""
+    """Four speculative-decode steps of T = 4: each step's sample is the previous step's result.
+    The same chain again with the results kept in a ring that every step samples whole and
+    writes one slot of (the output overlaps the sample) gives the same sets."""
+    import torch
     T, L, H, D, dt, k, nh = 4, 65536, 64, 128, "fp8", 1024, 4096
     first = _step_inputs(T, L, H, D, dt, k, nh, -4, tag=63)
     keys = _keys(first)
-    inp = first
-    sample = to_dev(first)["sample"]
-    for s in range(-4, 0):
-        if s > -4:
-            inp = _step_inputs(T, L, H, D, dt, k, nh, s, keys=keys, tag=63)
-        d = to_dev(inp)
-        idx = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
-                               k_scale=d["k_scale"])
+    ins = [first] + [_step_inputs(T, L, H, D, dt, k, nh, s, keys=keys, tag=63) for s in (-3, -2, -1)]
+    ds = [to_dev(x) for x in ins]
+    sample = ds[0]["sample"]
+    plain = []
+    for s, (inp, d) in enumerate(zip(ins, ds)):
+        idx = lib.score_select(d["q"], ds[0]["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                               k_scale=ds[0]["k_scale"])
         check_rows(inp, idx.cpu().numpy(), None, range(T), f"chain step {s}")
+        plain.append(canon(idx.cpu().numpy()))
         sample = idx.reshape(-1)
+    ring = torch.full((2, T, k), -1, dtype=torch.int32, device="cuda")
+    for s, d in enumerate(ds):
+        smp = ds[0]["sample"] if s == 0 else ring
+        out = lib.score_select(d["q"], ds[0]["k"], d["w"], d["pos"], k, sample=smp.reshape(-1),
+                               q_scale=d["q_scale"], k_scale=ds[0]["k_scale"], out=ring[s % 2])
+        assert out.data_ptr() == ring[s % 2].data_ptr()
+        assert np.array_equal(canon(out.cpu().numpy()), plain[s]), f"ring step {s}"
 
 
 def test_decode_graph_capture_replays(lib):

@@ -86,6 +86,11 @@ def _variants(inp):
         "low_index_keys": worst,
         "dups_invalid": np.concatenate([base[:50]] * 4 + [np.array([-7, -1, L, L + 100], np.int32)]).astype(np.int32),
         "other_seed": random_sample(3 * k, L, tag=77),
+        # 16,384 entries: the largest sample de-duplicated in one workgroup's hash table
+        "hash_table_full": np.resize(random_sample(min(4000, L), L, tag=78), 16384).astype(np.int32),
+        # past that size the key bitmap de-duplicates (duplicates and invalid entries included)
+        "bitmap_path": np.concatenate([np.resize(random_sample(min(3000, L), L, tag=79), 20000),
+                                       np.array([-3, L, L + 9], np.int32)]).astype(np.int32),
     }
 
 
