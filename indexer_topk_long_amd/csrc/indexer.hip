@@ -184,10 +184,14 @@ __device__ __forceinline__ void load_query(QueryRegs<DT, D, HB>& r, const IdxArg
             load_half_row<DT, D>(r.q[m], a.q + ((size_t)t * a.H + h) * RB, half);
         else
             zero_half_row<DT, D>(r.q[m]);
+        // every lane loads all 16 of its weights unconditionally (indices
+        // clamped into the array), so the loads issue back to back and are
+        // waited for once; padded heads and queries then get weight 0
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int hh = head_of(m, i, half);
-            r.w[m][i] = (tv && hh < a.H) ? sq * a.w[(size_t)t * a.H + hh] : 0.0f;
+            const float wv = a.w[(size_t)min(t, a.T - 1) * a.H + min(hh, a.H - 1)];
+            r.w[m][i] = (tv && hh < a.H) ? sq * wv : 0.0f;
         }
     }
 }
@@ -510,9 +514,10 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         }
     };
 
-    const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
     constexpr int LPW_HI = G::PER_WAVE + (G::SCALE_INST > 0 ? 1 : 0);   // loads per tile, waves < SCALE_INST
     constexpr int LPW_LO = G::PER_WAVE;                                  // loads per tile, other waves
+    // (issuing the first tiles before the query state measured 3 us slower at decode shape)
+    const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
     static_assert(NST == 3 || NST == 4, "two or three tiles load while one is scored");
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j)
@@ -917,7 +922,8 @@ static bool dispatch(int dt, int D, int HB, F&& f) {
 }
 
 // Waves per query of the fused scan: 4 for one or two queries, 2 for three or
-// four, else 1; at most the number of 64-key blocks in a tile.
+// four, else 1; at most the number of 64-key blocks in a tile.  (Eight waves
+// on one query, one 32-key slot each, measured slower at decode shape.)
 static int scan_waves_per_query(int T, int nb) {
     const int r = (T <= 2) ? 4 : (T <= 4) ? 2 : 1;
     return std::min(r, nb);
@@ -993,13 +999,15 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         // the decode-shape variants need room for four tile stages
         const bool few_fits = kScanStagesFew * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + scan_fixed <= kMaxLds;
         const int R = few_fits ? scan_waves_per_query(a.T, NB) : 1;
+        bool launched = false;
         if constexpr (NB % 4 == 0) {
-            if (R == 4) launch_scan(ic<4>{});
+            if (R == 4) { launch_scan(ic<4>{}); launched = true; }
         }
         if constexpr (NB % 2 == 0) {
-            if (R == 2) launch_scan(ic<2>{});
+            if (R == 2) { launch_scan(ic<2>{}); launched = true; }
         }
-        if (R == 1) launch_scan(ic<1>{});
+        if (R == 1) { launch_scan(ic<1>{}); launched = true; }
+        if (!launched) { err = hipErrorInvalidValue; return; }
         const size_t sel_lds = std::max(fin_lds_bytes(a), 256 * 4 + sort_lds(a));
         allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
         select_kernel<DT_, D_, HB_><<<a.T, 256, sel_lds, st>>>(a);

@@ -92,6 +92,7 @@ def test_decode_shared_threshold_small_splits(lib):
 VARIANTS = [
     # (T, H, D, dtype, k, opts) -- 2 or 4 waves per query, every tile geometry
     (1, 64, 64, "bf16", 128, {}),
+    (1, 20, 64, "fp8", 150, {}),
     (2, 20, 64, "fp8", 200, {}),
     (3, 64, 128, "bf16", 64, {}),
     (1, 20, 128, "f32", 100, {}),                 # one 64-key block per tile: one wave per query
