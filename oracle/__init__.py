@@ -6,6 +6,8 @@ leg.  It shares no code with the GPU library and never imports it.
 from .oracle import (  # noqa: F401
     bf16_to_f64,
     decode,
+    dsa_gather,
+    dsa_pack,
     e4m3fn_table,
     indexer_row_scores,
     indexer_scores,

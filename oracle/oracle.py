@@ -17,6 +17,9 @@ correctness"; summary, "Selection": exact top-k).  No sampling, no bins:
 The indexer score is the DSA-style indexer score (the pages call it the
 relevance score of every candidate token, "Problem statement"); the
 retrieval score is the inner product of the pages' vector-retrieval use.
+LiteDSA packing (arXiv abstract) is written out as plain set operations on
+the selected indices: per group of neighbouring queries, the sorted union of
+their selections and a membership bitmask per union entry.
 
 Inputs are the raw storage bits handed to the GPU (fp32 values, bf16 bit
 patterns, OCP e4m3fn bit patterns with fp32 per-token scales) and are decoded
@@ -197,3 +200,45 @@ def next_sample(prev_idx: np.ndarray, L: int, n: int) -> np.ndarray:
     p = np.asarray(prev_idx).ravel()
     counts = np.bincount(p[(p >= 0) & (p < L)], minlength=L)
     return np.lexsort((np.arange(L), -counts))[:n].astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# LiteDSA packing (arXiv abstract: LiteDSA packs the overlapping candidates of
+# neighbouring query tokens into one shared key/value list for joint
+# attention, and per-query masks keep each token's own top-k membership)
+# ---------------------------------------------------------------------------
+
+
+def dsa_pack(idx: np.ndarray, group: int, L: int):
+    """Shared lists and masks of groups of `group` consecutive query rows.
+
+    Reading of the abstract's one sentence: group g holds rows
+    [g*group, (g+1)*group); its shared list is the set union of the valid keys
+    (0 <= s < L) those rows selected, in ascending key order; entry j of the
+    list carries a mask whose bit i is set exactly when row g*group + i
+    selected that key.  The list and masks are padded to group*k entries with
+    -1 and 0.
+
+    Returns (shared [G, group*k] int32, masks [G, group*k] uint32,
+    lens [G] int32).
+    """
+    idx = np.asarray(idx)
+    T, k = idx.shape
+    ng = (T + group - 1) // group
+    cap = group * k
+    shared = np.full((ng, cap), -1, dtype=np.int32)
+    masks = np.zeros((ng, cap), dtype=np.uint32)
+    lens = np.zeros(ng, dtype=np.int32)
+    for g in range(ng):
+        rows = [set(int(s) for s in r if 0 <= s < L) for r in idx[g * group:(g + 1) * group]]
+        union = sorted(set().union(*rows))
+        lens[g] = len(union)
+        for j, s in enumerate(union):
+            shared[g, j] = s
+            masks[g, j] = sum(1 << i for i, r in enumerate(rows) if s in r)
+    return shared, masks, lens
+
+
+def dsa_gather(kv: np.ndarray, shared: np.ndarray, lens: np.ndarray) -> list:
+    """The key/value rows of each group's shared list: kv[shared[g, :lens[g]]]."""
+    return [kv[shared[g, :lens[g]]] for g in range(len(lens))]

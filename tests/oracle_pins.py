@@ -257,7 +257,101 @@ def check_retrieval_self_match(O, seed=10):
     assert np.array_equal(idx, idx2) and np.array_equal(sc, sc2)
 
 
+# --------------------------------------------------------------------------- LiteDSA packing
+
+
+def _topk_like_rows(rng, T, k, L, n_hot):
+    """Rows of k distinct keys drawn mostly from a shared hot set (neighbouring
+    queries overlap), with some -1 and out-of-range entries."""
+    hot = rng.choice(L, size=min(n_hot, L), replace=False)
+    rows = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        n = rng.integers(0, k + 1)
+        pool = np.concatenate([hot, rng.choice(L, size=k, replace=False)])
+        keys = np.unique(pool)[rng.permutation(len(np.unique(pool)))][:n]
+        rows[t, :n] = keys
+    flat = rows.ravel()
+    bad = rng.random(flat.shape) < 0.02
+    flat[bad] = L + rng.integers(0, 5, size=int(bad.sum()))   # not keys
+    return rows
+
+
+def check_dsa_hand_example(O):
+    """Hand-derived union, masks and padding (tests/golden/dsa_pack_hand.json)."""
+    g = _load("dsa_pack_hand.json")
+    sh, m, n = O.dsa_pack(np.array(g["idx"], np.int32), g["group"], g["L"])
+    assert np.array_equal(sh, np.array(g["shared"])), sh
+    assert np.array_equal(m, np.array(g["masks"], np.uint32)), m
+    assert np.array_equal(n, np.array(g["lens"])), n
+
+
+def check_dsa_membership(O, seed=11):
+    """Each query's own selection is exactly the list entries whose mask has its
+    bit; lists are strictly ascending, padded, and between the largest row and
+    the sum of the rows in size."""
+    rng = np.random.default_rng(seed)
+    for T, k, L, G in [(7, 5, 40, 3), (16, 8, 100, 8), (33, 6, 64, 32), (5, 4, 9, 1), (12, 16, 30, 5)]:
+        idx = _topk_like_rows(rng, T, k, L, n_hot=2 * k)
+        sh, m, n = O.dsa_pack(idx, G, L)
+        assert sh.shape == (-(-T // G), G * k) and m.shape == sh.shape
+        for g in range(len(n)):
+            u = sh[g, :n[g]]
+            assert np.all(np.diff(u) > 0) and np.all((u >= 0) & (u < L))
+            assert np.all(sh[g, n[g]:] == -1) and np.all(m[g, n[g]:] == 0)
+            rows = idx[g * G:(g + 1) * G]
+            sets = [set(int(x) for x in r if 0 <= x < L) for r in rows]
+            assert max(len(s) for s in sets) <= n[g] <= sum(len(s) for s in sets)
+            for i, s in enumerate(sets):
+                got = set(int(x) for x in u[(m[g, :n[g]] >> np.uint32(i)) & 1 == 1])
+                assert got == s, (g, i)
+            assert np.all(m[g, :n[g]] >> np.uint32(len(sets)) == 0)   # no bits for missing rows
+            assert np.all(m[g, :n[g]] != 0)
+
+
+def check_dsa_special_cases(O):
+    """Group of one: the sorted row, every mask 1.  Identical rows: one copy,
+    every row's bit.  No keys: empty lists."""
+    row = np.array([[9, 2, 5, -1, 7]], np.int32)
+    sh, m, n = O.dsa_pack(row, 1, 10)
+    assert n[0] == 4 and list(sh[0, :4]) == [2, 5, 7, 9] and np.all(m[0, :4] == 1)
+    same = np.tile(np.array([[4, 0, 3]], np.int32), (5, 1))
+    sh, m, n = O.dsa_pack(same, 5, 6)
+    assert n[0] == 3 and list(sh[0, :3]) == [0, 3, 4] and np.all(m[0, :3] == 0b11111)
+    sh, m, n = O.dsa_pack(np.full((4, 3), -1, np.int32), 2, 6)
+    assert np.all(n == 0) and np.all(sh == -1) and np.all(m == 0)
+
+
+def check_dsa_joint_attention(O, seed=12):
+    """What the packing is for: attention of each query over its group's shared
+    list, restricted by its mask, equals attention over its own selection
+    (softmax of q.k over the selected keys, weighted sum of their values)."""
+    rng = np.random.default_rng(seed)
+    T, k, L, G, D = 10, 6, 50, 4, 8
+    idx = _topk_like_rows(rng, T, k, L, n_hot=8)
+    K, V, Q = rng.standard_normal((L, D)), rng.standard_normal((L, D)), rng.standard_normal((T, D))
+    sh, m, n = O.dsa_pack(idx, G, L)
+    kv = O.dsa_gather(np.concatenate([K, V], axis=1), sh, n)
+    for t in range(T):
+        own = np.array(sorted(set(int(x) for x in idx[t] if 0 <= x < L)), dtype=np.int64)
+        if len(own) == 0:
+            continue
+        s = K[own] @ Q[t]
+        ref = np.exp(s - s.max()) @ V[own] / np.exp(s - s.max()).sum()
+        g, i = divmod(t, G)
+        keep = (m[g, :n[g]] >> np.uint32(i)) & 1 == 1
+        Kg, Vg = kv[g][:, :D], kv[g][:, D:]
+        s2 = np.where(keep, Kg @ Q[t], -np.inf)
+        e = np.exp(s2 - s2[keep].max())
+        got = e @ Vg / e.sum()
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), t
+        assert np.array_equal(kv[g], np.concatenate([K, V], axis=1)[sh[g, :n[g]]])
+
+
 ALL_CHECKS = [
+    check_dsa_hand_example,
+    check_dsa_membership,
+    check_dsa_special_cases,
+    check_dsa_joint_attention,
     check_hand_example, check_relu_identities, check_homogeneity, check_gemm_special_case,
     check_fp8_scale_factorisation, check_e4m3fn_points, check_e4m3fn_vs_torch, check_bf16_vs_torch,
     check_brute_force_ranks, check_exhaustive_subsets, check_selection_special_cases, check_causal,

@@ -114,7 +114,33 @@ def _transposed_keys(m):
     m.oracle_retrieval = oracle_retrieval
 
 
+def _dsa_bits_reversed(m):
+    orig = m.dsa_pack
+
+    def dsa_pack(idx, group, L):
+        sh, mk, n = orig(idx, group, L)
+        rev = np.zeros_like(mk)
+        for i in range(group):
+            rev |= ((mk >> np.uint32(i)) & np.uint32(1)) << np.uint32(group - 1 - i)
+        return sh, rev, n
+    m.dsa_pack = dsa_pack
+
+
+def _dsa_descending(m):
+    orig = m.dsa_pack
+
+    def dsa_pack(idx, group, L):
+        sh, mk, n = orig(idx, group, L)
+        for g in range(len(n)):
+            sh[g, :n[g]] = sh[g, :n[g]][::-1].copy()
+            mk[g, :n[g]] = mk[g, :n[g]][::-1].copy()
+        return sh, mk, n
+    m.dsa_pack = dsa_pack
+
+
 MUTANTS = {
+    "dsa_mask_bits_reversed": (_dsa_bits_reversed, [P.check_dsa_hand_example, P.check_dsa_membership]),
+    "dsa_list_descending": (_dsa_descending, [P.check_dsa_hand_example, P.check_dsa_membership]),
     "no_relu": (_no_relu, [P.check_hand_example, P.check_relu_identities]),
     "ties_to_higher_index": (_ties_high, [P.check_brute_force_ranks, P.check_hand_example,
                                            P.check_selection_special_cases]),
