@@ -351,6 +351,87 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_dsa(args):
+    """Separate line: LiteDSA packing of the 1M-context prefill chunk.
+
+    The chunk's selections come from the library itself: the last two chunks
+    of the 1M prefill run through prefill_chunked (the second samples the
+    first's top-3k), and the last chunk's [8192, 2048] result is packed in
+    groups of neighbouring queries.  Timed: litetopk_dsa_pack over the chunk
+    and litetopk_dsa_gather of the shared key/value rows (synthetic bf16
+    rows of the workload's width).
+    """
+    import torch
+    import indexer_topk_long_amd as ltk
+    from workloads import WORKLOADS, indexer_keys, prefill_queries
+
+    cfg = WORKLOADS[args.workload]
+    base = cfg["keys"]
+    c = WORKLOADS[base]
+    T, L, k, G, rb = c["T"], c["L"], c["topk"], cfg["group"], cfg["kv_row_bytes"]
+    log(f"generating the keys of {base} ...")
+    kr, ksr = indexer_keys(base)
+    kk = torch.from_numpy(kr).cuda().view(torch.float8_e4m3fn)
+    ks = torch.from_numpy(ksr).cuda()
+    del kr, ksr
+    qf = prefill_queries(base, device="cuda")
+    first = L - 2 * T
+    res = ltk.prefill_chunked(lambda c0, c1: qf(first + c0, first + c1), kk, k, 2 * T, chunk=T,
+                              n_sample=c["n_sample"], k_scale=ks, first_pos=first, keep_outputs=True)
+    idx = res["outputs"][-1].contiguous()
+    del kk, ks, res
+    torch.cuda.synchronize()
+    log("  selections of the chunk ready")
+    kv = torch.randint(-2 ** 15, 2 ** 15 - 1, (L, rb // 2), dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ng = T // G
+    out = torch.empty((ng, G * k, rb // 2), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        sh, m, n = ltk.dsa_pack(idx, L, G)
+        ltk.dsa_gather(kv, sh, n, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    pack_ms, gather_ms = [], []
+    for _ in range(args.steps):
+        ev[0].record()
+        sh, m, n = ltk.dsa_pack(idx, L, G)
+        ev[1].record()
+        ltk.dsa_gather(kv, sh, n, out=out)
+        ev[2].record()
+        ev[2].synchronize()
+        pack_ms.append(ev[0].elapsed_time(ev[1]))
+        gather_ms.append(ev[1].elapsed_time(ev[2]))
+    pack_ms, gather_ms = float(np.mean(pack_ms)), float(np.mean(gather_ms))
+    lens = n.cpu().numpy().astype(np.int64)
+    valid = int((idx >= 0).sum().item())
+    shared_rows = int(lens.sum())
+    # the pack reads the selections and writes the lists, masks and lengths
+    pack_bytes = T * k * 4 + 2 * ng * G * k * 4 + ng * 4
+    gather_bytes = shared_rows * rb * 2 + shared_rows * 4
+    log(f"  pack {pack_ms * 1e3:.1f} us, gather {gather_ms * 1e3:.1f} us, rows {valid} -> {shared_rows}")
+    line = {"metric": "LiteDSA: selected query-key entries packed per second (1M-context chunk, k=2048)",
+            "value": valid / (pack_ms * 1e-3), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(pack_ms + gather_ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+            "data": "synthetic (the library's own selections for the prefill-1m-fp8 chunk; random key/value rows)",
+            "config": {"workload": f"{args.workload}: the {T} selections (k={k}) of the last 1M-context chunk in "
+                                   f"groups of {G} neighbouring queries; key/value rows of {rb} bytes",
+                       "T": T, "topk": k, "group": G, "kv_row_bytes": rb},
+            "pack_ms": round(pack_ms, 4), "gather_ms": round(gather_ms, 4),
+            "shared_list": {"mean_len": round(float(lens.mean()), 1), "max_len": int(lens.max()),
+                            "capacity": G * k, "compression": round(valid / shared_rows, 3)},
+            "kv_bytes_per_query": {"own_lists": round(valid * rb / T, 1), "shared": round(shared_rows * rb / T, 1)},
+            "roofline": {"bound": "hbm", "achieved": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "dsa_pack_kernel", "algorithmic_bytes_per_launch": pack_bytes},
+            "gather_roofline": {"bound": "hbm", "achieved": round(gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
+                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                "frac": round(gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                "algorithmic_bytes_per_launch": gather_bytes},
+            "cpu_baseline": None}
+    print(json.dumps(line), flush=True)
+
+
 def _cores() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -400,6 +481,8 @@ def main():
         return bench_retrieval(args)
     if cfg["kind"] == "decode":
         return bench_decode(args)
+    if cfg["kind"] == "dsa":
+        return bench_dsa(args)
     log(f"generating workload {args.workload} ...")
     t0 = time.perf_counter()
     inp = indexer_workload(args.workload, with_prev=True)

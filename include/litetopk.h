@@ -153,6 +153,32 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
 int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64_t L, int32_t n_sample,
                          int32_t* out_sample, void* ws, size_t ws_bytes, void* stream);
 
+/* LiteDSA packing (LiteTopK pages, arXiv abstract: the candidates that
+ * neighbouring query tokens share are packed into one key/value list for
+ * joint attention, and per-query masks keep each token's own top-k
+ * membership).  Groups are the rows [g*group, (g+1)*group) of idx, the last
+ * one possibly shorter; ngroups = ceil(T / group), cap = group * topk.
+ *
+ *  idx     [T, topk] int32 selected keys per query (a litetopk_score_select
+ *          result; entries outside [0, L) are not keys)
+ *  group   1..32 queries per group; group * topk <= 32768; L <= 2^26
+ *  shared  [ngroups, cap] int32 out: per group its distinct keys in
+ *          ascending order, then -1
+ *  masks   [ngroups, cap] uint32 out: bit i of masks[g][j] is set when row
+ *          g*group + i selected shared[g][j]; 0 past the list
+ *  lens    [ngroups] int32 out: length of each group's list
+ * Returns LTK_EUNSUPPORTED past the size limits above. */
+int litetopk_dsa_pack(const int32_t* idx, int32_t T, int32_t topk, int64_t L, int32_t group,
+                      int32_t* shared, uint32_t* masks, int32_t* lens, void* stream);
+
+/* Gathers each group's shared key/value rows contiguously:
+ * out[g][j] = kv[shared[g][j]] for j < lens[g] (rows of row_bytes, a multiple
+ * of 16; kv [L, row_bytes] and out [ngroups, cap, row_bytes] 16-byte
+ * aligned).  Rows past lens[g] are left untouched; an entry outside [0, L)
+ * gives a zero row. */
+int litetopk_dsa_gather(const void* kv, int64_t L, int64_t row_bytes, const int32_t* shared,
+                        const int32_t* lens, int32_t ngroups, int32_t cap, void* out, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* litetopk_strerror(int status);
 

@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     Opts,
     Stats,
     device_check,
+    dsa_gather,
+    dsa_pack,
     exported_symbols,
     library,
     retrieve,
@@ -33,4 +35,5 @@ from .prefill import next_sample, prefill_chunked  # noqa: F401
 __all__ = [
     "score_select", "retrieve", "unfused_score_select", "workspace_bytes", "strerror", "device_check",
     "Opts", "Stats", "LtkError", "next_sample", "prefill_chunked", "library", "exported_symbols",
+    "dsa_pack", "dsa_gather",
 ]

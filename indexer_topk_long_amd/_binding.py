@@ -80,6 +80,10 @@ def library() -> ctypes.CDLL:
         lib.litetopk_strerror.argtypes = [ctypes.c_int]
         lib.litetopk_device_check.restype = ctypes.c_int
         lib.litetopk_device_check.argtypes = []
+        lib.litetopk_dsa_pack.restype = ctypes.c_int
+        lib.litetopk_dsa_pack.argtypes = [_c_p, _c_i32, _c_i32, _c_i64, _c_i32, _c_p, _c_p, _c_p, _c_p]
+        lib.litetopk_dsa_gather.restype = ctypes.c_int
+        lib.litetopk_dsa_gather.argtypes = [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p]
         _LIB = lib
     return _LIB
 
@@ -256,6 +260,47 @@ def retrieve(q, db, topk: int, sample=None, opts: Opts | None = None, return_sco
     if return_stats:
         res.append(_read_stats(st))
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def dsa_pack(idx, L: int, group: int):
+    """LiteDSA packing (litetopk_dsa_pack): for groups of `group` consecutive
+    rows of idx [T, k] (int32 selected keys), the ascending shared list of
+    their distinct keys, the per-entry masks (bit i: row g*group + i selected
+    the key) and the list lengths.  Returns (shared int32 [G, group*k],
+    masks uint32 [G, group*k], lens int32 [G])."""
+    import torch
+    _dev(idx, "idx", torch.int32)
+    if idx.dim() != 2:
+        raise ValueError("idx must be [T, k]")
+    T, k = idx.shape
+    ng = (T + group - 1) // group
+    shared = torch.empty((ng, group * k), dtype=torch.int32, device=idx.device)
+    masks = torch.empty((ng, group * k), dtype=torch.uint32, device=idx.device)
+    lens = torch.empty((ng,), dtype=torch.int32, device=idx.device)
+    rc = library().litetopk_dsa_pack(_ptr(idx), T, k, L, group, _ptr(shared), _ptr(masks), _ptr(lens), _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_dsa_pack")
+    return shared, masks, lens
+
+
+def dsa_gather(kv, shared, lens, out=None):
+    """The key/value rows of each group's shared list, contiguous
+    (litetopk_dsa_gather): out[g, j] = kv[shared[g, j]] for j < lens[g]; kv is
+    [L, ...] with 16-byte-multiple rows.  Returns out [G, cap, *kv.shape[1:]]."""
+    import torch
+    _dev(kv, "kv"), _dev(shared, "shared", torch.int32), _dev(lens, "lens", torch.int32)
+    L = kv.shape[0]
+    row_bytes = kv[0].numel() * kv.element_size() if L else 0
+    ng, cap = shared.shape
+    if out is None:
+        out = torch.empty((ng, cap) + tuple(kv.shape[1:]), dtype=kv.dtype, device=kv.device)
+    else:
+        _dev(out, "out", kv.dtype)
+    rc = library().litetopk_dsa_gather(_ptr(kv), L, row_bytes, _ptr(shared), _ptr(lens), ng, cap, _ptr(out),
+                                       _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_dsa_gather")
+    return out
 
 
 class HipEvents:

@@ -142,6 +142,34 @@ const char* litetopk_strerror(int status) {
 
 int litetopk_device_check(void) { return device_check(); }
 
+int litetopk_dsa_pack(const int32_t* idx, int32_t T, int32_t topk, int64_t L, int32_t group, int32_t* shared,
+                      uint32_t* masks, int32_t* lens, void* stream) {
+    if (T < 0 || topk < 1 || group < 1 || group > 32 || L < 1) return LTK_EINVAL;
+    if (L > kDsaMaxKeys || (int64_t)group * topk > kDsaMaxEntries) return LTK_EUNSUPPORTED;
+    if (T == 0) return LTK_OK;
+    if (!idx || !shared || !masks || !lens) return LTK_EINVAL;
+    int st;
+    if ((st = device_check()) != LTK_OK) return st;
+    if (launch_dsa_pack(idx, T, topk, (int)L, group, shared, masks, lens, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return LTK_EHIP;
+    return LTK_OK;
+}
+
+int litetopk_dsa_gather(const void* kv, int64_t L, int64_t row_bytes, const int32_t* shared, const int32_t* lens,
+                        int32_t ngroups, int32_t cap, void* out, void* stream) {
+    if (L < 1 || L > (int64_t)0x7fffffff || row_bytes < 16 || row_bytes % 16 != 0 || ngroups < 0 || cap < 1)
+        return LTK_EINVAL;
+    if (ngroups == 0) return LTK_OK;
+    if (!kv || !shared || !lens || !out || !aligned16(kv) || !aligned16(out)) return LTK_EINVAL;
+    int st;
+    if ((st = device_check()) != LTK_OK) return st;
+    if (launch_dsa_gather(kv, (int)L, (size_t)row_bytes, shared, lens, ngroups, cap, out,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return LTK_EHIP;
+    return LTK_OK;
+}
+
 size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, int64_t L, int32_t topk,
                                 int32_t n_sample, int32_t dtype, const ltk_opts* opts) {
     if (kind == LTK_KIND_UNFUSED) {

@@ -136,6 +136,12 @@ hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipSt
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st);
 hipError_t launch_finalize(const IdxArgs& a, hipStream_t st);
 hipError_t launch_retrieve(int D, const RetrArgs& a, const IdxArgs& fin, hipStream_t st);
+constexpr int kDsaMaxEntries = 32768;   // G x k selections packed by one workgroup (LDS)
+constexpr int64_t kDsaMaxKeys = (int64_t)1 << 26;   // key << 5 | row fits 31 bits
+hipError_t launch_dsa_pack(const int32_t* idx, int T, int k, int L, int G, int32_t* shared, uint32_t* masks,
+                           int32_t* lens, hipStream_t st);
+hipError_t launch_dsa_gather(const void* kv, int L, size_t row_bytes, const int32_t* shared, const int32_t* lens,
+                             int ngroups, int cap, void* out, hipStream_t st);
 hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
                               uint32_t* counts, hipStream_t st);
 

@@ -26,7 +26,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = ltk.exported_symbols()
-    assert len(names) == 7
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
 
@@ -136,3 +136,21 @@ def test_unfused_and_next_sample_argument_errors(L):
     assert ns(A16, 4, 8, 100, 101, A16, A16, 400, None) == EINVAL      # more samples than keys
     assert ns(A16, 4, 8, 100, 10, A16, A16, 399, None) == EWS
     assert ns(A16, 4, 8, 100, 0, A16, A16, 0, None) == OK
+
+
+def test_dsa_argument_errors(L):
+    pk, ga = L.litetopk_dsa_pack, L.litetopk_dsa_gather
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    pk.argtypes = [P, I32, I32, I64, I32, P, P, P, P]
+    ga.argtypes = [P, I64, I64, P, P, I32, I32, P, P]
+    assert pk(A16, 8, 2048, 1 << 20, 0, A16, A16, A16, None) == EINVAL      # group 0
+    assert pk(A16, 8, 2048, 1 << 20, 33, A16, A16, A16, None) == EINVAL     # more than 32 rows per mask
+    assert pk(A16, 8, 2048, 1 << 20, 17, A16, A16, A16, None) == EUNSUP     # 17 x 2048 > 32768 entries
+    assert pk(A16, 8, 64, (1 << 26) + 1, 4, A16, A16, A16, None) == EUNSUP  # key << 5 | row needs L <= 2^26
+    assert pk(A16, 8, 0, 100, 4, A16, A16, A16, None) == EINVAL
+    assert pk(None, 8, 64, 100, 4, A16, A16, A16, None) == EINVAL
+    assert pk(None, 0, 64, 100, 4, None, None, None, None) == OK            # no rows: nothing to do
+    assert ga(A16, 100, 24, A16, A16, 4, 64, A16, None) == EINVAL           # rows not whole 16-byte vectors
+    assert ga(MIS, 100, 32, A16, A16, 4, 64, A16, None) == EINVAL           # misaligned key/value rows
+    assert ga(A16, 100, 32, A16, A16, 4, 0, A16, None) == EINVAL
+    assert ga(None, 100, 32, None, None, 0, 64, None, None) == OK

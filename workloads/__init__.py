@@ -13,5 +13,6 @@ from .gen import (  # noqa: F401
     random_sample,
     retrieval_workload,
     retrieval_inputs,
+    selection_rows,
     to_storage,
 )

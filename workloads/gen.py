@@ -48,6 +48,10 @@ WORKLOADS = {
     # each step's sample being the previous step's result.
     "decode-1m-fp8": dict(kind="decode", keys="prefill-1m-fp8", T=1),
     "specdecode-1m-fp8": dict(kind="decode", keys="prefill-1m-fp8", T=8),
+    # LiteDSA packing of the 1M-context chunk's selections in groups of 16
+    # neighbouring queries; the key/value rows gathered are 576 bf16 values
+    # (1,152 bytes, the latent key/value row width of DSA-style attention)
+    "dsa-1m-fp8": dict(kind="dsa", keys="prefill-1m-fp8", group=16, kv_row_bytes=1152),
 }
 INDEXER_WORKLOADS = [n for n, c in WORKLOADS.items() if c["kind"] == "indexer"]
 
@@ -203,6 +207,29 @@ def indexer_keys(name: str, seed: int = SEED_BASE):
     out = indexer_inputs(0, c["L"], c["H"], c["D"], c["dtype"], c["topk"], c["n_hot"], drift=c["drift"],
                          w_range=c["w_range"], tag=c["tag"], seed=seed)
     return out["k"], out["k_scale"]
+
+
+_S_SELECT = 9    # stream id of the synthetic selection rows
+
+
+def selection_rows(T: int, k: int, L: int, tag: int = 0, seed: int = SEED_BASE, spread: float = 1.5,
+                   drift: int = 4, invalid: float = 0.0) -> np.ndarray:
+    """Top-k-like selections of T neighbouring queries: row t holds k distinct
+    keys drawn from a window of spread*k candidate keys that moves by `drift`
+    candidates per row, so neighbouring rows overlap heavily.  A fraction
+    `invalid` of the entries is replaced by -1.  int32 [T, k]."""
+    g = _rng(tag, _S_SELECT, seed)
+    w = max(int(spread * k), k)
+    n = min(L, w + drift * T)
+    cands = g.choice(L, size=n, replace=False).astype(np.int32)
+    rows = np.full((T, k), -1, dtype=np.int32)
+    for t in range(T):
+        win = cands[min(t * drift, max(n - w, 0)):][:w]
+        m = min(k, len(win))
+        rows[t, :m] = win[g.permutation(len(win))[:m]]
+    if invalid > 0:
+        rows[g.random(rows.shape) < invalid] = -1
+    return rows
 
 
 _S_PREFILL = 8   # stream id of the whole-prefill queries drawn on the device
