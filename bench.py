@@ -98,47 +98,97 @@ def cpu_baseline(inp, n_rows: int):
                       f"in {dt:.2f} s, fp64 numpy, including the fp64 decode of the keys"}
 
 
+def _retrieval_run(ltk, torch, q, db, k, smp, steps, warmup):
+    """Timed retrieve calls: (ms per step, scan ms from HIP events, stats)."""
+    T, D = q.shape
+    N = db.shape[0]
+    ws = torch.empty(ltk.workspace_bytes(ltk.KIND_RETRIEVE, T, 1, D, N, k, smp.numel(), 1), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        ltk.retrieve(q, db, k, sample=smp, workspace=ws)
+    torch.cuda.synchronize()
+    ev = ltk.HipEvents(steps)
+    opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ltk.retrieve(q, db, k, sample=smp, opts=opts[i], workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(steps)]))
+    ev.close()
+    _, st = ltk.retrieve(q, db, k, sample=smp, workspace=ws, return_stats=True)
+    return ms, scan_ms, st
+
+
 def bench_retrieval(args):
-    """Separate line: the 8M x 768 bf16 retrieval workload (k = 1,024, random 3,072-row sample)."""
+    """Separate line: the 8M x 768 bf16 retrieval workload (k = 1,024, random 3,072-row sample).
+
+    With --retrieval-sweep K1,K2,...: one line over those k, each with a
+    sample of 3k seeded-random rows, or with --sweep-sample earlier, the 3k
+    rows an earlier batch's queries selected most often (that batch runs first
+    on a random 3k sample; litetopk_next_sample ranks the rows)."""
     import torch
     import indexer_topk_long_amd as ltk
-    from workloads import retrieval_workload
+    from workloads import WORKLOADS, random_retrieval_sample_of, retrieval_queries, retrieval_workload
 
     log("generating retrieval-8m-d768-bf16 on the GPU ...")
     r = retrieval_workload(args.workload, device="cuda")
     T, N, D, k = r["T"], r["N"], r["D"], r["topk"]
     q = torch.from_numpy(np.ascontiguousarray(r["q"]).view(np.int16)).cuda().view(torch.bfloat16)
+
+    def roofline(scan_ms, traffic):
+        ach = 2.0 * D * T * N / (scan_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic, "kernel": "retr_scan_kernel",
+                "kernel_ms": round(scan_ms, 4), "db_read_GBps_at_kernel_time": round(N * D * 2 / (scan_ms * 1e-3) / 1e9, 1)}
+
+    if args.retrieval_sweep:
+        c = WORKLOADS[args.workload]
+        qp_raw, _ = retrieval_queries(T, D, c["n_centres"], c["sigma"], tag=c["tag"], batch=-1)
+        qp = torch.from_numpy(np.ascontiguousarray(qp_raw).view(np.int16)).cuda().view(torch.bfloat16)
+        rows = []
+        for kk in [int(x) for x in args.retrieval_sweep.split(",")]:
+            smp = torch.from_numpy(random_retrieval_sample_of(args.workload, 3 * kk)).cuda()
+            if args.sweep_sample == "earlier":
+                prev = ltk.retrieve(qp, r["db"], kk, sample=smp)
+                smp = ltk.next_sample(prev, N, 3 * kk)
+                del prev
+            ms, scan_ms, st = _retrieval_run(ltk, torch, q, r["db"], kk, smp, args.steps, args.warmup)
+            out = ltk.retrieve(q, r["db"], kk, sample=smp)
+            hit = float(torch.isin(out, smp).float().mean().item())
+            log(f"  k={kk}: {ms:.3f} ms/step, scan {scan_ms:.3f} ms, {st.cand_written / T:.0f} candidates/query")
+            rows.append({"topk": kk, "ms_per_step": round(ms, 4), "value": T * N / (ms * 1e-3),
+                         "roofline": roofline(scan_ms, None),
+                         "candidates_per_query": round(st.cand_written / T, 1),
+                         "max_candidates": st.max_cand_per_query, "overflow_rows": st.overflow_rows,
+                         "sample_hit_rate": round(hit, 4)})
+            del out, smp
+        best = rows[-1]
+        line = {"metric": "scored query-row pairs/s, retrieval k-sweep", "value": best["value"], "unit": "pairs/s",
+                "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": best["ms_per_step"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded Gaussian-mixture database)",
+                "config": {"workload": f"{args.workload}: T={T} queries, N={N} rows, D={D}, bf16, k in "
+                                       f"{args.retrieval_sweep} (value and ms_per_step: the last k); sample = "
+                                       + ("the 3k rows an earlier batch of queries selected most often"
+                                          if args.sweep_sample == "earlier" else "3k seeded-random rows"),
+                           "pairs": T * N},
+                "roofline": best["roofline"], "sweep": rows, "cpu_baseline": None}
+        print(json.dumps(line), flush=True)
+        return
+
     smp = torch.from_numpy(r["sample"]).cuda()
-    ws = torch.empty(ltk.workspace_bytes(ltk.KIND_RETRIEVE, T, 1, D, N, k, len(r["sample"]), 1), dtype=torch.uint8,
-                     device="cuda")
-    for _ in range(args.warmup):
-        ltk.retrieve(q, r["db"], k, sample=smp, workspace=ws)
-    torch.cuda.synchronize()
-    ev = ltk.HipEvents(args.steps)
-    opts = [ltk.Opts(scan_event_start=a, scan_event_stop=b) for a, b in ev.pairs]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ltk.retrieve(q, r["db"], k, sample=smp, opts=opts[i], workspace=ws)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    scan_ms = float(np.mean([ev.elapsed_ms(i) for i in range(args.steps)]))
-    ev.close()
-    _, st = ltk.retrieve(q, r["db"], k, sample=smp, workspace=ws, return_stats=True)
+    ms, scan_ms, st = _retrieval_run(ltk, torch, q, r["db"], k, smp, args.steps, args.warmup)
     pairs = T * N
-    flops = 2.0 * D * pairs
-    ach = flops / (scan_ms * 1e-3) / 1e12
+    traffic = (RETR_TRAFFIC["bytes"] if scan_source_digest(RETR_SOURCES) == RETR_TRAFFIC["digest"]
+               and args.workload == RETR_TRAFFIC["workload"] else None)
     line = {"metric": "scored query-row pairs/s, retrieval k=1024", "value": pairs / (ms * 1e-3), "unit": "pairs/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic (seeded Gaussian-mixture database, random sample)",
             "config": {"workload": f"{args.workload}: T={T} queries, N={N} rows, D={D}, bf16, k={k}, "
                                    f"sample={len(r['sample'])} random rows", "pairs": pairs},
-            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                         "traffic": (RETR_TRAFFIC["bytes"] if scan_source_digest(RETR_SOURCES) == RETR_TRAFFIC["digest"]
-                                     and args.workload == RETR_TRAFFIC["workload"] else None),
-                         "kernel": "retr_scan_kernel", "kernel_ms": round(scan_ms, 4),
-                         "db_read_GBps_at_kernel_time": round(N * D * 2 / (scan_ms * 1e-3) / 1e9, 1)},
+            "roofline": roofline(scan_ms, traffic),
             "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
             "overflow_rows": st.overflow_rows, "cpu_baseline": None}
     print(json.dumps(line), flush=True)
@@ -450,6 +500,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=72)
     ap.add_argument("--prefill-chunks", type=int, default=-1,
                     help="time a chunked prefill over the 1M-context keys: the first N chunks (0 = all 128)")
+    ap.add_argument("--retrieval-sweep", default="", metavar="K1,K2,...",
+                    help="retrieval workload only: one line over these k, sample from an earlier batch's results")
+    ap.add_argument("--sweep-sample", default="random", choices=["random", "earlier"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")

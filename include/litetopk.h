@@ -69,8 +69,9 @@ typedef struct {
     int32_t refresh_every;  /* threshold refresh after every N candidate batches; default 1; <0 = never */
     int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
     int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
-    int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval 131072;
-                               shared thresholds: L when T x L x 8 B <= 512 MiB, else >= 256 per split) */
+    int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval
+                               max(262144, 64 x topk); shared thresholds: L when T x L x 8 B <= 512 MiB,
+                               else >= 256 per split) */
     void* scan_event_start; /* optional hipEvent_t recorded on `stream` just before the fused scan kernel */
     void* scan_event_stop;  /* optional hipEvent_t recorded just after it (profiling; NULL = none) */
     int32_t shared_threshold; /* indexer: key splits of a query share one threshold histogram in the

@@ -179,7 +179,8 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
     (void)H; (void)D;
     Opts o;
-    if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? kDefaultCcapRetrieve : kDefaultCcap, o) != LTK_OK) return 0;
+    if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? retrieve_default_ccap(topk) : kDefaultCcap, o) != LTK_OK)
+        return 0;
     if (kind == LTK_KIND_RETRIEVE)
         return ws_layout(T, L, n_sample, o.ccap, retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
@@ -315,7 +316,7 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     if (!aligned16(q) || !aligned16(db) || !aligned16(ws)) return LTK_EINVAL;
     Opts o;
     int st;
-    if ((st = resolve_opts(opts, kDefaultCcapRetrieve, o)) != LTK_OK) return st;
+    if ((st = resolve_opts(opts, retrieve_default_ccap(topk), o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
     const int ns = retr_splits(T, N, o.l_splits);
     const WsLayout lay = ws_layout(T, N, n_sample, o.ccap, retr_hist_words(T, o.nbins, ns));

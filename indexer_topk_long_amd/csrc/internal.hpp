@@ -15,7 +15,15 @@ constexpr int kFlush = 64;           // write-back batch (one wave64 of 8-byte e
 constexpr int kDefaultBins = 256;
 constexpr int kMaxBins = 1024;
 constexpr int64_t kDefaultCcap = 16384;
-constexpr int64_t kDefaultCcapRetrieve = 131072;
+constexpr int64_t kDefaultCcapRetrieve = 262144;
+// Retrieval candidates per query by default: every database split keeps a
+// fixed slice of the buffer (1,024 entries at 256 splits), and the total grows
+// with k (a random 3k-row sample lets some 15k rows per query through at
+// k = 1,024, 65k at k = 8,192; 512-entry slices overflowed at k = 2,048).
+inline int64_t retrieve_default_ccap(int32_t topk) {
+    const int64_t c = (int64_t)64 * topk;
+    return c > kDefaultCcapRetrieve ? c : kDefaultCcapRetrieve;
+}
 constexpr int kMaxSortedK = 8192;
 constexpr size_t kMaxLds = 160 * 1024;   // LDS one gfx950 workgroup may allocate
 

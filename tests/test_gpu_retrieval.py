@@ -31,7 +31,8 @@ def _check(r, idx, sc, rows, where):
     return swaps
 
 
-SMALL = [(40, 5000, 64, 100), (33, 7001, 128, 64), (20, 3000, 768, 50), (70, 4500, 256, 300), (9, 2100, 512, 2000)]
+SMALL = [(40, 5000, 64, 100), (33, 7001, 128, 64), (20, 3000, 768, 50), (70, 4500, 256, 300), (9, 2100, 512, 2000),
+         (12, 30000, 256, 4096), (6, 40000, 768, 8192)]   # the k-sweep's upper end
 
 
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: f"T{s[0]}_N{s[1]}_D{s[2]}_k{s[3]}")
@@ -93,3 +94,24 @@ def test_retrieval_full_size(lib):
     rows = [0, 1, 511, 1022, 1023] + list(np.random.default_rng(4).choice(T, 3, replace=False))
     say(f"retrieval-8m-d768-bf16: oracle rows {rows}")
     _check(r, idx_h, sc_h, rows, "retrieval-8m")
+
+
+def test_retrieval_earlier_batch_sample(lib):
+    """k = 2,048 with the sample built from an earlier batch's results (the
+    rows that batch's queries selected most often): exact, and bit-identical to
+    the random-sample run."""
+    import torch
+    from workloads import retrieval_queries
+    T, N, D, k = 24, 50000, 256, 2048
+    r = retrieval_inputs(T, N, D, k, n_centres=60, sigma=0.3, n_sample=3 * k, device="cuda", block=8192)
+    qp_raw, _ = retrieval_queries(T, D, 60, 0.3, tag=4, batch=-1)
+    qp = torch.from_numpy(np.ascontiguousarray(qp_raw).view(np.int16)).cuda().view(torch.bfloat16)
+    prev = lib.retrieve(qp, r["db"], k, sample=torch.from_numpy(r["sample"]).cuda())
+    smp = lib.next_sample(prev, N, 3 * k)
+    q = _q_dev(r)
+    idx, sc = lib.retrieve(q, r["db"], k, sample=smp, return_scores=True)
+    ref, ref_sc = lib.retrieve(q, r["db"], k, sample=torch.from_numpy(r["sample"]).cuda(), return_scores=True)
+    a, a_sc = canon(idx.cpu().numpy(), sc.cpu().numpy())
+    b, b_sc = canon(ref.cpu().numpy(), ref_sc.cpu().numpy())
+    assert np.array_equal(a, b) and np.array_equal(a_sc.view(np.uint32), b_sc.view(np.uint32))
+    _check(r, idx.cpu().numpy(), sc.cpu().numpy(), range(0, T, 5), "earlier-batch sample")

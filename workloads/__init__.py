@@ -10,9 +10,11 @@ from .gen import (  # noqa: F401
     indexer_workload,
     indexer_inputs,
     prefill_queries,
+    random_retrieval_sample_of,
     random_sample,
     retrieval_workload,
     retrieval_inputs,
+    retrieval_queries,
     selection_rows,
     to_storage,
 )

@@ -283,6 +283,24 @@ def prefill_queries(name: str, device: str = "cuda", seed: int = SEED_BASE):
     return chunk
 
 
+def _retrieval_centres(n_centres: int, D: int, tag: int, seed: int) -> np.ndarray:
+    return _rng(tag, _S_HOT, seed).standard_normal((n_centres, D)).astype(np.float32)
+
+
+def retrieval_queries(T: int, D: int, n_centres: int = 1000, sigma: float = 0.3, tag: int = 4,
+                      seed: int = SEED_BASE, batch: int = 0, db_dtype: str = "bf16"):
+    """Queries of the retrieval workload: unit(c_j + sigma * N(0, I_D)) with j
+    uniform over the centres.  Batch 0 is the workload's own batch; batch -1,
+    -2, ... are earlier batches of the same distribution (their own streams).
+    Returns (raw storage bits, centre of each query)."""
+    gq = _rng(tag, _S_QUERIES if batch == 0 else _S_PREV_QUERIES + 16 * (-batch - 1), seed)
+    cq = gq.integers(0, n_centres, size=T)
+    centres = _retrieval_centres(n_centres, D, tag, seed)
+    q = _unit(centres[cq] + sigma * gq.standard_normal((T, D)).astype(np.float32)).astype(np.float32)
+    q_raw, _ = to_storage(q, db_dtype)
+    return q_raw, cq
+
+
 def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, sigma: float = 0.3,
                      n_sample: int = 3072, tag: int = 4, seed: int = SEED_BASE, device: str = "cpu",
                      block: int = 1 << 20, db_dtype: str = "bf16"):
@@ -298,12 +316,8 @@ def retrieval_inputs(T: int, N: int, D: int, topk: int, n_centres: int = 1000, s
     """
     import torch
 
-    gc = _rng(tag, _S_HOT, seed)
-    centres = gc.standard_normal((n_centres, D)).astype(np.float32)
-    gq = _rng(tag, _S_QUERIES, seed)
-    cq = gq.integers(0, n_centres, size=T)
-    q = _unit(centres[cq] + sigma * gq.standard_normal((T, D)).astype(np.float32)).astype(np.float32)
-    q_raw, _ = to_storage(q, db_dtype)
+    centres = _retrieval_centres(n_centres, D, tag, seed)
+    q_raw, cq = retrieval_queries(T, D, n_centres, sigma, tag=tag, seed=seed, db_dtype=db_dtype)
 
     dev = torch.device(device)
     seed_db = int(np.random.SeedSequence([seed, tag, _S_DB]).generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF)
@@ -331,3 +345,9 @@ def retrieval_workload(name: str = "retrieval-8m-d768-bf16", device: str = "cpu"
     assert c["kind"] == "retrieval"
     return retrieval_inputs(T or c["T"], N or c["N"], c["D"], c["topk"], c["n_centres"], c["sigma"],
                             c["n_sample"], tag=c["tag"], seed=seed, device=device)
+
+
+def random_retrieval_sample_of(name: str, n: int, seed: int = SEED_BASE) -> np.ndarray:
+    """n distinct seeded-random rows of the named retrieval workload's database."""
+    c = WORKLOADS[name]
+    return random_sample(n, c["N"], c["tag"], seed, stream=_S_SAMPLE)
