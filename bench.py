@@ -29,17 +29,24 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# HBM-side bytes per launch of each scan kernel at its workload, from rocprofv3
-# FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings (FETCH x2.0, WRITE
-# x1.0; profiles/scan_kernel_prefill-1m-fp8.md, profiles/retr_scan_kernel_
-# retrieval-8m-d768-bf16.md).  Valid only for the kernel sources with the
-# recorded digest; reported as null otherwise.
+# HBM-side bytes per launch of each measured kernel at its workload, from
+# rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain copy's readings (FETCH
+# x2.0, WRITE x1.0; profiles/scan_kernel_prefill-1m-fp8.md,
+# profiles/retr_scan_kernel_retrieval-8m-d768-bf16.md,
+# profiles/decode_step_decode-1m-fp8.md, profiles/dsa_pack_dsa-1m-fp8.md).
+# Valid only for the kernel sources with the recorded digest; null otherwise.
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
-SCAN_TRAFFIC = {"digest": "2ccda14b383fdfde", "workload": "prefill-1m-fp8",
-                "bytes": 2223930 * 1024 * 2.0 + 151690 * 1024 * 1.0}
-RETR_TRAFFIC = {"digest": "cef33f8a64b052eb", "workload": "retrieval-8m-d768-bf16",
-                "bytes": 8856324 * 1024 * 2.0 + 1293637 * 1024 * 1.0}
+DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
+SCAN_TRAFFIC = {"digest": "5566efd8f017d9b0", "workload": "prefill-1m-fp8",
+                "bytes": 2223954 * 1024 * 2.0 + 152274 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "e49413a32dbe74ae", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 10334410 * 1024 * 2.0 + 1296822 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "5566efd8f017d9b0", "workload": "decode-1m-fp8",
+                  "bytes": 67640 * 1024 * 2.0 + 47 * 1024 * 1.0}
+DSA_TRAFFIC = {"digest": "2177c8beb290b6bd", "workload": "dsa-1m-fp8",
+               "pack_bytes": 32798 * 1024 * 2.0 + 159819 * 1024 * 1.0,
+               "gather_bytes": 746979 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
@@ -390,7 +397,9 @@ def bench_decode(args):
                        "graph_same_sets_as_eager": graph_same},
             "roofline": {"bound": "hbm", "achieved": round(scan_bytes / (scan_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(scan_bytes / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": (DECODE_TRAFFIC["bytes"] if scan_source_digest() == DECODE_TRAFFIC["digest"]
+                                     and args.workload == DECODE_TRAFFIC["workload"] else None),
                          "kernel": "scan_kernel (fused score + filter)", "kernel_us": round(scan_ms * 1e3, 2),
                          "algorithmic_bytes_per_launch": scan_bytes},
             "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
@@ -458,6 +467,7 @@ def bench_dsa(args):
     pack_bytes = T * k * 4 + 2 * ng * G * k * 4 + ng * 4
     gather_bytes = shared_rows * rb * 2 + shared_rows * 4
     log(f"  pack {pack_ms * 1e3:.1f} us, gather {gather_ms * 1e3:.1f} us, rows {valid} -> {shared_rows}")
+    dsa_ok = scan_source_digest(DSA_SOURCES) == DSA_TRAFFIC["digest"] and args.workload == DSA_TRAFFIC["workload"]
     line = {"metric": "LiteDSA: selected query-key entries packed per second (1M-context chunk, k=2048)",
             "value": valid / (pack_ms * 1e-3), "unit": "entries/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(pack_ms + gather_ms, 4), "higher_is_better": True,
@@ -472,11 +482,13 @@ def bench_dsa(args):
             "kv_bytes_per_query": {"own_lists": round(valid * rb / T, 1), "shared": round(shared_rows * rb / T, 1)},
             "roofline": {"bound": "hbm", "achieved": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": DSA_TRAFFIC["pack_bytes"] if dsa_ok else None,
                          "kernel": "dsa_pack_kernel", "algorithmic_bytes_per_launch": pack_bytes},
             "gather_roofline": {"bound": "hbm", "achieved": round(gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                 "frac": round(gather_bytes / (gather_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                "traffic": DSA_TRAFFIC["gather_bytes"] if dsa_ok else None,
                                 "algorithmic_bytes_per_launch": gather_bytes},
             "cpu_baseline": None}
     print(json.dumps(line), flush=True)

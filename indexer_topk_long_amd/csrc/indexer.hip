@@ -184,14 +184,26 @@ __device__ __forceinline__ void load_query(QueryRegs<DT, D, HB>& r, const IdxArg
             load_half_row<DT, D>(r.q[m], a.q + ((size_t)t * a.H + h) * RB, half);
         else
             zero_half_row<DT, D>(r.q[m]);
-        // every lane loads all 16 of its weights unconditionally (indices
-        // clamped into the array), so the loads issue back to back and are
-        // waited for once; padded heads and queries then get weight 0
+        // the lane's 16 weights load unconditionally, so they issue back to
+        // back and are waited for once (a load per condition would be waited
+        // for one by one).  When all 16 heads exist they come from one row
+        // address with immediate offsets (few registers); otherwise the head
+        // index is clamped into the row.  Padded heads and queries then get
+        // weight 0.
+        const float* wq = a.w + (size_t)min(t, a.T - 1) * a.H;
+        const int h0 = head_of(m, 0, half);
+        float wv[16];
+        if (h0 + 27 < a.H) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wv[i] = wq[h0 + 8 * (i >> 2) + (i & 3)];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wv[i] = wq[min(h0 + 8 * (i >> 2) + (i & 3), a.H - 1)];
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int hh = head_of(m, i, half);
-            const float wv = a.w[(size_t)min(t, a.T - 1) * a.H + min(hh, a.H - 1)];
-            r.w[m][i] = (tv && hh < a.H) ? sq * wv : 0.0f;
+            r.w[m][i] = (tv && hh < a.H) ? sq * wv[i] : 0.0f;
         }
     }
 }
