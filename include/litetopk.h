@@ -27,7 +27,8 @@
  *    different workspaces.
  *  - Host-side argument errors are reported before anything is enqueued.
  *    Data conditions are NOT errors: duplicate, out-of-range or non-causal
- *    sample entries are ignored; an empty sample is allowed; a candidate
+ *    sample entries are ignored; with no sample (n_sample == 0) the library
+ *    samples min(3 topk, L, 16384) evenly spaced causal keys itself; a candidate
  *    buffer that overflows is recovered exactly on the device; rows with
  *    fewer than k valid keys are padded with -1 (score NaN).
  *  - Inputs must be finite (no NaN/Inf in q, k, w, scales).

@@ -182,9 +182,10 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? retrieve_default_ccap(topk) : kDefaultCcap, o) != LTK_OK)
         return 0;
     if (kind == LTK_KIND_RETRIEVE)
-        return ws_layout(T, L, n_sample, o.ccap, retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
+        return ws_layout(T, L, sample_slots(n_sample, topk, L), o.ccap,
+                         retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
-    return ws_layout(T, L, n_sample, p.ccap, p.shared ? (size_t)T * o.nbins : 0).total;
+    return ws_layout(T, L, sample_slots(n_sample, topk, L), p.ccap, p.shared ? (size_t)T * o.nbins : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -203,7 +204,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     if ((st = resolve_opts(opts, kDefaultCcap, o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
     const IdxPlan plan = indexer_plan(T, L, dtype, o);
-    const WsLayout lay = ws_layout(T, L, n_sample, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0);
+    const int32_t n_slots = sample_slots(n_sample, topk, L);
+    const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0);
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -221,13 +223,13 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.L = (int)L;
     a.topk = topk;
     a.nbins = o.nbins;
-    a.n_sample = n_sample > 0 ? n_sample : 1;
+    a.n_sample = n_slots > 0 ? n_slots : 1;
     const int nqg = (T + kQPG - 1) / kQPG;
     a.n_splits = plan.n_splits;
     a.s_splits = 1;
     // sample splits: about 512 workgroups of >= 8 key blocks, down to one block
     // each while the queries alone fill fewer than 128 workgroups (decode)
-    while (nqg * a.s_splits < 512 && (n_sample / 32) / (a.s_splits * 2) >= (nqg * a.s_splits < 128 ? 1 : 8))
+    while (nqg * a.s_splits < 512 && (n_slots / 32) / (a.s_splits * 2) >= (nqg * a.s_splits < 128 ? 1 : 8))
         a.s_splits *= 2;
     a.refresh_every = o.refresh_every;
     a.sorted = o.sorted;
@@ -319,7 +321,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     if ((st = resolve_opts(opts, retrieve_default_ccap(topk), o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
     const int ns = retr_splits(T, N, o.l_splits);
-    const WsLayout lay = ws_layout(T, N, n_sample, o.ccap, retr_hist_words(T, o.nbins, ns));
+    const int32_t n_slots = sample_slots(n_sample, topk, N);
+    const WsLayout lay = ws_layout(T, N, n_slots, o.ccap, retr_hist_words(T, o.nbins, ns));
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -332,7 +335,7 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     f.L = (int)N;
     f.topk = topk;
     f.nbins = o.nbins;
-    f.n_sample = n_sample > 0 ? n_sample : 1;
+    f.n_sample = n_slots > 0 ? n_slots : 1;
     f.sorted = o.sorted;
     f.ccap = o.ccap;
     f.pos = nullptr;   // no causal mask

@@ -58,7 +58,8 @@ constexpr uint32_t kHashEmpty = 0xffffffffu;
 
 __global__ __launch_bounds__(1024) void sample_prep_kernel(const int32_t* sample, int n, int L, int log2_slots,
                                                            uint32_t* zero, size_t n_zero, ltk_stats* stats,
-                                                           int32_t* out, uint32_t* nu) {
+                                                           int32_t* out, uint32_t* nu, int n_own,
+                                                           const int32_t* pos, int T) {
     const int tid = threadIdx.x;
     if (blockIdx.x > 0) {
         const size_t i0 = (size_t)(blockIdx.x - 1) * 1024 + tid;
@@ -68,6 +69,23 @@ __global__ __launch_bounds__(1024) void sample_prep_kernel(const int32_t* sample
             stats->max_cand_per_query = 0;
             stats->overflow_rows = 0;
         }
+        return;
+    }
+    if (n == 0) {
+        // no sample given: n_own evenly spaced keys below the largest causal
+        // bound of the call's queries (every key without positions), ascending
+        __shared__ int s_e[16];
+        int e = pos ? 0 : L;
+        if (pos)
+            for (int t = tid; t < T; t += 1024) e = max(e, min(pos[t], L - 1) + 1);
+        e = wave_max_i32(e);
+        if (lane_id() == 0) s_e[tid >> 6] = e;
+        __syncthreads();
+        int kmax = 0;
+        for (int w = 0; w < 16; ++w) kmax = max(kmax, s_e[w]);
+        const int nw = min(n_own, kmax);
+        for (int j = tid; j < nw; j += 1024) out[j] = (int32_t)(((int64_t)j * kmax) / nw);
+        if (tid == 0) *nu = (uint32_t)nw;
         return;
     }
     extern __shared__ uint32_t tab[];   // [1 << log2_slots]
@@ -971,7 +989,8 @@ hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_
         allow_lds(sample_prep_kernel, lds);
         sample_prep_kernel<<<1 + std::max(zb, 1), 1024, lds, st>>>(sample, n_sample, a.L, lg,
                                                                      reinterpret_cast<uint32_t*>(ws + lay.zero_begin),
-                                                                     nz, a.stats, a.sample_u, a.nu);
+                                                                     nz, a.stats, a.sample_u, a.nu, a.n_sample,
+                                                                     a.pos, a.T);
         return hipGetLastError();
     }
     const size_t nz = (lay.zero_end - lay.zero_begin) / 4;

@@ -56,6 +56,17 @@ struct WsLayout {
 // tail of the cleared range, then stay untouched).
 constexpr int kHashSampleMax = 16384;
 
+// Sample slots of a call: the caller's sample size, or, with no sample,
+// min(3 k, L, 16384) evenly spaced causal keys drawn by the library (the
+// pages' sample is 3 k keys of the previous chunk's result).
+inline int32_t sample_slots(int32_t n_sample, int32_t topk, int64_t L) {
+    if (n_sample > 0) return n_sample;
+    int64_t n = (int64_t)3 * topk;
+    if (n > L) n = L;
+    if (n > kHashSampleMax) n = kHashSampleMax;
+    return (int32_t)n;
+}
+
 // hist_words: 32-bit counters of the histograms shared across workgroups
 // (retrieval: T x (nbins + super-bins) + T x splits; indexer: T x nbins when
 // its splits share thresholds, else 0).
@@ -138,7 +149,7 @@ struct RetrArgs {
 
 // Host launchers (return hipSuccess or the first launch error).
 hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
-                                 uint8_t* ws, hipStream_t st);
+                                 uint8_t* ws, hipStream_t st);   // n_sample == 0: the library's own (a.n_sample keys)
 hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
 hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st);

@@ -196,3 +196,17 @@ def test_next_sample_vs_oracle(lib):
     prev = g.integers(-1, 500, size=(64, 40)).astype(np.int32)
     got = lib.next_sample(torch.from_numpy(prev).cuda(), 500, 120).cpu().numpy()
     assert np.array_equal(np.sort(got), np.sort(next_sample(prev, 500, 120)))
+
+
+def test_no_sample_draws_its_own(lib):
+    """With no sample the library samples 3k evenly spaced causal keys itself:
+    at a long context the gate is no longer open, so no row overflows, and the
+    result is exact."""
+    T, L, k = 24, 200000, 256
+    inp = indexer_inputs(T, L, 64, 128, "fp8", k, 2000, drift=True, tag=44)
+    d = to_dev(inp)
+    idx, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                               return_stats=True)
+    say("no sample: candidates/query", st.cand_written / T, "overflow rows", st.overflow_rows)
+    assert st.overflow_rows == 0
+    check_rows(inp, idx.cpu().numpy(), None, [0, 11, T - 1], "no sample")
