@@ -398,12 +398,52 @@ struct TileGeom {
     static_assert(SCALE_INST <= kScanWaves, "at most one scale load per wave");
 };
 
-// Issue this wave's share of the direct loads of the tile starting at key0.
-// ASYNC: issued as inline assembly, ordered by the caller's own vmcnt waits
-// (the builtin form makes the compiler drain every load before each barrier).
-template <int DT, int D, bool ASYNC = false>
-__device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* st, int wave, int lane) {
+// Per-lane byte offsets, inside a tile, of the wave's share of the tile's
+// direct loads (fixed for the whole kernel: row r of the tile, swizzled chunk).
+template <int DT, int D>
+struct TileOffsets {
+    uint32_t key[TileGeom<DT, D>::PER_WAVE];
+};
+
+template <int DT, int D>
+__device__ __forceinline__ void tile_offsets(TileOffsets<DT, D>& o, int wave, int lane) {
     using G = TileGeom<DT, D>;
+#pragma unroll
+    for (int j = 0; j < G::PER_WAVE; ++j) {
+        const int p = (wave + j * kScanWaves) * 64 + lane;
+        const int r = p / G::CPR, pc = p % G::CPR;
+        o.key[j] = (uint32_t)(r * G::RB + (pc ^ chunk_swz<G::RB, G::CPR>(r)) * 16);
+    }
+}
+
+// Issue this wave's share of the direct loads of the tile starting at key0.
+// A tile wholly inside the context loads from one wave-uniform base plus the
+// precomputed lane offsets; the last, partial tile clamps its rows (keys past
+// the context re-read the last one).  ASYNC: issued as inline assembly,
+// ordered by the caller's own vmcnt waits (the builtin form makes the
+// compiler drain every load before each barrier).
+template <int DT, int D, bool ASYNC = false>
+__device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT, D>& to, int key0, uint8_t* st,
+                                          int wave, int lane) {
+    using G = TileGeom<DT, D>;
+    if (key0 + G::TK <= a.L) {
+        const uint8_t* tb = a.k + (size_t)key0 * G::RB;
+#pragma unroll
+        for (int j = 0; j < G::PER_WAVE; ++j) {
+            uint8_t* dst = st + (wave + j * kScanWaves) * 1024;
+            if constexpr (ASYNC) lds_direct16_async(tb, to.key[j], dst);
+            else lds_direct16(tb + to.key[j], dst);
+        }
+        if constexpr (DT == DT_FP8) {
+            const float* sb = a.k_scale + key0;
+#pragma unroll
+            for (int j = wave; j < G::TK / 64; j += kScanWaves) {
+                if constexpr (ASYNC) lds_direct4_async(sb, (uint32_t)(j * 256 + lane * 4), st + kTileBytes + j * 256);
+                else lds_direct4(sb + j * 64 + lane, st + kTileBytes + j * 256);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < G::PER_WAVE; ++j) {
         const int inst = wave + j * kScanWaves;
@@ -415,7 +455,6 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, int key0, uint8_t* s
         else lds_direct16(a.k + (size_t)key * G::RB + c * 16, st + inst * 1024);
     }
     if constexpr (DT == DT_FP8) {
-        // one per-key scale per lane (keys past the context re-read the last one)
 #pragma unroll
         for (int j = wave; j < G::TK / 64; j += kScanWaves) {
             const int key = min(key0 + j * 64 + lane, a.L - 1);
@@ -444,7 +483,7 @@ template <int DT, int D, int HB, int R>
 __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     using G = TileGeom<DT, D>;
     constexpr int NST = (R > 1) ? kScanStagesFew : kScanStages;            // tile stages
-    constexpr bool ASYNC = R > 1;
+    constexpr bool ASYNC = true;   // loads as inline assembly from a uniform base (no per-load VALU)
     constexpr int QPG = kScanWaves / R;
     constexpr int NB = G::TK / 64;                                         // 64-key blocks per tile
     static_assert(R >= 1 && NB % R == 0, "a tile's blocks split evenly over a query's waves");
@@ -453,10 +492,12 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     uint8_t* tiles = shm;                                                  // NST stages
     uint32_t* hist = reinterpret_cast<uint32_t*>(shm + NST * G::STAGE_BYTES);  // [waves][nbins]
     uint2* stage = reinterpret_cast<uint2*>(hist + kScanWaves * nbins);    // [waves][kStage]
-    const int wave = threadIdx.x >> 6, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int t0 = qg * QPG;
     const int t = t0 + wave / R;                                           // the wave's query
+    TileOffsets<DT, D> toff;
+    tile_offsets<DT, D>(toff, wave, lane);
     const int sub = wave % R;                                              // its blocks: sub, sub + R, ...
     const uint32_t k = (uint32_t)a.topk;
     uint32_t* hl = hist + wave * nbins;                                    // the wave's own counts
@@ -470,7 +511,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         const int tt = t0 + i;
         if (tt < a.T) e = max(e, min(a.pos[tt], a.L - 1) + 1);
     }
-    const int kend = wave_max_i32(e);
+    const int kend = __builtin_amdgcn_readfirstlane(wave_max_i32(e));   // uniform: every lane holds the max
     const int per = ((kend + a.n_splits - 1) / a.n_splits + G::TK - 1) / G::TK * G::TK;
     const int k_lo = split * per, k_hi = min(kend, k_lo + per);
 
@@ -551,7 +592,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     static_assert(NST == 3 || NST == 4, "two or three tiles load while one is scored");
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j)
-        if (j < ntiles) load_tile<DT, D, ASYNC>(a, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
+        if (j < ntiles) load_tile<DT, D, ASYNC>(a, toff, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
     int sbuf = 0;   // stage holding tile `it`
     for (int it = 0; it < ntiles; ++it) {
         // tile `it` has landed once at most the loads of the later tiles in
@@ -565,7 +606,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         __syncthreads();
         if (it + NST - 1 < ntiles) {   // into the stage every wave finished scoring before the barrier
             const int nb = (sbuf + NST - 1) % NST;
-            load_tile<DT, D, ASYNC>(a, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
+            load_tile<DT, D, ASYNC>(a, toff, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
         }
         const int key0 = k_lo + it * G::TK;
         const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;

@@ -61,6 +61,29 @@ __device__ __forceinline__ void lds_direct16_async(const void* g, void* lds) {
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(off) : "memory", "m0");
 }
+// The same copy from a wave-uniform base (SGPRs) plus a per-lane 32-bit byte
+// offset, so that no per-load address arithmetic is needed.
+// A wave-uniform 64-bit pointer in scalar registers.  The builtin returns a
+// signed int: each half goes through uint32_t before widening, so the low
+// half is zero-extended (a sign-extended low half would corrupt the high one).
+__device__ __forceinline__ uint64_t uniform_ptr(const void* p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+__device__ __forceinline__ void lds_direct16_async(const void* base, uint32_t off, void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(uniform_ptr(base)), "s"(m)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_direct4_async(const void* base, uint32_t off, void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(uniform_ptr(base)), "s"(m)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void lds_direct4_async(const void* g, void* lds) {
     const uint32_t off = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds);

@@ -184,3 +184,29 @@ def test_decode_graph_capture_replays(lib):
                          k_scale=ks, workspace=ws)
         torch.cuda.synchronize()
     check_rows(ins[2], gouts[2].cpu().numpy(), None, range(T), "graph replay, last step")
+
+
+def test_keys_past_two_gib_uniform_tile_addresses(lib):
+    """A 2.1 GB key array, so that some tile base addresses have bit 31 of their
+    low word set and others not: the tile loads that take a wave-uniform base
+    in scalar registers must give the same result as the unfused path (which
+    addresses every lane separately)."""
+    import torch
+    L, H, D, k = (1 << 24) + 77, 64, 128, 512
+    g = torch.Generator(device="cuda")
+    g.manual_seed(81)
+    codes = torch.randint(0, 126, (L, D), generator=g, device="cuda", dtype=torch.uint8)   # finite e4m3 codes
+    codes |= (torch.randint(0, 2, (L, D), generator=g, device="cuda", dtype=torch.uint8) << 7)
+    kk = codes.view(torch.float8_e4m3fn)
+    ks = torch.rand(L, generator=g, device="cuda") + 0.5
+    q = torch.randint(0, 126, (2, H, D), generator=g, device="cuda", dtype=torch.uint8).view(torch.float8_e4m3fn)
+    qs = torch.rand(2, generator=g, device="cuda") + 0.5
+    w = torch.rand(2, H, generator=g, device="cuda")
+    for T in (1, 2):   # four and two waves per query
+        pos = torch.tensor([L - 1, L - 2][:T], dtype=torch.int32, device="cuda")
+        idx = lib.score_select(q[:T].contiguous(), kk, w[:T].contiguous(), pos, k, q_scale=qs[:T].contiguous(),
+                               k_scale=ks)
+        uidx = lib.unfused_score_select(q[:T].contiguous(), kk, w[:T].contiguous(), pos, k,
+                                        q_scale=qs[:T].contiguous(), k_scale=ks)
+        assert np.array_equal(canon(idx.cpu().numpy()), canon(uidx.cpu().numpy())), T
+    say("2.1 GB keys: fused == unfused")
