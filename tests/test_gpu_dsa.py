@@ -67,22 +67,26 @@ def test_dsa_pack_duplicates_and_empty_rows(lib):
 
 
 def test_dsa_pack_union_past_hash_table(lib):
-    """Groups whose distinct keys crowd the LDS hash table (3/4 of its 8,192
-    slots) are packed by sorting every selection: uniformly drawn rows give
+    """Groups with more distinct keys than half the LDS hash table's 16,384
+    slots are packed by sorting every selection: uniformly drawn rows give
     about 32,000 distinct keys per group of 16, beside groups of heavily
-    shared rows, and a group just below and just above the switch."""
+    shared rows, and a group just below and just above the switch.  The last
+    group's keys crowd one key-range bucket (3,000 keys near 0 and one near
+    2^26), which sends its distinct keys to the bitonic sort."""
     rng = np.random.default_rng(75)
     k, G = 2048, 16
-    rows = rng.integers(0, 1 << 26, (5 * G, k), dtype=np.int64).astype(np.int32)
+    rows = rng.integers(0, 1 << 26, (6 * G, k), dtype=np.int64).astype(np.int32)
     rows[G:2 * G] = rng.integers(0, 3000, (G, k))                    # about 3,000 distinct
-    for g, n_distinct in ((2, 6100), (3, 6200)):                      # either side of 6,144
+    rows[5 * G:] = rng.integers(0, 3000, (G, k))
+    rows[5 * G + 7, 100] = (1 << 26) - 1
+    for g, n_distinct in ((2, 8100), (3, 8200)):                      # either side of 8,192
         pool = rng.choice(1 << 24, n_distinct, replace=False)
         blk = rng.choice(pool, (G, k))
         blk.reshape(-1)[:n_distinct] = pool                           # every pool key appears
         rows[g * G:(g + 1) * G] = blk
     sh, m, n = _check_pack(lib, rows, 1 << 26, G)
     say("  union sizes", n.tolist())
-    assert n[2] == 6100 and n[3] == 6200
+    assert n[2] == 8100 and n[3] == 8200 and n[5] == len(np.unique(rows[5 * G:]))
 
 
 def test_dsa_full_size_sampled_groups(lib):
