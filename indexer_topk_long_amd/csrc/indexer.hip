@@ -302,9 +302,11 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
     if (in_regs) {
 #pragma unroll
         for (int i = 0; i < kStatsRegs; ++i) {
+            // the score loads do not wait for the key loads (one round trip)
             const int j = tid + 256 * i;
+            const float sj = (j < nu) ? S[j] : NAN;
             const bool ok = j < nu && a.sample_u[j] <= pos_t;
-            v[i] = ok ? S[j] : NAN;
+            v[i] = ok ? sj : NAN;
             if (ok) {
                 ++c;
                 mn = fminf(mn, v[i]);

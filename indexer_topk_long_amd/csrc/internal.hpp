@@ -47,8 +47,8 @@ inline int sample_chunks(int64_t L) {
 // Workspace of one fused call.  The [zero_begin, zero_end) range is cleared
 // by the first kernel of every call.
 struct WsLayout {
-    size_t tail, flags, nu, hist, bitmap, ccount, zero_begin, zero_end;
-    size_t meta, sample_u, sscore, cand, total;
+    size_t tail, flags, hist, bitmap, ccount, zero_begin, zero_end;
+    size_t nu, meta, sample_u, sscore, cand, total;
 };
 
 // Samples of at most this many entries are de-duplicated in one workgroup's
@@ -73,14 +73,18 @@ inline int32_t sample_slots(int32_t n_sample, int32_t topk, int64_t L) {
 inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0) {
     WsLayout w{};
     size_t o = 0;
+    // cleared by the sample preparation of every call
     w.zero_begin = o;
     w.tail = o;   o = align_up(o + (size_t)T * 4, 256);
     w.flags = o;  o = align_up(o + (size_t)T * 4, 256);
-    w.nu = o;     o = align_up(o + 64, 256);
     w.hist = o;   o = align_up(o + hist_words * 4, 256);
     w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
     w.ccount = o; o = align_up(o + (size_t)sample_chunks(L) * 4, 256);
     w.zero_end = o;
+    // written whole by the kernel that produces it (the de-duplicated sample
+    // count is written by the sample preparation, which clears the range
+    // above in other workgroups of the same launch)
+    w.nu = o;       o = align_up(o + 64, 256);
     w.meta = o;     o = align_up(o + (size_t)T * sizeof(int32_t) * 4, 256);
     w.sample_u = o; o = align_up(o + (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
     w.sscore = o;   o = align_up(o + (size_t)T * (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
