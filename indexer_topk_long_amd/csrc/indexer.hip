@@ -381,35 +381,53 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 // SIMD let one wave's VALU epilogue overlap the other's MFMAs.
 
 constexpr int kScanWaves = 8;
-constexpr int kTileBytes = 32768;
-constexpr int kScanStages = 3;     // tile stages at prefill shape: compute one, two loading
-constexpr int kScanStagesFew = 4;  // at decode shape (R > 1), where the key stream bounds the scan
+constexpr int kTileBytes = 32768;      // key bytes per tile at decode shape (R > 1) and for narrow rows
+constexpr int kTileBytesWide = 65536;  // one wave per query, rows of 128 bytes or more
+constexpr int kScanStagesWide = 2;     // 64 KB tiles: one scored while the next loads
+constexpr int kScanStages = 3;         // 32 KB tiles, one wave per query: one scored, two loading
+constexpr int kScanStagesFew = 4;      // at decode shape (R > 1), where the key stream bounds the scan
 
-template <int DT, int D>
+template <int DT, int D, int TB = kTileBytes>
 struct TileGeom {
     static constexpr int RB = D * DTraits<DT>::ESZ;        // bytes per key row
     static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
-    static constexpr int TK = kTileBytes / RB;             // keys per tile
+    static constexpr int TILE_BYTES = TB;
+    static constexpr int TK = TB / RB;                     // keys per tile
     static constexpr int NINST = TK * CPR / 64;            // wave-wide 1 KB loads per tile
     static constexpr int PER_WAVE = NINST / kScanWaves;
     static constexpr int SCALE_BYTES = (DT == DT_FP8) ? TK * 4 : 0;
-    static constexpr int STAGE_BYTES = kTileBytes + SCALE_BYTES;
+    static constexpr int STAGE_BYTES = TB + SCALE_BYTES;
     static_assert(NINST % kScanWaves == 0, "tile loads split evenly over the waves");
     static_assert(TK % 64 == 0, "per-key scales load in whole 64-lane wave loads");
     static constexpr int SCALE_INST = (DT == DT_FP8) ? TK / 64 : 0;       // wave loads of scales per tile
     static_assert(SCALE_INST <= kScanWaves, "at most one scale load per wave");
 };
 
-// Per-lane byte offsets, inside a tile, of the wave's share of the tile's
-// direct loads (fixed for the whole kernel: row r of the tile, swizzled chunk).
-template <int DT, int D>
-struct TileOffsets {
-    uint32_t key[TileGeom<DT, D>::PER_WAVE];
+// Tile size and stages of a scan with R waves per query.  At one wave per
+// query (prefill shape) the MFMA/VALU work bounds the scan, and each tile
+// ends in a workgroup barrier that drains the wave's software pipeline:
+// 64 KB tiles halve those (measured 1.5 % faster than 32 KB tiles with three
+// stages).  WIDE needs rows of at least 128 bytes (at most 512 keys, whose
+// scales take one wave load each) and the LDS for two such stages, which the
+// launch checks against the bin count.  Decode shapes keep 32 KB tiles and
+// four stages in flight.
+template <int DT, int D, int R, bool WIDE>
+struct ScanShape {
+    static_assert(!WIDE || (R == 1 && D * DTraits<DT>::ESZ >= 128), "wide tiles: one wave per query, rows >= 128 B");
+    static constexpr int TB = WIDE ? kTileBytesWide : kTileBytes;
+    static constexpr int NST = (R > 1) ? kScanStagesFew : (WIDE ? kScanStagesWide : kScanStages);
 };
 
-template <int DT, int D>
-__device__ __forceinline__ void tile_offsets(TileOffsets<DT, D>& o, int wave, int lane) {
-    using G = TileGeom<DT, D>;
+// Per-lane byte offsets, inside a tile, of the wave's share of the tile's
+// direct loads (fixed for the whole kernel: row r of the tile, swizzled chunk).
+template <int DT, int D, int TB>
+struct TileOffsets {
+    uint32_t key[TileGeom<DT, D, TB>::PER_WAVE];
+};
+
+template <int DT, int D, int TB>
+__device__ __forceinline__ void tile_offsets(TileOffsets<DT, D, TB>& o, int wave, int lane) {
+    using G = TileGeom<DT, D, TB>;
 #pragma unroll
     for (int j = 0; j < G::PER_WAVE; ++j) {
         const int p = (wave + j * kScanWaves) * 64 + lane;
@@ -424,10 +442,10 @@ __device__ __forceinline__ void tile_offsets(TileOffsets<DT, D>& o, int wave, in
 // the context re-read the last one).  ASYNC: issued as inline assembly,
 // ordered by the caller's own vmcnt waits (the builtin form makes the
 // compiler drain every load before each barrier).
-template <int DT, int D, bool ASYNC = false>
-__device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT, D>& to, int key0, uint8_t* st,
+template <int DT, int D, int TB, bool ASYNC = false>
+__device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT, D, TB>& to, int key0, uint8_t* st,
                                           int wave, int lane) {
-    using G = TileGeom<DT, D>;
+    using G = TileGeom<DT, D, TB>;
     if (key0 + G::TK <= a.L) {
         const uint8_t* tb = a.k + (size_t)key0 * G::RB;
 #pragma unroll
@@ -440,8 +458,8 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT
             const float* sb = a.k_scale + key0;
 #pragma unroll
             for (int j = wave; j < G::TK / 64; j += kScanWaves) {
-                if constexpr (ASYNC) lds_direct4_async(sb, (uint32_t)(j * 256 + lane * 4), st + kTileBytes + j * 256);
-                else lds_direct4(sb + j * 64 + lane, st + kTileBytes + j * 256);
+                if constexpr (ASYNC) lds_direct4_async(sb, (uint32_t)(j * 256 + lane * 4), st + TB + j * 256);
+                else lds_direct4(sb + j * 64 + lane, st + TB + j * 256);
             }
         }
         return;
@@ -460,8 +478,8 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT
 #pragma unroll
         for (int j = wave; j < G::TK / 64; j += kScanWaves) {
             const int key = min(key0 + j * 64 + lane, a.L - 1);
-            if constexpr (ASYNC) lds_direct4_async(a.k_scale + key, st + kTileBytes + j * 256);
-            else lds_direct4(a.k_scale + key, st + kTileBytes + j * 256);
+            if constexpr (ASYNC) lds_direct4_async(a.k_scale + key, st + TB + j * 256);
+            else lds_direct4(a.k_scale + key, st + TB + j * 256);
         }
     }
 }
@@ -481,10 +499,11 @@ __device__ __forceinline__ void read_frag(HalfRow<DT, D>& f, const uint8_t* st, 
 // waves of a query take every R-th 64-key block of each tile.  R = 1 at
 // prefill shape; a decode step of one to four queries uses R = 4 or 2, so
 // that the waves score real queries instead of empty slots.
-template <int DT, int D, int HB, int R>
+template <int DT, int D, int HB, int R, bool WIDE>
 __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
-    using G = TileGeom<DT, D>;
-    constexpr int NST = (R > 1) ? kScanStagesFew : kScanStages;            // tile stages
+    using SS = ScanShape<DT, D, R, WIDE>;
+    using G = TileGeom<DT, D, SS::TB>;
+    constexpr int NST = SS::NST;                                           // tile stages
     constexpr bool ASYNC = true;   // loads as inline assembly from a uniform base (no per-load VALU)
     constexpr int QPG = kScanWaves / R;
     constexpr int NB = G::TK / 64;                                         // 64-key blocks per tile
@@ -498,8 +517,8 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int t0 = qg * QPG;
     const int t = t0 + wave / R;                                           // the wave's query
-    TileOffsets<DT, D> toff;
-    tile_offsets<DT, D>(toff, wave, lane);
+    TileOffsets<DT, D, SS::TB> toff;
+    tile_offsets<DT, D, SS::TB>(toff, wave, lane);
     const int sub = wave % R;                                              // its blocks: sub, sub + R, ...
     const uint32_t k = (uint32_t)a.topk;
     uint32_t* hl = hist + wave * nbins;                                    // the wave's own counts
@@ -591,10 +610,10 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     constexpr int LPW_LO = G::PER_WAVE;                                  // loads per tile, other waves
     // (issuing the first tiles before the query state measured 3 us slower at decode shape)
     const int ntiles = (k_hi > k_lo) ? (k_hi - k_lo + G::TK - 1) / G::TK : 0;
-    static_assert(NST == 3 || NST == 4, "two or three tiles load while one is scored");
+    static_assert(NST >= 2 && NST <= 4, "one to three tiles load while one is scored");
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j)
-        if (j < ntiles) load_tile<DT, D, ASYNC>(a, toff, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
+        if (j < ntiles) load_tile<DT, D, SS::TB, ASYNC>(a, toff, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
     int sbuf = 0;   // stage holding tile `it`
     for (int it = 0; it < ntiles; ++it) {
         // tile `it` has landed once at most the loads of the later tiles in
@@ -608,12 +627,12 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         __syncthreads();
         if (it + NST - 1 < ntiles) {   // into the stage every wave finished scoring before the barrier
             const int nb = (sbuf + NST - 1) % NST;
-            load_tile<DT, D, ASYNC>(a, toff, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
+            load_tile<DT, D, SS::TB, ASYNC>(a, toff, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
         }
         const int key0 = k_lo + it * G::TK;
         const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
         sbuf = (sbuf + 1) % NST;
-        const float* sks = reinterpret_cast<const float*>(st + kTileBytes);
+        const float* sks = reinterpret_cast<const float*>(st + SS::TB);
         if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
         if constexpr (HalfRow<DT, D>::NV > 4) {
             // wide fragments (bf16/fp32 at D = 128): the two 32-key slots of a
@@ -1060,14 +1079,15 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
         const size_t scan_fixed = (size_t)kScanWaves * a.nbins * 4 + (size_t)kScanWaves * kStage * 8;
         constexpr int NB = TileGeom<DT_, D_>::TK / 64;
-        auto launch_scan = [&](auto Rc) {
+        auto launch_scan = [&](auto Rc, auto Wc) {
             constexpr int R_ = decltype(Rc)::value;
+            constexpr bool W_ = decltype(Wc)::value;
             constexpr int QPG = kScanWaves / R_;
-            const size_t scan_lds = (R_ > 1 ? kScanStagesFew : kScanStages) * (size_t)TileGeom<DT_, D_>::STAGE_BYTES +
-                                    scan_fixed;
-            allow_lds(scan_kernel<DT_, D_, HB_, R_>, scan_lds);
+            using SS = ScanShape<DT_, D_, R_, W_>;
+            const size_t scan_lds = SS::NST * (size_t)TileGeom<DT_, D_, SS::TB>::STAGE_BYTES + scan_fixed;
+            allow_lds(scan_kernel<DT_, D_, HB_, R_, W_>, scan_lds);
             if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-            scan_kernel<DT_, D_, HB_, R_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
+            scan_kernel<DT_, D_, HB_, R_, W_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
             if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
         };
         // the decode-shape variants need room for four tile stages
@@ -1075,12 +1095,17 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         const int R = few_fits ? scan_waves_per_query(a.T, NB) : 1;
         bool launched = false;
         if constexpr (NB % 4 == 0) {
-            if (R == 4) { launch_scan(ic<4>{}); launched = true; }
+            if (R == 4) { launch_scan(ic<4>{}, std::false_type{}); launched = true; }
         }
         if constexpr (NB % 2 == 0) {
-            if (R == 2) { launch_scan(ic<2>{}); launched = true; }
+            if (R == 2) { launch_scan(ic<2>{}, std::false_type{}); launched = true; }
         }
-        if (R == 1) { launch_scan(ic<1>{}); launched = true; }
+        if constexpr (TileGeom<DT_, D_>::RB >= 128) {
+            constexpr size_t wide_stages =
+                kScanStagesWide * (size_t)TileGeom<DT_, D_, kTileBytesWide>::STAGE_BYTES;
+            if (R == 1 && wide_stages + scan_fixed <= kMaxLds) { launch_scan(ic<1>{}, std::true_type{}); launched = true; }
+        }
+        if (R == 1 && !launched) { launch_scan(ic<1>{}, std::false_type{}); launched = true; }
         if (!launched) { err = hipErrorInvalidValue; return; }
         const size_t sel_lds = std::max(fin_lds_bytes(a), 256 * 4 + sort_lds(a));
         allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
