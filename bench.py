@@ -38,15 +38,15 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
 DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
-SCAN_TRAFFIC = {"digest": "5566efd8f017d9b0", "workload": "prefill-1m-fp8",
-                "bytes": 2223954 * 1024 * 2.0 + 152274 * 1024 * 1.0}
-RETR_TRAFFIC = {"digest": "e49413a32dbe74ae", "workload": "retrieval-8m-d768-bf16",
-                "bytes": 10334410 * 1024 * 2.0 + 1296822 * 1024 * 1.0}
-DECODE_TRAFFIC = {"digest": "5566efd8f017d9b0", "workload": "decode-1m-fp8",
-                  "bytes": 67640 * 1024 * 2.0 + 47 * 1024 * 1.0}
-DSA_TRAFFIC = {"digest": "2177c8beb290b6bd", "workload": "dsa-1m-fp8",
-               "pack_bytes": 32798 * 1024 * 2.0 + 159819 * 1024 * 1.0,
-               "gather_bytes": 746979 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
+SCAN_TRAFFIC = {"digest": "ccd08e740dc01cf8", "workload": "prefill-1m-fp8",
+                "bytes": 2223753 * 1024 * 2.0 + 152131 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "ae85b21ac5548331", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 10344475 * 1024 * 2.0 + 1295177 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "ccd08e740dc01cf8", "workload": "decode-1m-fp8",
+                  "bytes": 67651 * 1024 * 2.0 + 46 * 1024 * 1.0}
+DSA_TRAFFIC = {"digest": "992d0cb731e25588", "workload": "dsa-1m-fp8",
+               "pack_bytes": 33068 * 1024 * 2.0 + 134034 * 1024 * 1.0,
+               "gather_bytes": 743244 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
