@@ -60,7 +60,8 @@ typedef enum {
 typedef enum {
     LTK_KIND_SCORE_SELECT = 0,   /* litetopk_score_select */
     LTK_KIND_RETRIEVE = 1,       /* litetopk_retrieve */
-    LTK_KIND_UNFUSED = 2         /* litetopk_unfused_score_select */
+    LTK_KIND_UNFUSED = 2,        /* litetopk_unfused_score_select */
+    LTK_KIND_NEXT_SAMPLE = 3     /* litetopk_next_sample */
 } ltk_kind;
 
 /* Tuning options (HOST struct).  Pass NULL for the defaults; a zero field
@@ -89,8 +90,9 @@ typedef struct {
 
 /* Bytes of workspace a call of `kind` needs.  For LTK_KIND_RETRIEVE, H is
  * ignored and L is the database size N; for LTK_KIND_UNFUSED, topk, n_sample
- * and opts are ignored (it holds the full T x L fp32 score matrix).
- * Returns 0 for invalid sizes. */
+ * and opts are ignored (it holds the full T x L fp32 score matrix); for
+ * LTK_KIND_NEXT_SAMPLE only L counts (4 * L bytes of key counts and a fixed
+ * 69,888 bytes more).  Returns 0 for invalid sizes. */
 size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, int64_t L,
                                 int32_t topk, int32_t n_sample, int32_t dtype, const ltk_opts* opts);
 
@@ -150,8 +152,10 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
  * chunk's top-3k tokens are reused as the next chunk's sample).  Ranks the
  * keys 0..L-1 by how many rows of prev_idx [T, topk] (int32, -1 entries
  * ignored) selected them, ties to the lower index, and writes the first
- * n_sample of them to out_sample [n_sample] (int32).  The workspace holds
- * L 32-bit counters: ws_bytes >= 4 * L. */
+ * n_sample of them to out_sample [n_sample] (int32), in no particular order.
+ * ws_bytes >= litetopk_workspace_bytes(LTK_KIND_NEXT_SAMPLE, 0, 0, 0, L, 1,
+ * 0, 0, NULL): the key counts, a histogram of the count values and a few
+ * words per workgroup.  Returns LTK_EWORKSPACE below that. */
 int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64_t L, int32_t n_sample,
                          int32_t* out_sample, void* ws, size_t ws_bytes, void* stream);
 

@@ -8,7 +8,7 @@ from dataclasses import dataclass
 
 from .build import INCLUDE, lib_path
 
-KIND_SCORE_SELECT, KIND_RETRIEVE, KIND_UNFUSED = 0, 1, 2
+KIND_SCORE_SELECT, KIND_RETRIEVE, KIND_UNFUSED, KIND_NEXT_SAMPLE = 0, 1, 2, 3
 _STATUS = {0: "LTK_OK", -1: "LTK_EINVAL", -2: "LTK_EUNSUPPORTED", -3: "LTK_EWORKSPACE", -4: "LTK_EHIP"}
 
 _c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p

@@ -176,6 +176,11 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
         if (T < 0 || L < 1) return 0;
         return align_up((size_t)T * (size_t)L * 4, 256);
     }
+    if (kind == LTK_KIND_NEXT_SAMPLE) {
+        if (L < 1 || L > (int64_t)0x7fffff00) return 0;
+        return ns_layout(L).words * 4;
+    }
+    if (kind != LTK_KIND_SCORE_SELECT && kind != LTK_KIND_RETRIEVE) return 0;
     if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
     (void)H; (void)D;
     Opts o;
@@ -298,7 +303,7 @@ int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64
     if (n_sample == 0) return LTK_OK;
     if ((T > 0 && !prev_idx) || !out_sample || !ws) return LTK_EINVAL;
     if ((int64_t)n_sample > L) return LTK_EINVAL;
-    if (ws_bytes < (size_t)L * 4) return LTK_EWORKSPACE;
+    if (ws_bytes < ns_layout(L).words * 4) return LTK_EWORKSPACE;
     int st = device_check();
     if (st != LTK_OK) return st;
     if (launch_next_sample(prev_idx, (size_t)T * (size_t)topk, (int)L, n_sample, out_sample,

@@ -984,15 +984,144 @@ __global__ void count_selected_kernel(const int32_t* idx, size_t n, int L, uint3
     }
 }
 
-// counts are < 2^24, so their fp32 values order exactly like the integers
-__global__ void counts_to_f32_kernel(uint32_t* counts, int L) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < L) reinterpret_cast<float*>(counts)[i] = (float)counts[i];
+// The first n keys in (count descending, index ascending) order:
+//  1. a histogram of the counts over kNsBins values (the last bin takes every
+//     count from kNsBins - 1 up);
+//  2. from the top of it, the threshold count c* of the n-th key, the number
+//     `above` of keys with larger counts and the number of ties to take;
+//  3. keys counted above c* go to slots [0, above) in any order, and the
+//     first `need` keys counted exactly c*, in index order, to [above, n)
+//     (each workgroup's share of them found from the ties of the workgroups
+//     before it).
+// Only when c* falls in the last bin, where counts are not told apart, does
+// one workgroup rank the whole count array instead.
+struct NsHeader {
+    uint32_t cstar, above, need, fallback, slot;
+};
+
+__global__ __launch_bounds__(256) void ns_hist_kernel(const uint32_t* counts, int L, int chunk, uint32_t* hist) {
+    __shared__ uint32_t s_zero;
+    if (threadIdx.x == 0) s_zero = 0u;
+    __syncthreads();
+    const int k0 = blockIdx.x * chunk, k1 = min(L, k0 + chunk);
+    uint32_t zeros = 0;
+    for (int key = k0 + threadIdx.x; key < k1; key += 256) {
+        const uint32_t c = counts[key];
+        if (c == 0u) ++zeros;
+        else atomicAdd(&hist[min(c, (uint32_t)(kNsBins - 1))], 1u);
+    }
+    zeros = wave_sum_u32(zeros);
+    if (lane_id() == 0 && zeros) atomicAdd(&s_zero, zeros);
+    __syncthreads();
+    if (threadIdx.x == 0 && s_zero) atomicAdd(&hist[0], s_zero);
 }
 
-__global__ __launch_bounds__(256) void select_counts_kernel(const float* counts, int L, int n, int32_t* out) {
+__global__ __launch_bounds__(1024) void ns_pick_kernel(const uint32_t* hist, int n, NsHeader* hdr) {
+    constexpr int PER = kNsBins / 1024;
+    __shared__ uint32_t s_wsum[16];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    // thread tid holds bins [kNsBins - PER (tid + 1), kNsBins - PER tid): the
+    // scan runs from the top bin down
+    const int hi = kNsBins - PER * tid;
+    uint32_t h[PER], part = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        h[i] = hist[hi - 1 - i];
+        part += h[i];
+    }
+    uint32_t incl = part;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    uint32_t run = incl - part;   // keys in the bins above this thread's
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+    const uint32_t nn = (uint32_t)n;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (run < nn && run + h[i] >= nn) {   // exactly one bin holds the n-th key
+            const uint32_t c = (uint32_t)(hi - 1 - i);
+            hdr->cstar = c;
+            hdr->above = run;
+            hdr->need = nn - run;
+            hdr->fallback = (c == (uint32_t)(kNsBins - 1)) ? 1u : 0u;
+        }
+        run += h[i];
+    }
+}
+
+// Keys counted above c* to their slots; the ties of each workgroup counted.
+__global__ __launch_bounds__(256) void ns_above_kernel(const uint32_t* counts, int L, int chunk, NsHeader* hdr,
+                                                       uint32_t* ties, int32_t* out) {
+    __shared__ uint32_t s_t;
+    if (hdr->fallback) return;
+    const uint32_t cstar = hdr->cstar;
+    if (threadIdx.x == 0) s_t = 0u;
+    __syncthreads();
+    const int k0 = blockIdx.x * chunk, k1 = min(L, k0 + chunk);
+    uint32_t t = 0;
+    for (int b = k0; b < k1; b += 256) {
+        const int key = b + (int)threadIdx.x;
+        const uint32_t c = key < k1 ? counts[key] : 0u;
+        const bool up = key < k1 && c > cstar;
+        t += (key < k1 && c == cstar) ? 1u : 0u;
+        const uint64_t m = __ballot(up);
+        if (m) {
+            uint32_t base = 0u;
+            if (lane_id() == 0) base = atomicAdd(&hdr->slot, (uint32_t)__popcll(m));
+            base = __shfl(base, 0);
+            if (up) out[base + mbcnt(m)] = key;
+        }
+    }
+    t = wave_sum_u32(t);
+    if (lane_id() == 0 && t) atomicAdd(&s_t, t);
+    __syncthreads();
+    if (threadIdx.x == 0) ties[blockIdx.x] = s_t;
+}
+
+// The first `need` ties in index order to slots [above, n).
+__global__ __launch_bounds__(256) void ns_ties_kernel(const uint32_t* counts, int L, int chunk, const NsHeader* hdr,
+                                                      const uint32_t* ties, int32_t* out) {
+    __shared__ uint32_t s_wsum[4], s_base;
+    if (hdr->fallback) return;
+    const uint32_t cstar = hdr->cstar, need = hdr->need, above = hdr->above;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    uint32_t before = 0;   // ties of the workgroups before this one
+    for (int b = tid; b < (int)blockIdx.x; b += 256) before += ties[b];
+    before = wave_sum_u32(before);
+    if (lane == 0) s_wsum[wave] = before;
+    __syncthreads();
+    if (tid == 0) s_base = s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    __syncthreads();
+    uint32_t base = s_base;
+    if (base >= need) return;
+    const int k0 = blockIdx.x * chunk, k1 = min(L, k0 + chunk);
+    for (int b = k0; b < k1 && base < need; b += 256) {
+        const int key = b + tid;
+        const bool tie = key < k1 && counts[key] == cstar;
+        const uint64_t m = __ballot(tie);
+        __syncthreads();   // s_wsum of the previous round read by every thread
+        if (lane == 0) s_wsum[wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t r = base + (uint32_t)mbcnt(m);
+        for (int w = 0; w < wave; ++w) r += s_wsum[w];
+        if (tie && r < need) out[above + r] = key;
+        base += s_wsum[0] + s_wsum[1] + s_wsum[2] + s_wsum[3];
+    }
+}
+
+// Counts past the histogram's range decide: one workgroup ranks them all
+// (counts below 2^24 order exactly as fp32).
+__global__ __launch_bounds__(256) void ns_fallback_kernel(uint32_t* counts, int L, int n, const NsHeader* hdr,
+                                                          int32_t* out) {
     extern __shared__ uint32_t sh[];
-    MemSource src{counts};
+    if (!hdr->fallback) return;
+    for (int i = threadIdx.x; i < L; i += 256) reinterpret_cast<float*>(counts)[i] = (float)counts[i];
+    __syncthreads();
+    MemSource src{reinterpret_cast<const float*>(counts)};
     select_row(src, L, n, out, nullptr, sh);
 }
 
@@ -1142,11 +1271,20 @@ hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipSt
 }
 
 hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
-                              uint32_t* counts, hipStream_t st) {
-    zero_kernel<<<std::max(1, std::min((L + 255) / 256, 2048)), 256, 0, st>>>(counts, (size_t)L, nullptr);
+                              uint32_t* ws, hipStream_t st) {
+    const NsLayout lay = ns_layout(L);
+    uint32_t* counts = ws;
+    uint32_t* hist = ws + lay.hist;
+    NsHeader* hdr = reinterpret_cast<NsHeader*>(ws + lay.hdr);
+    uint32_t* ties = ws + lay.ties;
+    const int chunk = ns_chunk(L), nb = (L + chunk - 1) / chunk;
+    zero_kernel<<<std::max(1, std::min((int)((lay.ties + 255) / 256), 2048)), 256, 0, st>>>(ws, lay.ties, nullptr);
     if (n > 0) count_selected_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(prev_idx, n, L, counts);
-    counts_to_f32_kernel<<<(L + 255) / 256, 256, 0, st>>>(counts, L);
-    select_counts_kernel<<<1, 256, 256 * 4, st>>>(reinterpret_cast<const float*>(counts), L, n_sample, out);
+    ns_hist_kernel<<<nb, 256, 0, st>>>(counts, L, chunk, hist);
+    ns_pick_kernel<<<1, 1024, 0, st>>>(hist, n_sample, hdr);
+    ns_above_kernel<<<nb, 256, 0, st>>>(counts, L, chunk, hdr, ties, out);
+    ns_ties_kernel<<<nb, 256, 0, st>>>(counts, L, chunk, hdr, ties, out);
+    ns_fallback_kernel<<<1, 256, 256 * 4, st>>>(counts, L, n_sample, hdr, out);
     return hipGetLastError();
 }
 

@@ -165,6 +165,28 @@ hipError_t launch_dsa_pack(const int32_t* idx, int T, int k, int L, int G, int32
                            int32_t* lens, hipStream_t st);
 hipError_t launch_dsa_gather(const void* kv, int L, size_t row_bytes, const int32_t* shared, const int32_t* lens,
                              int ngroups, int cap, void* out, hipStream_t st);
+// Workspace of litetopk_next_sample, in 32-bit words: the key counts [L],
+// a histogram of count values [kNsBins], a header, and the count of ties in
+// each workgroup's key range [at most kNsBlocks].
+constexpr int kNsBins = 16384;
+constexpr int kNsBlocks = 1024;
+struct NsLayout {
+    size_t hist, hdr, ties, words;
+};
+inline NsLayout ns_layout(int64_t L) {
+    NsLayout w{};
+    w.hist = (size_t)((L + 63) / 64 * 64);
+    w.hdr = w.hist + kNsBins;
+    w.ties = w.hdr + 64;
+    w.words = w.ties + kNsBlocks;
+    return w;
+}
+// keys per workgroup: a multiple of 256, at least 4,096, at most kNsBlocks workgroups
+inline int ns_chunk(int64_t L) {
+    int64_t c = (L + kNsBlocks - 1) / kNsBlocks;
+    c = (c + 255) / 256 * 256;
+    return (int)(c < 4096 ? 4096 : c);
+}
 hipError_t launch_next_sample(const int32_t* prev_idx, size_t n, int L, int n_sample, int32_t* out,
                               uint32_t* counts, hipStream_t st);
 

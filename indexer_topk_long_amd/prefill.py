@@ -4,12 +4,21 @@ from __future__ import annotations
 
 import ctypes
 
-from ._binding import LtkError, _dev, _ptr, _stream, library
+from ._binding import KIND_NEXT_SAMPLE, LtkError, _dev, _ptr, _stream, library
+
+
+def next_sample_workspace_bytes(L: int) -> int:
+    """Workspace bytes litetopk_next_sample needs for L keys."""
+    n = library().litetopk_workspace_bytes(KIND_NEXT_SAMPLE, 0, 0, 0, L, 1, 0, 0, None)
+    if n == 0:
+        raise ValueError(f"invalid key count {L}")
+    return int(n)
 
 
 def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
     """int32 [n_sample] keys most often selected by the rows of prev_idx [T, k]
-    (ties to the lower index), computed on the device by litetopk_next_sample."""
+    (ties to the lower index; in no particular order), computed on the device
+    by litetopk_next_sample."""
     import torch
     _dev(prev_idx, "prev_idx", torch.int32)
     T, k = prev_idx.shape
@@ -19,7 +28,7 @@ def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     out = torch.empty(n_sample, dtype=torch.int32, device=prev_idx.device)
-    ws = workspace if workspace is not None else torch.empty(max(4 * L, 256), dtype=torch.uint8,
+    ws = workspace if workspace is not None else torch.empty(next_sample_workspace_bytes(L), dtype=torch.uint8,
                                                              device=prev_idx.device)
     rc = fn(_ptr(prev_idx), T, k, L, n_sample, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream())
     if rc != 0:
@@ -28,7 +37,8 @@ def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
 
 
 def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_sample: int | None = None,
-                    k_scale=None, first_pos: int = 0, opts=None, keep_outputs: bool = False):
+                    k_scale=None, first_pos: int = 0, opts=None, keep_outputs: bool = False,
+                    diagnostics: bool = True):
     """Whole-prefill driver: the queries at positions first_pos .. first_pos+n_queries-1
     in chunks of `chunk`, each chunk scored against every key at or before its
     queries, with the previous chunk's most-selected 3k keys as its sample (the
@@ -41,9 +51,11 @@ def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_
 
     Returns {"chunks": [per-chunk dict], "workspace_bytes": int, "last": int32
     [rows, topk] of the last chunk, "outputs": list of every chunk's indices if
-    keep_outputs}.  Per chunk: queries, causal pairs, ms of the select call
-    (device events), candidates per query, overflow rows, and the sample hit
-    rate (fraction of the chunk's selected keys that were in its sample).
+    keep_outputs}.  Per chunk: queries, causal pairs, and with `diagnostics`
+    the ms of the select call (device events), candidates per query, overflow
+    rows, and the sample hit rate (fraction of the chunk's selected keys that
+    were in its sample).  Without `diagnostics` the chunks are enqueued back to
+    back with no host synchronisation between them.
     """
     import torch
     from ._binding import KIND_SCORE_SELECT, _dtype_code, score_select, workspace_bytes
@@ -61,13 +73,25 @@ def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_
     H, D = q0.shape[1], q0.shape[2]
     nbytes = workspace_bytes(KIND_SCORE_SELECT, chunk, H, D, L, topk, n_sample, _dtype_code(q0), opts)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
-    ws_sample = torch.empty(max(4 * L, 256), dtype=torch.uint8, device=k.device)
+    ws_sample = torch.empty(next_sample_workspace_bytes(L), dtype=torch.uint8, device=k.device)
     records, outputs, prev = [], [], None
     for c0 in range(0, n_queries, chunk):
         c1 = min(n_queries, c0 + chunk)
         q, w, qs = get(c0, c1)
         pos = torch.arange(first_pos + c0, first_pos + c1, dtype=torch.int32, device=k.device)
         sample = next_sample(prev, L, n_sample, workspace=ws_sample) if prev is not None else None
+        if not diagnostics:
+            idx = score_select(q, k, w, pos, topk, sample=sample, q_scale=qs, k_scale=k_scale, opts=opts,
+                               workspace=ws)
+            # causal pairs: query at position p sees min(p, L - 1) + 1 keys
+            p0, p1 = first_pos + c0, first_pos + c1
+            below = max(0, min(p1, L) - p0)
+            pairs = below * (p0 + 1) + below * (below - 1) // 2 + (c1 - c0 - below) * L
+            records.append({"chunk": c0 // chunk, "queries": c1 - c0, "pairs": pairs})
+            if keep_outputs:
+                outputs.append(idx)
+            prev = idx
+            continue
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         idx, st = score_select(q, k, w, pos, topk, sample=sample, q_scale=qs, k_scale=k_scale, opts=opts,

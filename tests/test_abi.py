@@ -133,9 +133,13 @@ def test_unfused_and_next_sample_argument_errors(L):
     assert f(A16, None, A16, None, A16, A16, 0, 4, 64, 100, F32, 8, A16, None, A16, 0, None) == OK
     ns = L.litetopk_next_sample
     ns.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
-    assert ns(A16, 4, 8, 100, 101, A16, A16, 400, None) == EINVAL      # more samples than keys
-    assert ns(A16, 4, 8, 100, 10, A16, A16, 399, None) == EWS
+    assert ns(A16, 4, 8, 100, 101, A16, A16, 1 << 20, None) == EINVAL  # more samples than keys
+    need = L.litetopk_workspace_bytes(3, 0, 0, 0, 100, 1, 0, 0, None)    # LTK_KIND_NEXT_SAMPLE
+    assert need == 4 * (128 + 16384 + 64 + 1024)                          # counts, histogram, header, ties
+    assert ns(A16, 4, 8, 100, 10, A16, A16, need - 1, None) == EWS
     assert ns(A16, 4, 8, 100, 0, A16, A16, 0, None) == OK
+    assert L.litetopk_workspace_bytes(3, 0, 0, 0, 0, 1, 0, 0, None) == 0   # no keys
+    assert L.litetopk_workspace_bytes(7, 1, 1, 1, 100, 1, 0, 0, None) == 0  # no such kind
 
 
 def test_dsa_argument_errors(L):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from tests.gpu_util import canon, check_rows, say, to_dev
-from workloads import indexer_inputs, indexer_workload, random_sample
+from workloads import selection_rows, indexer_inputs, indexer_workload, random_sample
 
 pytestmark = pytest.mark.gpu
 
@@ -189,13 +189,38 @@ def test_determinism(lib, tiny):
         assert np.array_equal(canon(a[0]), canon(b[0]))
 
 
-def test_next_sample_vs_oracle(lib):
+def _next_sample_cases():
+    g = np.random.default_rng(3)
+    cases = [("random", g.integers(-1, 500, size=(64, 40)).astype(np.int32), 500, 120)]
+    # the 1M-context chunk shape: 2,048 overlapping top-2,048 rows, 6,144 keys
+    cases.append(("chunk_1m", selection_rows(2048, 2048, 1 << 20, tag=81), 1 << 20, 6144))
+    # every row the same 3,000 keys, spread over several workgroups' ranges:
+    # the threshold cuts a tie of 3,000 keys, taken in index order
+    keys = np.sort(g.choice(40000, 3000, replace=False)).astype(np.int32)
+    cases.append(("one_big_tie", np.tile(keys, (50, 1)), 40000, 1234))
+    # fewer selected keys than samples: keys never selected fill in by index
+    cases.append(("zeros_fill", g.integers(0, 70000, size=(3, 100)).astype(np.int32), 70000, 5000))
+    # counts past the histogram's range (20,000 rows): the ranking fallback
+    hot = np.tile(np.array([7, 3, 900, 12], np.int32), (20000, 1))
+    hot[::3, 1] = 5   # counts 13,333 and 6,667 below and 20,000 above the range end
+    cases.append(("counts_past_range", hot, 1000, 3))
+    # repeated keys within rows, invalid entries, a ragged key range
+    rep = g.integers(-3, 12305, size=(40, 64)).astype(np.int32)
+    rep[:, 32:] = rep[:, :32]
+    cases.append(("repeats_ragged", rep, 12305, 777))
+    cases.append(("no_rows", np.zeros((0, 16), np.int32), 300, 50))
+    return cases
+
+
+@pytest.mark.parametrize("case", _next_sample_cases(), ids=lambda c: c[0])
+def test_next_sample_vs_oracle(lib, case):
     import torch
     from oracle import next_sample
-    g = np.random.default_rng(3)
-    prev = g.integers(-1, 500, size=(64, 40)).astype(np.int32)
-    got = lib.next_sample(torch.from_numpy(prev).cuda(), 500, 120).cpu().numpy()
-    assert np.array_equal(np.sort(got), np.sort(next_sample(prev, 500, 120)))
+    name, prev, L, n = case
+    say("next_sample", name, prev.shape, L, n)
+    got = lib.next_sample(torch.from_numpy(np.ascontiguousarray(prev)).cuda(), L, n).cpu().numpy()
+    assert got.shape == (n,)
+    assert np.array_equal(np.sort(got), np.sort(next_sample(prev, L, n))), name
 
 
 def test_no_sample_draws_its_own(lib):

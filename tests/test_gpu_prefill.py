@@ -40,3 +40,21 @@ def test_prefill_chunked_vs_oracle_and_unfused(lib, case):
     uidx = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
                                     k_scale=d["k_scale"]).cpu().numpy()
     assert np.array_equal(canon(idx), canon(uidx))
+
+
+def test_prefill_without_diagnostics_same_sets(lib):
+    """The driver enqueued back to back (no per-chunk events, statistics or
+    synchronisation) selects the same key sets, chunk by chunk, and counts the
+    same causal pairs."""
+    L, chunk, H, D, dt, k, nh = 2048, 512, 64, 128, "fp8", 100, 200
+    inp = indexer_inputs(L, L, H, D, dt, k, nh, drift=True, tag=52, pos=np.arange(L), n_sample=3 * k)
+    d = to_dev(inp)
+    args = ((d["q"], d["w"], d["q_scale"]), d["k"], k, L)
+    kw = dict(chunk=chunk, n_sample=3 * k, k_scale=d["k_scale"], keep_outputs=True)
+    a = lib.prefill_chunked(*args, **kw)
+    b = lib.prefill_chunked(*args, diagnostics=False, **kw)
+    assert [r["pairs"] for r in a["chunks"]] == [r["pairs"] for r in b["chunks"]]
+    assert [r["queries"] for r in a["chunks"]] == [r["queries"] for r in b["chunks"]]
+    for x, y in zip(a["outputs"], b["outputs"]):
+        assert np.array_equal(canon(x.cpu().numpy()), canon(y.cpu().numpy()))
+
