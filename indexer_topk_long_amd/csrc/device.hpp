@@ -166,16 +166,55 @@ __device__ __forceinline__ int mbcnt(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Cross-lane steps on the DPP network: row shifts inside 16-lane rows, then
+// the row broadcasts of lane 15 and lane 31.  Each step costs a few cycles,
+// where a shuffle (ds_bpermute) waits on the LDS crossbar.  Inclusive scans
+// over the wave's 64 lanes (lane i gets op over lanes 0..i); every lane of
+// the wave must be active.
+template <int CTRL, int ROWM = 0xf, int BANKM = 0xf>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWM, BANKM, false);   // masked or outside lanes: old
+}
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v, uint32_t ident, Op op) {
+    const int id = (int)ident;
+    v = op(v, (uint32_t)dpp_i32<0x111>(id, (int)v));         // row_shr:1
+    v = op(v, (uint32_t)dpp_i32<0x112>(id, (int)v));         // row_shr:2
+    v = op(v, (uint32_t)dpp_i32<0x114>(id, (int)v));         // row_shr:4
+    v = op(v, (uint32_t)dpp_i32<0x118>(id, (int)v));         // row_shr:8
+    v = op(v, (uint32_t)dpp_i32<0x142, 0xa>(id, (int)v));    // row_bcast:15 into rows 1, 3
+    v = op(v, (uint32_t)dpp_i32<0x143, 0xc>(id, (int)v));    // row_bcast:31 into rows 2, 3
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_scan_add_u32(uint32_t v) {
+    return wave_scan_u32(v, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+}
+__device__ __forceinline__ uint32_t lane63_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return lane63_u32(wave_scan_add_u32(v)); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    return lane63_u32(wave_scan_u32(v, 0xffffffffu, [](uint32_t x, uint32_t y) { return x < y ? x : y; }));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    return lane63_u32(wave_scan_u32(v, 0u, [](uint32_t x, uint32_t y) { return x > y ? x : y; }));
+}
 __device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-    return v;
+    return (int)lane63_u32(wave_scan_u32((uint32_t)v, 0x80000000u,
+                                         [](uint32_t x, uint32_t y) { return (uint32_t)max((int)x, (int)y); }));
 }
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
+__device__ __forceinline__ float wave_min_f32(float v) {
+    return __uint_as_float(lane63_u32(wave_scan_u32(__float_as_uint(v), __float_as_uint(INFINITY), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fminf(__uint_as_float(x), __uint_as_float(y)));
+    })));
 }
+__device__ __forceinline__ float wave_max_f32(float v) {
+    return __uint_as_float(lane63_u32(wave_scan_u32(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t x, uint32_t y) {
+        return __float_as_uint(fmaxf(__uint_as_float(x), __uint_as_float(y)));
+    })));
+}
+// lane 0's value in every lane (lane 0 active)
+__device__ __forceinline__ uint32_t lane0_u32(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 
 // Top-down accumulation of a histogram (one wave, all 64 lanes): the largest
 // bin b with sum_{b' >= b} h[b'] >= k, and sum_{b' > b} h[b'].  Returns b = -1
@@ -190,14 +229,9 @@ __device__ __forceinline__ SuffixPick suffix_pick(const uint32_t* h, int nbins, 
     uint32_t local = 0;
     for (int i = 0; i < per; ++i)
         if (lo + i < nbins) local += h[lo + i];
-    // inclusive suffix sum over lanes
-    uint32_t S = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_down(S, off);
-        if (lane + off < 64) S += o;
-    }
-    uint32_t c = S - local;  // entries in bins of higher lanes
+    // entries in the bins of higher lanes: the total less the inclusive prefix
+    const uint32_t pre = wave_scan_add_u32(local), total = lane63_u32(pre);
+    uint32_t c = total - pre;
     int best = -1;
     uint32_t best_above = 0;
     for (int i = per - 1; i >= 0; --i) {
@@ -214,7 +248,7 @@ __device__ __forceinline__ SuffixPick suffix_pick(const uint32_t* h, int nbins, 
     const int bmax = wave_max_i32(best);
     // bins are split across lanes, so exactly one lane owns bmax
     uint32_t ab = wave_sum_u32((bmax >= 0 && best == bmax) ? best_above : 0u);
-    if (bmax < 0) ab = __shfl(S, 0);
+    if (bmax < 0) ab = total;
     return SuffixPick{bmax, ab};
 }
 

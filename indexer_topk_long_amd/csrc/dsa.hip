@@ -79,12 +79,7 @@ __device__ void dsa_pack_by_sort(uint32_t* v, const int32_t* src, int rows, int 
     };
     uint32_t heads = 0;
     for (int p = p0; p < p1; ++p) heads += is_head(p) ? 1u : 0u;
-    uint32_t incl = heads;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    uint32_t incl = wave_scan_add_u32(heads);
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
     uint32_t o = incl - heads, total = 0;
@@ -120,16 +115,6 @@ constexpr int kDsaSlotsPerThread = (1 << kDsaLog2SlotsMax) / kDsaThreads;
 constexpr int kDsaBuckets = 4096;       // key-range buckets of the ranking pass
 constexpr int kDsaBucketMax = 64;       // a fuller bucket sends the group to the bitonic sort
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d));
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d));
-    return v;
-}
 
 // Hash path (sh: 2 * slots + kDsaBuckets + 1 words of LDS).  Returns false,
 // having written nothing, when the group has more distinct keys than half the
@@ -241,8 +226,7 @@ __device__ bool dsa_pack_by_hash(uint32_t* sh, const int32_t* src, int rows, int
         }
         // the wave's new keys are counted together; past the limit the
         // group stops inserting (every wave polls the flag)
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) n_fresh += (uint32_t)__shfl_xor((int)n_fresh, d);
+        n_fresh = wave_sum_u32(n_fresh);
         if (lane == 0 && n_fresh) {
             if (atomicAdd(&s_n, n_fresh) + n_fresh > limit) s_over = 1u;
         }
@@ -280,12 +264,7 @@ __device__ bool dsa_pack_by_hash(uint32_t* sh, const int32_t* src, int rows, int
         part += c[i];
         cmax = max(cmax, c[i]);
     }
-    uint32_t incl = part;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    uint32_t incl = wave_scan_add_u32(part);
     cmax = wave_max_u32(cmax);
     if (lane == 63) s_wsum[wave] = incl;
     if (lane == 0) s_wmax[wave] = cmax;
@@ -338,7 +317,7 @@ __device__ bool dsa_pack_by_hash(uint32_t* sh, const int32_t* src, int rows, int
             const uint64_t m = __ballot(v);
             uint32_t base = 0u;
             if (lane == 0 && m) base = atomicAdd(&s_c, (uint32_t)__popcll(m));
-            base = __shfl(base, 0);
+            base = lane0_u32(base);
             if (v) pv[base + mbcnt(m)] = ((uint64_t)mk[j] << 32) | (uint64_t)mm[j];
         }
         int n2 = 1;

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(1024) void sample_prep_kernel(const int32_t* sample
         const uint64_t m = __ballot(fresh);
         uint32_t base = 0u;
         if (lane == 0 && m) base = atomicAdd(&s_n, (uint32_t)__popcll(m));
-        base = __shfl(base, 0);
+        base = lane0_u32(base);
         if (fresh) out[base + mbcnt(m)] = (int32_t)key;
     }
     __syncthreads();
@@ -156,12 +156,7 @@ __global__ __launch_bounds__(256) void sample_compact_kernel(const uint32_t* bit
     uint32_t cnt = 0;
     for (int j = 0; j < wpt; ++j)
         if (w0 + j < nwords) cnt += __popc(bitmap[w0 + j]);
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    uint32_t incl = wave_scan_add_u32(cnt);
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
     uint32_t o = off + incl - cnt;
@@ -324,11 +319,8 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
     }
     c = wave_sum_u32(c);
     for (int i = tid; i < a.nbins; i += 256) sh[i] = 0u;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, off));
-        mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
+    mn = wave_min_f32(mn);
+    mx = wave_max_f32(mx);
     if (lane == 0) {
         s_nv[wave] = c;
         s_min[wave] = mn;
@@ -554,7 +546,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     auto flush = [&]() {
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)kFlush);
-        base = __shfl(base, 0);
+        base = lane0_u32(base);
         const uint2 en = stg[lane];
         if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
         const int rem = cnt - kFlush;
@@ -695,7 +687,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     if (cnt > 0) {
         uint32_t base = 0;
         if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)cnt);
-        base = __shfl(base, 0);
+        base = lane0_u32(base);
         if (lane < cnt) {
             const uint2 en = stg[lane];
             if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
@@ -1033,12 +1025,7 @@ __global__ __launch_bounds__(1024) void ns_pick_kernel(const uint32_t* hist, int
         h[i] = hist[hi - 1 - i];
         part += h[i];
     }
-    uint32_t incl = part;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    uint32_t incl = wave_scan_add_u32(part);
     if (lane == 63) s_wsum[wave] = incl;
     __syncthreads();
     uint32_t run = incl - part;   // keys in the bins above this thread's
@@ -1076,7 +1063,7 @@ __global__ __launch_bounds__(256) void ns_above_kernel(const uint32_t* counts, i
         if (m) {
             uint32_t base = 0u;
             if (lane_id() == 0) base = atomicAdd(&hdr->slot, (uint32_t)__popcll(m));
-            base = __shfl(base, 0);
+            base = lane0_u32(base);
             if (up) out[base + mbcnt(m)] = key;
         }
     }
