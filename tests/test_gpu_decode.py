@@ -98,6 +98,7 @@ VARIANTS = [
     (1, 20, 128, "f32", 100, {}),                 # one 64-key block per tile: one wave per query
     (1, 64, 128, "fp8", 256, {"nbins": 1024}),    # four tile stages do not fit: one wave per query
     (4, 33, 128, "fp8", 300, {"l_splits": 5}),
+    (1, 20, 64, "fp8", 3200, {}),                 # 9,600 sample slots: statistics by their own kernel
 ]
 
 
