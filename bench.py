@@ -38,15 +38,15 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
 DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
-SCAN_TRAFFIC = {"digest": "ccd08e740dc01cf8", "workload": "prefill-1m-fp8",
-                "bytes": 2223753 * 1024 * 2.0 + 152131 * 1024 * 1.0}
-RETR_TRAFFIC = {"digest": "ae85b21ac5548331", "workload": "retrieval-8m-d768-bf16",
-                "bytes": 10344475 * 1024 * 2.0 + 1295177 * 1024 * 1.0}
-DECODE_TRAFFIC = {"digest": "ccd08e740dc01cf8", "workload": "decode-1m-fp8",
-                  "bytes": 67651 * 1024 * 2.0 + 46 * 1024 * 1.0}
-DSA_TRAFFIC = {"digest": "992d0cb731e25588", "workload": "dsa-1m-fp8",
-               "pack_bytes": 33068 * 1024 * 2.0 + 134034 * 1024 * 1.0,
-               "gather_bytes": 743244 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
+SCAN_TRAFFIC = {"digest": "5f9df6273d23734e", "workload": "prefill-1m-fp8",
+                "bytes": 2223762 * 1024 * 2.0 + 151311 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "f856f9695cf01582", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 10401972 * 1024 * 2.0 + 1295802 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "5f9df6273d23734e", "workload": "decode-1m-fp8",
+                  "bytes": 67649 * 1024 * 2.0 + 46 * 1024 * 1.0}
+DSA_TRAFFIC = {"digest": "295e9303474d2832", "workload": "dsa-1m-fp8",
+               "pack_bytes": 33067 * 1024 * 2.0 + 134234 * 1024 * 1.0,
+               "gather_bytes": 745525 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
