@@ -627,23 +627,38 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         const float* sks = reinterpret_cast<const float*>(st + SS::TB);
         if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
         if constexpr (HalfRow<DT, D>::NV > 4) {
-            // wide fragments (bf16/fp32 at D = 128): the two 32-key slots of a
-            // block one after the other, keeping one slot's registers live
-#pragma unroll 1
-            for (int blk = sub; blk < NB; blk += R) {
-                const int kb = key0 + 64 * blk;
-                if (kb >= wave_end) break;
-                HalfRow<DT, D> kf;
-                v16f acc[HB];
-                read_frag<DT, D>(kf, st, 64 * blk, lane);
-                mfma_1slot<DT, D, HB>(ra.q, kf, acc);
-                const float pa = relu_wsum<HB>(acc, ra.w);
-                read_frag<DT, D>(kf, st, 64 * blk + 32, lane);
-                mfma_1slot<DT, D, HB>(ra.q, kf, acc);
-                const float pb = relu_wsum<HB>(acc, ra.w);
-                float I = combine_halves(pa, pb);
-                if constexpr (DT == DT_FP8) I = I * sks[64 * blk + lane];
-                process(I, kb + lane);
+            // wide fragments (bf16/fp32 at D = 128): the same software pipeline
+            // as below with one fragment buffer (a wide fragment takes twice
+            // the registers): slot s+1's fragment is read just before its MFMAs,
+            // which are issued before the ReLU*w reduction of slot s (2.4 %
+            // faster at bf16 than scoring a block's two slots one after the
+            // other); keys past the query's position fail the gate in process
+            constexpr int NS = G::TK / 32 / R;
+            auto row0 = [&](int j) { return 64 * (sub + R * (j >> 1)) + 32 * (j & 1); };
+            HalfRow<DT, D> kf;
+            v16f accC[HB], accN[HB];
+            read_frag<DT, D>(kf, st, row0(0), lane);
+            mfma_1slot<DT, D, HB>(ra.q, kf, accC);
+            float pprev = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                if (sl + 1 < NS) {
+                    read_frag<DT, D>(kf, st, row0(sl + 1), lane);
+                    mfma_1slot<DT, D, HB>(ra.q, kf, accN);
+                }
+                const float p = relu_wsum<HB>(accC, ra.w);
+                if (sl & 1) {
+                    const int r0 = row0(sl - 1);
+                    float I = combine_halves(pprev, p);
+                    if constexpr (DT == DT_FP8) I = I * sks[r0 + lane];
+                    process(I, key0 + r0 + lane);
+                } else {
+                    pprev = p;
+                }
+                if (sl + 1 < NS) {
+#pragma unroll
+                    for (int mm = 0; mm < HB; ++mm) accC[mm] = accN[mm];
+                }
             }
         } else {
             // 32-key slots, software-pipelined: the MFMAs of slot s+1 are issued
