@@ -265,13 +265,39 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
     load_query<DT, D, HB>(ra, a, ta);
     load_query<DT, D, HB>(rb, a, tb);
     const int t = half ? tb : ta;
+    if constexpr (HalfRow<DT, D>::NV > 4) {
+        // wide fragments: no room for a second one
+        for (int blk = b0; blk < b1; ++blk) {
+            const int j = blk * 32 + (lane & 31);
+            const int key = a.sample_u[min(j, nu - 1)];
+            HalfRow<DT, D> kf;
+            load_key<DT, D>(kf, a.k, key);
+            float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+            if constexpr (DT == DT_FP8) I = I * a.k_scale[key];
+            if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
+        }
+        return;
+    }
+    // the next block's key rows (and the one after's key indices) are in
+    // flight while a block is scored
+    auto key_at = [&](int blk) { return a.sample_u[min(blk * 32 + (lane & 31), nu - 1)]; };
+    int key = key_at(b0);
+    int key2 = (b0 + 1 < b1) ? key_at(b0 + 1) : key;
+    HalfRow<DT, D> kf;
+    load_key<DT, D>(kf, a.k, key);
+    float ks = (DT == DT_FP8) ? a.k_scale[key] : 1.0f;
     for (int blk = b0; blk < b1; ++blk) {
         const int j = blk * 32 + (lane & 31);
-        const int key = a.sample_u[min(j, nu - 1)];
-        HalfRow<DT, D> kf;
-        load_key<DT, D>(kf, a.k, key);
-        float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-        if constexpr (DT == DT_FP8) I = I * a.k_scale[key];
+        const HalfRow<DT, D> cur = kf;
+        const float cks = ks;
+        if (blk + 1 < b1) {
+            key = key2;
+            load_key<DT, D>(kf, a.k, key);
+            if constexpr (DT == DT_FP8) ks = a.k_scale[key];
+            if (blk + 2 < b1) key2 = key_at(blk + 2);
+        }
+        float I = score_2slots<DT, D, HB>(ra, cur, rb, cur);
+        if constexpr (DT == DT_FP8) I = I * cks;
         if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
     }
 }
