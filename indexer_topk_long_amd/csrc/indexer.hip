@@ -652,7 +652,40 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         sbuf = (sbuf + 1) % NST;
         const float* sks = reinterpret_cast<const float*>(st + SS::TB);
         if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
-        if constexpr (HalfRow<DT, D>::NV > 4) {
+        if constexpr (DT == DT_F32) {
+            // fp32: a whole fragment is 16 registers per 16 dimensions and
+            // the query's head blocks as many again per block, so the slots
+            // are scored one after the other and each fragment is read and
+            // consumed 16 dimensions at a time; holding it whole spills
+            constexpr int NS = G::TK / 32 / R, NV = HalfRow<DT, D>::NV, PV = 2;
+            const int h = lane >> 5;
+            float pprev = 0.0f;
+            for (int sl = 0; sl < NS; ++sl) {
+                const int r0 = 64 * (sub + R * (sl >> 1)) + 32 * (sl & 1), r = r0 + (lane & 31);
+                v16f acc[HB];
+#pragma unroll
+                for (int mm = 0; mm < HB; ++mm) acc[mm] = v16f{};
+#pragma unroll
+                for (int pc = 0; pc < NV / PV; ++pc) {
+                    u32x4 kv[PV];
+#pragma unroll
+                    for (int i = 0; i < PV; ++i) {
+                        const int c = h * (G::CPR / 2) + pc * PV + i;
+                        kv[i] = *reinterpret_cast<const u32x4*>(st + r * G::RB + ((c ^ chunk_swz<G::RB, G::CPR>(r)) * 16));
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4 * PV; ++j)
+#pragma unroll
+                        for (int mm = 0; mm < HB; ++mm)
+                            acc[mm] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                                __uint_as_float(ra.q[mm].v[pc * PV + (j >> 2)][j & 3]), __uint_as_float(kv[j >> 2][j & 3]),
+                                acc[mm], 0, 0, 0);
+                }
+                const float p = relu_wsum<HB>(acc, ra.w);
+                if (sl & 1) process(combine_halves(pprev, p), key0 + r0 - 32 + lane);
+                else pprev = p;
+            }
+        } else if constexpr (HalfRow<DT, D>::NV > 4) {
             // wide fragments (bf16/fp32 at D = 128): the same software pipeline
             // as below with one fragment buffer (a wide fragment takes twice
             // the registers): slot s+1's fragment is read just before its MFMAs,
@@ -1261,7 +1294,8 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         if constexpr (NB % 2 == 0) {
             if (R == 2) { launch_scan(ic<2>{}, std::false_type{}); launched = true; }
         }
-        if constexpr (TileGeom<DT_, D_>::RB >= 128) {
+        // (fp32 at D = 128 keeps 32 KB tiles: its wide variant spills registers)
+        if constexpr (TileGeom<DT_, D_>::RB >= 128 && !(DT_ == DT_F32 && D_ >= 128)) {
             constexpr size_t wide_stages =
                 kScanStagesWide * (size_t)TileGeom<DT_, D_, kTileBytesWide>::STAGE_BYTES;
             if (R == 1 && wide_stages + scan_fixed <= kMaxLds) { launch_scan(ic<1>{}, std::true_type{}); launched = true; }

@@ -57,6 +57,8 @@ SMALL = [
     (19, 2500, 20, 64, "bf16", 64, 100),
     (16, 1100, 33, 64, "fp8", 300, 50),
     (9, 777, 8, 128, "f32", 50, 40),
+    (37, 3001, 64, 128, "f32", 100, 200),   # two head blocks: fragments read in pieces, 32 KB tiles
+    (19, 2500, 40, 64, "f32", 64, 100),     # two head blocks, 64 KB tiles
 ]
 
 
