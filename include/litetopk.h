@@ -102,7 +102,9 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
  *  q        [T, H, D] queries (dtype); k [L, D] keys (dtype)
  *  q_scale  [T] fp32 per-query scales (fp8 only; NULL otherwise)
  *  k_scale  [L] fp32 per-key scales (fp8 only; NULL otherwise)
- *  w        [T, H] fp32 head weights (>= 0)
+ *  w        [T, H] fp32 head weights (either sign)
+ *           (with T == 0 the per-query arrays q, q_scale, w, pos and the
+ *           outputs may be NULL: the call checks its sizes and returns 0)
  *  pos      [T] int32 query positions; keys 0..pos[t] (and < L) are valid
  *  T >= 0, 1 <= H <= 64, D in {64, 128}, 1 <= L < 2^31, 1 <= topk <= 65536
  *           (a decode or speculative-decode step is the same call with T = 1..8

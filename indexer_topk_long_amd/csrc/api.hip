@@ -203,7 +203,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     if (T > 0 && (!q || !k || !w || !pos || !out_idx || !ws)) return LTK_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return LTK_EINVAL;
     const bool fp8 = dtype == LTK_FP8_E4M3FN;
-    if (fp8 && (!q_scale || !k_scale)) return LTK_EINVAL;
+    if (fp8 && ((T > 0 && !q_scale) || !k_scale)) return LTK_EINVAL;   // no queries: no query scales
     if (!fp8 && (q_scale || k_scale)) return LTK_EINVAL;
     Opts o;
     if ((st = resolve_opts(opts, kDefaultCcap, o)) != LTK_OK) return st;
@@ -270,7 +270,7 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
     if (T > 0 && (!q || !k || !w || !pos || !out_idx || !ws)) return LTK_EINVAL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(ws)) return LTK_EINVAL;
     const bool fp8 = dtype == LTK_FP8_E4M3FN;
-    if (fp8 && (!q_scale || !k_scale)) return LTK_EINVAL;
+    if (fp8 && ((T > 0 && !q_scale) || !k_scale)) return LTK_EINVAL;   // no queries: no query scales
     if (!fp8 && (q_scale || k_scale)) return LTK_EINVAL;
     if (ws_bytes < (size_t)T * (size_t)L * 4) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;

@@ -104,6 +104,9 @@ def _ss(L, **kw):
     (dict(opts=ltk.Opts(nbins=1025)), EINVAL), (dict(opts=ltk.Opts(l_splits=-2)), EINVAL),
     (dict(opts=ltk.Opts(sorted_output=True), topk=9000), EINVAL), (dict(opts=ltk.Opts(cand_capacity=-5)), EINVAL),
     (dict(T=0), OK),
+    # no queries: the per-query arrays (query scales included) may be NULL; key scales may not
+    (dict(T=0, q=None, w=None, pos=None, out=None, dt=FP8, ks=A16), OK),
+    (dict(T=0, dt=FP8, qs=A16), EINVAL),
 ])
 def test_score_select_argument_errors(L, kw, code):
     assert _ss(L, **kw) == code
@@ -131,6 +134,7 @@ def test_unfused_and_next_sample_argument_errors(L):
     assert f(A16, None, A16, None, A16, A16, 4, 4, 64, 100, F32, 8, A16, None, A16, 10, None) == EWS
     assert f(A16, None, A16, None, A16, A16, 4, 4, 64, 100, FP8, 8, A16, None, A16, 1 << 20, None) == EINVAL
     assert f(A16, None, A16, None, A16, A16, 0, 4, 64, 100, F32, 8, A16, None, A16, 0, None) == OK
+    assert f(None, None, A16, A16, None, None, 0, 4, 64, 100, FP8, 8, None, None, A16, 0, None) == OK
     ns = L.litetopk_next_sample
     ns.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, P, P, ctypes.c_size_t, P]
     assert ns(A16, 4, 8, 100, 101, A16, A16, 1 << 20, None) == EINVAL  # more samples than keys

@@ -100,8 +100,8 @@ def _variants(inp):
 def test_sample_bins_refresh_capacity_independence(lib, dt):
     """The result does not depend on the sample, the bin count, the refresh
     period, the key split or the buffer capacity (forced overflow included):
-    the GPU output is bit-identical across all of them.  For fp8 at D = 128
-    this also covers the scan's filter, whose threshold differs per case."""
+    the GPU output is bit-identical across all of them, although the scan's
+    gate threshold differs per case."""
     inp = indexer_inputs(24, 5000, 64, 128, dt, 200, 300, drift=True, tag=31, n_sample=600)
     d = to_dev(inp)
     import indexer_topk_long_amd as ltk
@@ -130,8 +130,8 @@ def test_sample_bins_refresh_capacity_independence(lib, dt):
 
 @pytest.mark.parametrize("w_range", [(-1.0, 1.0), (-1.0, 0.0)], ids=["mixed_sign", "non_positive"])
 def test_fp8_signed_head_weights(lib, w_range):
-    """Head weights of either sign (the scan's filter bounds its bf16 estimate
-    by a second sum over |w|): fused = oracle = unfused, bit-identical scores."""
+    """Head weights of either sign, so that scores can be negative: fused =
+    oracle = unfused, bit-identical scores."""
     say("fp8 signed weights", w_range)
     inp = indexer_inputs(40, 6000, 64, 128, "fp8", 150, 300, drift=True, w_range=w_range, tag=43, n_sample=450)
     d = to_dev(inp)
@@ -170,6 +170,31 @@ def test_edge_positions_and_small_k(lib):
         check_rows(inp, idx, sc, range(T), f"edge k={k}")
         uidx, usc = _run_unfused(lib, d, k)
         check_rows(inp, uidx, usc, range(T), f"edge unfused k={k}")
+
+
+def test_degenerate_sizes(lib):
+    """No queries (empty outputs, nothing launched) and a one-key context in
+    every dtype: positions 0, -1 and past the context, k above the one valid
+    key, and sample entries past the context (dropped by the preparation)."""
+    for dt in ("f32", "bf16", "fp8"):
+        inp = indexer_inputs(0, 500, 64, 128, dt, 16, 10, tag=55, pos=np.zeros(0, np.int32), n_sample=48)
+        d = to_dev(inp)
+        say("degenerate T=0", dt)
+        idx, sc = _run_fused(lib, d, 16)
+        assert idx.shape == (0, 16) and sc.shape == (0, 16)
+        uidx, usc = _run_unfused(lib, d, 16)
+        assert uidx.shape == (0, 16) and usc.shape == (0, 16)
+        pos = np.array([0, -1, 7, 0, 3], np.int32)
+        for k in (1, 4):
+            inp = indexer_inputs(5, 1, 64, 128, dt, k, 1, tag=56, pos=pos, n_sample=3 * k)
+            d = to_dev(inp)
+            say("degenerate L=1", dt, "k", k)
+            idx, sc = _run_fused(lib, d, k)
+            check_rows(inp, idx, sc, range(5), f"L=1 {dt} k={k}")
+            for t in range(5):   # the one key, or nothing, then padding
+                assert sorted(idx[t].tolist()) == [-1] * (k - (pos[t] >= 0)) + [0] * int(pos[t] >= 0)
+            uidx, usc = _run_unfused(lib, d, k)
+            check_rows(inp, uidx, usc, range(5), f"L=1 unfused {dt} k={k}")
 
 
 def test_sorted_output(lib):
