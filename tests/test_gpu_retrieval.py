@@ -49,6 +49,24 @@ def test_retrieval_small(lib, shape):
     _check(r, idx, sc, range(T), f"retrieve {shape}")
 
 
+def test_retrieval_degenerate_sizes(lib):
+    """No queries (nothing launched), a one-row database, and fewer rows than
+    k (-1 padding): every valid row is returned with its exact score."""
+    import torch
+    r = retrieval_inputs(0, 500, 128, 16, n_centres=4, n_sample=0, device="cuda")
+    idx, sc = lib.retrieve(_q_dev(r), r["db"], 16, return_scores=True)
+    assert tuple(idx.shape) == (0, 16) and tuple(sc.shape) == (0, 16)
+    for T, N, D, k in [(3, 1, 64, 1), (3, 1, 64, 5), (37, 20, 128, 50), (5, 31, 768, 31)]:
+        say("retrieval degenerate", (T, N, D, k))
+        r = retrieval_inputs(T, N, D, k, n_centres=4, n_sample=min(N, 3 * k) // 2, device="cuda")
+        smp = torch.from_numpy(r["sample"]).cuda()
+        idx, sc = lib.retrieve(_q_dev(r), r["db"], k, sample=smp, return_scores=True)
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        _check(r, idx, sc, range(T), f"retrieve degenerate {(T, N, D, k)}")
+        for t in range(T):   # all N rows, then padding
+            assert sorted(idx[t].tolist()) == [-1] * max(0, k - N) + list(range(min(N, k)))
+
+
 def test_retrieval_independence(lib):
     import torch
     import indexer_topk_long_amd as ltk
