@@ -742,6 +742,26 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                     if (sl + 2 < NS) read_frag<DT, D>(kf[sl & 1], st, row0(sl + 2), lane);
                 }
                 const float p = relu_wsum<HB>(accC, ra.w);
+                if constexpr (DT == DT_FP8 && R == 1) {
+                    // issue order of the slot: its first MFMA, the LDS reads
+                    // of the fragment two slots ahead, then 14 VALU
+                    // instructions of the head sum behind each MFMA.  Left to
+                    // itself the scheduler sinks half of those reads to just
+                    // before their MFMA, which then waits on LDS (0.8-1 %
+                    // slower at 1M context; 12 and 16 per MFMA measured about
+                    // the same as 14, 8 and 10 slower; no gain at decode shape)
+                    if (sl + 1 < NS) {
+                        constexpr int NM = HB * HalfRow<DT, D>::KSTEPS;
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                        if (sl + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, HalfRow<DT, D>::NV, 0);   // LDS reads
+                        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
+#pragma unroll
+                        for (int g = 1; g < NM; ++g) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+                        }
+                    }
+                }
                 if (sl & 1) {
                     const int r0 = row0(sl - 1);
                     float I = combine_halves(pprev, p);
