@@ -106,7 +106,8 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
  *           (with T == 0 the per-query arrays q, q_scale, w, pos and the
  *           outputs may be NULL: the call checks its sizes and returns 0)
  *  pos      [T] int32 query positions; keys 0..pos[t] (and < L) are valid
- *  T >= 0, 1 <= H <= 64, D in {64, 128}, 1 <= L < 2^31, 1 <= topk <= 65536
+ *  T >= 0, 1 <= H <= 64, D in {64, 128}, 1 <= L <= 2^31 - 256 (key offsets
+ *           past a tile's end stay in int32), 1 <= topk <= 65536
  *           (a decode or speculative-decode step is the same call with T = 1..8
  *           queries at the newest positions; the key range is then split over
  *           every CU and the splits share one threshold per query)
@@ -129,7 +130,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
  * serves vector retrieval; "Large-scale retrieval", k from 1,024).
  *
  *  q [T, D] queries, db [N, D] database rows, both dtype (LTK_BF16 only),
- *  D in {64, 128, 256, 512, 768}, 1 <= N < 2^31; sample [n_sample] database
+ *  D in {64, 128, 256, 512, 768}, 1 <= N <= 2^31 - 256; sample [n_sample] database
  *  rows used to estimate the score range (duplicates and out-of-range
  *  entries ignored).  opts->l_splits sets the number of database splits.
  *  Other arguments as above.
@@ -157,7 +158,8 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
  * n_sample of them to out_sample [n_sample] (int32), in no particular order.
  * ws_bytes >= litetopk_workspace_bytes(LTK_KIND_NEXT_SAMPLE, 0, 0, 0, L, 1,
  * 0, 0, NULL): the key counts, a histogram of the count values and a few
- * words per workgroup.  Returns LTK_EWORKSPACE below that. */
+ * words per workgroup.  Returns LTK_EWORKSPACE below that, and LTK_EINVAL
+ * unless T >= 0, topk >= 1, 1 <= L <= 2^31 - 256 and 0 <= n_sample <= L. */
 int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64_t L, int32_t n_sample,
                          int32_t* out_sample, void* ws, size_t ws_bytes, void* stream);
 
