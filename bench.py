@@ -643,8 +643,9 @@ def main():
         log("  timing the CPU oracle ...")
         cpu = cpu_baseline(inp, args.cpu_rows)
 
+    ctx = "1M" if L == 1 << 20 else f"{L // 1024}K"
     line = {
-        "metric": "scored query-key pairs/s at 1M context, k=2048",
+        "metric": f"scored query-key pairs/s at {ctx} context, k={k}",
         "value": pairs / (ms_step * 1e-3),
         "unit": "pairs/s",
         "n_gpus": 1,
