@@ -58,3 +58,41 @@ def test_full_size_prefill(lib, name):
     torch.cuda.empty_cache()
     assert np.array_equal(a, b)
     assert np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 8], ids=["decode", "specdecode"])
+def test_full_size_decode(lib, T):
+    """Decode steps over the 1M-context fp8 keys, launched as the benchmark
+    launches them (the key range split over every CU, shared thresholds): the
+    newest T queries of the chunk, a bootstrap step on a random sample, then a
+    step sampled from its result.  Every row against the oracle, and
+    bit-identical to the unfused baseline."""
+    from workloads import random_sample
+    import torch
+    say(f"decode T={T}: generating")
+    full = indexer_workload("prefill-1m-fp8")
+    inp = dict(full)
+    for f in ("q", "q_scale", "w", "pos"):
+        inp[f] = np.ascontiguousarray(full[f][-T:])
+    inp["T"] = T
+    del full
+    d = to_dev(inp, sample=random_sample(3 * inp["topk"], inp["L"], tag=91))
+    k = inp["topk"]
+    say(f"decode T={T}: bootstrap step")
+    first = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=d["sample"], q_scale=d["q_scale"],
+                             k_scale=d["k_scale"])
+    say(f"decode T={T}: sampled step")
+    idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=first.flatten(),
+                                   q_scale=d["q_scale"], k_scale=d["k_scale"], return_scores=True,
+                                   return_stats=True)
+    assert st.overflow_rows == 0
+    idx_h, sc_h = idx.cpu().numpy(), sc.cpu().numpy()
+    check_rows(inp, idx_h, sc_h, range(T), f"decode T={T}")
+    uidx, usc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                         k_scale=d["k_scale"], return_scores=True)
+    a, asc = canon(idx_h, sc_h)
+    b, bsc = canon(uidx.cpu().numpy(), usc.cpu().numpy())
+    del uidx, usc
+    torch.cuda.empty_cache()
+    assert np.array_equal(a, b)
+    assert np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
