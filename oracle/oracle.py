@@ -193,9 +193,11 @@ def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t: int, dtype: s
 
 
 def next_sample(prev_idx: np.ndarray, L: int, n: int) -> np.ndarray:
-    """Keys 0..L-1 ranked by how many rows of prev_idx selected them (-1 entries
-    ignored), ties to the lower index; the first n.  This is the reading of
-    the pages' "reuse the previous chunk's top-3k tokens as the sample"
+    """Keys 0..L-1 ranked by how many entries of prev_idx name them (entries
+    outside [0, L), such as -1 padding, are ignored; a top-k row names a key
+    at most once, so this is the number of rows that selected it), ties to
+    the lower index; the first n, in rank order.  This is the reading of the
+    pages' "reuse the previous chunk's top-3k tokens as the sample"
     ("Sampling") for one shared sample per chunk."""
     p = np.asarray(prev_idx).ravel()
     counts = np.bincount(p[(p >= 0) & (p < L)], minlength=L)

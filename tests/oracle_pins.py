@@ -257,6 +257,93 @@ def check_retrieval_self_match(O, seed=10):
     assert np.array_equal(idx, idx2) and np.array_equal(sc, sc2)
 
 
+def check_retrieval_row_scores_closed_form(O):
+    """Scores of one query against a database of scaled basis vectors: row s is
+    c_s times unit vector e_{(7 s) mod D}, so its inner product with q is
+    c_s * q[(7 s) mod D] exactly.  Every value is a small dyadic number, exact
+    in bf16 and fp64.  The block size (5) does not divide N (23), so a block
+    written at the wrong offset or a transposed operand changes the result."""
+    import torch
+    N, D = 23, 16
+    c = np.array([(s % 9) - 4 + 0.5 * (s % 2) for s in range(N)], np.float32)
+    x = np.zeros((N, D), np.float32)
+    for s in range(N):
+        x[s, (7 * s) % D] = c[s]
+    q = np.array([[(d - 7) * 0.25 for d in range(D)], [1.0 + d for d in range(D)]], np.float32)
+
+    def bits(a):
+        return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    xb, qb = bits(x), bits(q)
+    for t in range(2):
+        ref = np.array([float(c[s]) * float(q[t, (7 * s) % D]) for s in range(N)])
+        for blk in (5, 1 << 18):
+            got = O.retrieval_row_scores(qb, xb, t, block=blk)
+            assert got.shape == (N,) and np.array_equal(got, ref), (t, blk, got, ref)
+
+
+def check_retrieval_row_scores_self_match(O, seed=13):
+    """Unit rows, query = a database row: by Cauchy-Schwarz that row scores
+    highest, with its squared norm; queries sit in every block of a block size
+    that does not divide N."""
+    import torch
+    g = np.random.default_rng(seed)
+    N, D, blk = 101, 12, 17
+    x = g.standard_normal((N, D))
+    x /= np.linalg.norm(x, axis=1, keepdims=True)
+    bits = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xd = O.bf16_to_f64(bits)
+    for r in (0, 16, 17, 50, 99, 100):
+        s = O.retrieval_row_scores(bits[r:r + 1], bits, 0, block=blk)
+        assert int(np.argmax(s)) == r
+        assert np.isclose(s[r], (xd[r] ** 2).sum(), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------- sample carried to the next chunk
+
+
+def check_next_sample_hand_example(O):
+    """Hand-derived count ranking with ties, padding and entries that are not
+    keys (tests/golden/next_sample_hand.json)."""
+    g = _load("next_sample_hand.json")
+    prev = np.array(g["prev_idx"], np.int32)
+    for c in g["cases"]:
+        got = O.next_sample(prev, g["L"], c["n"])
+        assert got.tolist() == c["sample"], (c, got.tolist())
+
+
+def _brute_next_sample(prev, L, n):
+    """Key s is taken iff fewer than n keys beat it, where key a beats key b
+    when it was selected more often, or as often with a lower index; counts
+    ignore entries outside [0, L)."""
+    counts = [0] * L
+    for row in prev:
+        for s in row:
+            if 0 <= int(s) < L:
+                counts[int(s)] += 1
+    taken = []
+    for s in range(L):
+        beats = sum(1 for a in range(L) if counts[a] > counts[s] or (counts[a] == counts[s] and a < s))
+        if beats < n:
+            taken.append(s)
+    return taken, counts
+
+
+def check_next_sample_brute_force(O, seed=14, trials=40):
+    """Brute-force ranks on small inputs full of ties, -1 padding and entries
+    past the key range; the oracle returns the taken keys in rank order."""
+    g = np.random.default_rng(seed)
+    for _ in range(trials):
+        L = int(g.integers(1, 30))
+        T, k = int(g.integers(0, 8)), int(g.integers(1, 7))
+        prev = g.integers(-2, L + 3, size=(T, k)).astype(np.int32)
+        n = int(g.integers(1, L + 1))
+        taken, counts = _brute_next_sample(prev, L, n)
+        got = O.next_sample(prev, L, n)
+        assert sorted(got.tolist()) == taken, (prev, L, n, got)
+        assert got.tolist() == sorted(taken, key=lambda s: (-counts[s], s))
+
+
 # --------------------------------------------------------------------------- LiteDSA packing
 
 
@@ -355,5 +442,6 @@ ALL_CHECKS = [
     check_hand_example, check_relu_identities, check_homogeneity, check_gemm_special_case,
     check_fp8_scale_factorisation, check_e4m3fn_points, check_e4m3fn_vs_torch, check_bf16_vs_torch,
     check_brute_force_ranks, check_exhaustive_subsets, check_selection_special_cases, check_causal,
-    check_retrieval_self_match,
+    check_retrieval_self_match, check_retrieval_row_scores_closed_form, check_retrieval_row_scores_self_match,
+    check_next_sample_hand_example, check_next_sample_brute_force,
 ]

@@ -138,6 +138,41 @@ def _dsa_descending(m):
     m.dsa_pack = dsa_pack
 
 
+def _ns_ties_high(m):
+    def next_sample(prev_idx, L, n):
+        p = np.asarray(prev_idx).ravel()
+        counts = np.bincount(p[(p >= 0) & (p < L)], minlength=L)
+        return np.lexsort((-np.arange(L), -counts))[:n].astype(np.int32)
+    m.next_sample = next_sample
+
+
+def _ns_counts_invalid(m):
+    # -1 padding wraps to the last key and entries past the range are clipped onto it
+    def next_sample(prev_idx, L, n):
+        p = np.asarray(prev_idx).ravel()
+        counts = np.bincount(np.clip(p % max(L, 1), 0, L - 1), minlength=L)
+        return np.lexsort((np.arange(L), -counts))[:n].astype(np.int32)
+    m.next_sample = next_sample
+
+
+def _rrs_block_offset(m):
+    orig = m.retrieval_row_scores
+
+    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18):
+        out = orig(q_raw, db_raw, t, dtype, block)
+        for s0 in range(0, len(out), block):
+            out[s0:s0 + block] = np.roll(out[s0:s0 + block], 1)
+        return out
+    m.retrieval_row_scores = retrieval_row_scores
+
+
+def _rrs_transposed(m):
+    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18):
+        qd = m.decode(q_raw[t:t + 1], dtype)[0]
+        return m.decode(db_raw, dtype)[:, ::-1] @ qd
+    m.retrieval_row_scores = retrieval_row_scores
+
+
 MUTANTS = {
     "dsa_mask_bits_reversed": (_dsa_bits_reversed, [P.check_dsa_hand_example, P.check_dsa_membership]),
     "dsa_list_descending": (_dsa_descending, [P.check_dsa_hand_example, P.check_dsa_membership]),
@@ -150,6 +185,14 @@ MUTANTS = {
     "head_weights_reversed": (_weights_reversed, [P.check_hand_example, P.check_relu_identities]),
     "bf16_wrong_shift": (_bf16_shift15, [P.check_bf16_vs_torch, P.check_retrieval_self_match]),
     "retrieval_transposed": (_transposed_keys, [P.check_retrieval_self_match]),
+    "next_sample_ties_to_higher_index": (_ns_ties_high, [P.check_next_sample_hand_example,
+                                                         P.check_next_sample_brute_force]),
+    "next_sample_counts_invalid_entries": (_ns_counts_invalid, [P.check_next_sample_hand_example,
+                                                                P.check_next_sample_brute_force]),
+    "retrieval_row_scores_block_offset": (_rrs_block_offset, [P.check_retrieval_row_scores_closed_form,
+                                                              P.check_retrieval_row_scores_self_match]),
+    "retrieval_row_scores_transposed": (_rrs_transposed, [P.check_retrieval_row_scores_closed_form,
+                                                          P.check_retrieval_row_scores_self_match]),
 }
 
 
