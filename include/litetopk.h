@@ -70,7 +70,8 @@ typedef struct {
     int32_t nbins;          /* equal-width bins over the sample's score range; 1..1024, default 256 */
     int32_t refresh_every;  /* threshold refresh after every N candidate batches; default 1; <0 = never */
     int32_t l_splits;       /* key-range splits per query group; default: chosen to fill the GPU */
-    int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc); needs topk <= 8192 */
+    int32_t sorted_output;  /* nonzero: each row ordered by (score desc, index asc), with or without
+                               out_score; needs topk <= 8192 */
     int64_t cand_capacity;  /* candidate-buffer entries per query; default 16384 (retrieval
                                max(262144, 64 x topk); shared thresholds: L when T x L x 8 B <= 512 MiB,
                                else >= 256 per split) */
@@ -79,11 +80,18 @@ typedef struct {
     int32_t shared_threshold; /* indexer: key splits of a query share one threshold histogram in the
                                  workspace (decode: few queries over a long context); 0 = when the
                                  scan has >= 16 splits, > 0 = always, < 0 = never */
+    int32_t flush_batch;    /* indexer: candidates per write-back batch of a wave's list, 32 or 64
+                               (LiteTopK summary, Methodology > 2. Filtering: batches of 32 or 64);
+                               default 64 */
 } ltk_opts;
 
 /* Optional counters (DEVICE struct, written by the call; pass NULL to skip). */
 typedef struct {
     uint64_t cand_written;        /* candidates appended over all queries (incl. dropped ones) */
+    uint64_t bytes_written;       /* bytes the call wrote to device memory for its rows: stored
+                                     candidates (8 B each), sample scores (4 B per query and
+                                     distinct sample key) and the outputs (4 B per index, 4 B per
+                                     score when asked); the full score matrix would be 4 B per pair */
     uint32_t max_cand_per_query;  /* largest per-query candidate count */
     uint32_t overflow_rows;       /* rows recovered by the exact overflow fallback */
 } ltk_stats;
@@ -100,8 +108,10 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
  * Sample -> Filter -> Select).
  *
  *  q        [T, H, D] queries (dtype); k [L, D] keys (dtype)
- *  q_scale  [T] fp32 per-query scales (fp8 only; NULL otherwise)
- *  k_scale  [L] fp32 per-key scales (fp8 only; NULL otherwise)
+ *  q_scale  [T] fp32 per-query scales (fp8 only; NULL otherwise), finite and > 0
+ *  k_scale  [L] fp32 per-key scales (fp8 only; NULL otherwise), finite and > 0
+ *           (the kernels move both scales out of the ReLU, which is exact for
+ *           positive scales only)
  *  w        [T, H] fp32 head weights (either sign)
  *           (with T == 0 the per-query arrays q, q_scale, w, pos and the
  *           outputs may be NULL: the call checks its sizes and returns 0)

@@ -30,10 +30,10 @@ from ._binding import (  # noqa: F401
     unfused_score_select,
     workspace_bytes,
 )
-from .prefill import next_sample, prefill_chunked  # noqa: F401
+from .prefill import next_sample, prefill_chunked, prefill_workspace_bytes  # noqa: F401
 
 __all__ = [
     "score_select", "retrieve", "unfused_score_select", "workspace_bytes", "strerror", "device_check",
     "Opts", "Stats", "LtkError", "next_sample", "prefill_chunked", "library", "exported_symbols",
-    "dsa_pack", "dsa_gather",
+    "dsa_pack", "dsa_gather", "prefill_workspace_bytes",
 ]

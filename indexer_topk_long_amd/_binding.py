@@ -17,7 +17,8 @@ _c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, c
 class _COpts(ctypes.Structure):
     _fields_ = [("nbins", _c_i32), ("refresh_every", _c_i32), ("l_splits", _c_i32),
                 ("sorted_output", _c_i32), ("cand_capacity", _c_i64),
-                ("scan_event_start", _c_p), ("scan_event_stop", _c_p), ("shared_threshold", _c_i32)]
+                ("scan_event_start", _c_p), ("scan_event_stop", _c_p), ("shared_threshold", _c_i32),
+                ("flush_batch", _c_i32)]
 
 
 @dataclass
@@ -31,15 +32,18 @@ class Opts:
     scan_event_start: int | None = None   # raw hipEvent_t handles (profiling)
     scan_event_stop: int | None = None
     shared_threshold: int = 0             # 0 auto (>= 16 key splits), 1 always, -1 never
+    flush_batch: int = 0                  # candidates per write-back batch: 32 or 64 (0 = 64)
 
     def c(self) -> _COpts:
         return _COpts(self.nbins, self.refresh_every, self.l_splits, int(bool(self.sorted_output)),
-                      self.cand_capacity, self.scan_event_start, self.scan_event_stop, self.shared_threshold)
+                      self.cand_capacity, self.scan_event_start, self.scan_event_stop, self.shared_threshold,
+                      self.flush_batch)
 
 
 @dataclass
 class Stats:
     cand_written: int
+    bytes_written: int
     max_cand_per_query: int
     overflow_rows: int
 
@@ -126,6 +130,49 @@ def _dev(t, name, dtype=None):
     return t
 
 
+def _expect(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(ref, **named):
+    for name, t in named.items():
+        if t is not None:
+            _expect(t.device == ref.device, f"{name} is on {t.device}, q on {ref.device}: all tensors must share one device")
+
+
+def _check_indexer_args(q, k, w, pos, q_scale=None, k_scale=None, sample=None):
+    """Shapes, dtypes and devices of an indexer call, checked before anything
+    reaches the library (a mismatch would make the kernels read past the end
+    of a buffer).  Returns (T, H, D, L, dtype code)."""
+    import torch
+    _expect(q.dim() == 3, f"q must be [T, H, D], got shape {tuple(q.shape)}")
+    _expect(k.dim() == 2, f"k must be [L, D], got shape {tuple(k.shape)}")
+    _expect(q.dtype == k.dtype, f"q ({q.dtype}) and k ({k.dtype}) must share one dtype")
+    T, H, D = q.shape
+    L = k.shape[0]
+    _expect(k.shape[1] == D, f"k rows have {k.shape[1]} elements, q rows {D}")
+    _expect(tuple(w.shape) == (T, H), f"w must be [{T}, {H}], got {tuple(w.shape)}")
+    _expect(w.dtype == torch.float32, f"w must be float32, got {w.dtype}")
+    _expect(tuple(pos.shape) == (T,), f"pos must be [{T}], got {tuple(pos.shape)}")
+    _expect(pos.dtype == torch.int32, f"pos must be int32, got {pos.dtype}")
+    dt = _dtype_code(q)
+    if dt == 2:
+        _expect(q_scale is not None and k_scale is not None, "fp8 needs q_scale [T] and k_scale [L]")
+        _expect(tuple(q_scale.shape) == (T,), f"q_scale must be [{T}], got {tuple(q_scale.shape)}")
+        _expect(tuple(k_scale.shape) == (L,), f"k_scale must be [{L}], got {tuple(k_scale.shape)}")
+        _expect(q_scale.dtype == torch.float32 and k_scale.dtype == torch.float32, "scales must be float32")
+    else:
+        _expect(q_scale is None and k_scale is None, "q_scale and k_scale are for float8_e4m3fn inputs only")
+    if sample is not None:
+        _expect(sample.dtype == torch.int32, f"sample must be int32, got {sample.dtype}")
+    _same_device(q, k=k, w=w, pos=pos, q_scale=q_scale, k_scale=k_scale, sample=sample)
+    for name, t in (("q", q), ("k", k), ("w", w), ("pos", pos), ("q_scale", q_scale), ("k_scale", k_scale),
+                    ("sample", sample)):
+        _dev(t, name)
+    return T, H, D, L, dt
+
+
 def _stream():
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -149,12 +196,12 @@ def _workspace(nbytes: int, device, ws=None):
 
 def _stats_buf(device):
     import torch
-    return torch.zeros(2, dtype=torch.int64, device=device)
+    return torch.zeros(3, dtype=torch.int64, device=device)   # ltk_stats: u64, u64, u32, u32
 
 
 def _read_stats(buf) -> Stats:
     v = buf.cpu()
-    return Stats(int(v[0]), int(v[1]) & 0xFFFFFFFF, (int(v[1]) >> 32) & 0xFFFFFFFF)
+    return Stats(int(v[0]), int(v[1]), int(v[2]) & 0xFFFFFFFF, (int(v[2]) >> 32) & 0xFFFFFFFF)
 
 
 def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=None, opts: Opts | None = None,
@@ -168,15 +215,7 @@ def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=Non
     sample), plus fp32 scores and/or Stats when asked.
     """
     import torch
-    _dev(q, "q"), _dev(k, "k"), _dev(w, "w", torch.float32), _dev(pos, "pos", torch.int32)
-    _dev(q_scale, "q_scale", torch.float32), _dev(k_scale, "k_scale", torch.float32)
-    if sample is not None:
-        _dev(sample, "sample", torch.int32)
-    if q.dim() != 3 or k.dim() != 2 or q.dtype != k.dtype:
-        raise ValueError("q must be [T, H, D] and k [L, D] of the same dtype")
-    T, H, D = q.shape
-    L = k.shape[0]
-    dt = _dtype_code(q)
+    T, H, D, L, dt = _check_indexer_args(q, k, w, pos, q_scale, k_scale, sample)
     ns = 0 if sample is None else sample.numel()
     lib = library()
     o = opts.c() if opts is not None else None
@@ -211,10 +250,7 @@ def unfused_score_select(q, k, w, pos, topk: int, q_scale=None, k_scale=None, re
                          workspace=None):
     """Unfused comparison path (full score matrix + radix select)."""
     import torch
-    _dev(q, "q"), _dev(k, "k"), _dev(w, "w", torch.float32), _dev(pos, "pos", torch.int32)
-    T, H, D = q.shape
-    L = k.shape[0]
-    dt = _dtype_code(q)
+    T, H, D, L, dt = _check_indexer_args(q, k, w, pos, q_scale, k_scale)
     lib = library()
     nbytes = lib.litetopk_workspace_bytes(KIND_UNFUSED, T, H, D, L, topk, 0, dt, None)
     ws = _workspace(nbytes, q.device, workspace)
@@ -232,9 +268,13 @@ def retrieve(q, db, topk: int, sample=None, opts: Opts | None = None, return_sco
              return_stats: bool = False, workspace=None):
     """Fused inner-product retrieval top-k (litetopk_retrieve); q [T, D], db [N, D] bfloat16."""
     import torch
-    _dev(q, "q"), _dev(db, "db")
+    _expect(q.dim() == 2 and db.dim() == 2, f"q must be [T, D] and db [N, D], got {tuple(q.shape)}, {tuple(db.shape)}")
+    _expect(q.dtype == db.dtype, f"q ({q.dtype}) and db ({db.dtype}) must share one dtype")
+    _expect(db.shape[1] == q.shape[1], f"db rows have {db.shape[1]} elements, q rows {q.shape[1]}")
     if sample is not None:
-        _dev(sample, "sample", torch.int32)
+        _expect(sample.dtype == torch.int32, f"sample must be int32, got {sample.dtype}")
+    _same_device(q, db=db, sample=sample)
+    _dev(q, "q"), _dev(db, "db"), _dev(sample, "sample")
     T, D = q.shape
     N = db.shape[0]
     dt = _dtype_code(q)
@@ -269,9 +309,8 @@ def dsa_pack(idx, L: int, group: int):
     the key) and the list lengths.  Returns (shared int32 [G, group*k],
     masks uint32 [G, group*k], lens int32 [G])."""
     import torch
+    _expect(idx.dim() == 2, f"idx must be [T, k], got {tuple(idx.shape)}")
     _dev(idx, "idx", torch.int32)
-    if idx.dim() != 2:
-        raise ValueError("idx must be [T, k]")
     T, k = idx.shape
     ng = (T + group - 1) // group
     shared = torch.empty((ng, group * k), dtype=torch.int32, device=idx.device)
@@ -288,6 +327,10 @@ def dsa_gather(kv, shared, lens, out=None):
     (litetopk_dsa_gather): out[g, j] = kv[shared[g, j]] for j < lens[g]; kv is
     [L, ...] with 16-byte-multiple rows.  Returns out [G, cap, *kv.shape[1:]]."""
     import torch
+    _expect(shared.dim() == 2 and lens.dim() == 1 and lens.shape[0] == shared.shape[0] and kv.dim() >= 1,
+            f"shared must be [G, cap], lens [G] and kv [L, ...]; got {tuple(shared.shape)}, {tuple(lens.shape)}, "
+            f"{tuple(kv.shape)}")
+    _same_device(kv, shared=shared, lens=lens, out=out)
     _dev(kv, "kv"), _dev(shared, "shared", torch.int32), _dev(lens, "lens", torch.int32)
     L = kv.shape[0]
     row_bytes = kv[0].numel() * kv.element_size() if L else 0
@@ -295,6 +338,8 @@ def dsa_gather(kv, shared, lens, out=None):
     if out is None:
         out = torch.empty((ng, cap) + tuple(kv.shape[1:]), dtype=kv.dtype, device=kv.device)
     else:
+        _expect(tuple(out.shape) == (ng, cap) + tuple(kv.shape[1:]),
+                f"out must be {(ng, cap) + tuple(kv.shape[1:])}, got {tuple(out.shape)}")
         _dev(out, "out", kv.dtype)
     rc = library().litetopk_dsa_gather(_ptr(kv), L, row_bytes, _ptr(shared), _ptr(lens), ng, cap, _ptr(out),
                                        _stream())

@@ -27,7 +27,7 @@ static int device_check() {
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Opts {
-    int nbins, refresh_every, l_splits, sorted, shared;
+    int nbins, refresh_every, l_splits, sorted, shared, flush;
     int64_t ccap;
     bool ccap_given;
     hipEvent_t ev0, ev1;
@@ -39,6 +39,7 @@ static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
     r.l_splits = 0;
     r.sorted = 0;
     r.shared = 0;
+    r.flush = kFlush;
     r.ccap = default_ccap;
     r.ccap_given = false;
     r.ev0 = r.ev1 = nullptr;
@@ -55,6 +56,8 @@ static int resolve_opts(const ltk_opts* o, int64_t default_ccap, Opts& r) {
     if (o->cand_capacity) r.ccap = o->cand_capacity;
     r.ccap_given = o->cand_capacity != 0;
     r.shared = o->shared_threshold;
+    if (o->flush_batch != 0 && o->flush_batch != 32 && o->flush_batch != 64) return LTK_EINVAL;
+    if (o->flush_batch) r.flush = o->flush_batch;
     return LTK_OK;
 }
 
@@ -238,6 +241,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
         a.s_splits *= 2;
     a.refresh_every = o.refresh_every;
     a.sorted = o.sorted;
+    a.flush = o.flush;
     a.ccap = plan.ccap;
     a.tail = reinterpret_cast<uint32_t*>(wsb + lay.tail);
     a.flags = reinterpret_cast<uint32_t*>(wsb + lay.flags);

@@ -35,6 +35,7 @@ __global__ void zero_kernel(uint32_t* p, size_t n_words, ltk_stats* stats) {
     for (size_t i = i0; i < n_words; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
     if (stats && i0 == 0) {
         stats->cand_written = 0;
+        stats->bytes_written = 0;
         stats->max_cand_per_query = 0;
         stats->overflow_rows = 0;
     }
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(1024) void sample_prep_kernel(const int32_t* sample
         for (size_t i = i0; i < n_zero; i += (size_t)(gridDim.x - 1) * 1024) zero[i] = 0u;
         if (stats && i0 == 0) {
             stats->cand_written = 0;
+            stats->bytes_written = 0;
             stats->max_cand_per_query = 0;
             stats->overflow_rows = 0;
         }
@@ -464,7 +466,7 @@ template <int DT, int D, int TB, bool ASYNC = false>
 __device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT, D, TB>& to, int key0, uint8_t* st,
                                           int wave, int lane) {
     using G = TileGeom<DT, D, TB>;
-    if (key0 + G::TK <= a.L) {
+    if (tile_inside(key0, G::TK, a.L)) {
         const uint8_t* tb = a.k + (size_t)key0 * G::RB;
 #pragma unroll
         for (int j = 0; j < G::PER_WAVE; ++j) {
@@ -551,8 +553,8 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         if (tt < a.T) e = max(e, min(a.pos[tt], a.L - 1) + 1);
     }
     const int kend = __builtin_amdgcn_readfirstlane(wave_max_i32(e));   // uniform: every lane holds the max
-    const int per = ((kend + a.n_splits - 1) / a.n_splits + G::TK - 1) / G::TK * G::TK;
-    const int k_lo = split * per, k_hi = min(kend, k_lo + per);
+    const KeyRange kr = split_range(kend, a.n_splits, split, G::TK);
+    const int k_lo = kr.lo, k_hi = kr.hi;
 
     const bool tv = t < a.T;
     const int my_pos = tv ? min(a.pos[t], a.L - 1) : -1;
@@ -569,15 +571,16 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     int cnt = 0;   // staged entries (wave-uniform)
     int fl = 0;    // batches written back
 
+    const int fb = a.flush;   // write-back batch: 32 or 64 entries
     auto flush = [&]() {
         uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)kFlush);
+        if (lane == 0) base = atomicAdd(&a.tail[t], (uint32_t)fb);
         base = lane0_u32(base);
         const uint2 en = stg[lane];
-        if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
-        const int rem = cnt - kFlush;
+        if (lane < fb && (int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
+        const int rem = cnt - fb;   // < 64: at most 63 + 64 entries were staged
         uint2 r{0u, 0u};
-        if (lane < rem) r = stg[kFlush + lane];
+        if (lane < rem) r = stg[fb + lane];
         if (lane < rem) stg[lane] = r;
         cnt = rem;
         ++fl;
@@ -620,7 +623,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 stg[cnt + mbcnt(mask)] = make_uint2((uint32_t)key, __float_as_uint(I));
             }
             cnt += __popcll(mask);
-            if (cnt >= kFlush) flush();
+            while (cnt >= fb) flush();   // twice at most, with batches of 32
         }
     };
 
@@ -798,10 +801,19 @@ constexpr int kRankMax = 512;   // threshold-bin entries ranked in LDS by counti
 // 32-bit LDS words of the select's counters: max(nbins, 256), rounded up to even.
 __host__ __device__ inline int fin_words(int nbins) { return ((nbins > 256 ? nbins : 256) + 1) & ~1; }
 
+// Score row of query t: the caller's out_score row, or, for a sorted output
+// without scores, an LDS row (the sort needs the scores; nothing reads them
+// afterwards), else none.
+__device__ __forceinline__ float* score_row(const IdxArgs& a, int t, float* lds_row) {
+    if (a.out_score) return a.out_score + (size_t)t * a.topk;
+    return a.sorted ? lds_row : nullptr;
+}
+
 // Select of one row (LiteTopK pages, "Selection").  Returns true, with the
 // row's overflow flag set, when the candidate buffer overflowed and the row
 // must be recomputed.  LDS (sh): fin_words(nbins) counters, then kRankMax
-// rank keys and candidate entries, then the sort keys of a sorted output.
+// rank keys and candidate entries, then the sort keys of a sorted output and,
+// without out_score, its scores.
 __device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
     __shared__ int s_pick;
     __shared__ uint32_t s_above, s_cnt, s_ocnt, s_mcnt;
@@ -809,13 +821,17 @@ __device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
     const int k = a.topk;
     const uint32_t n = a.tail[t];
     int32_t* out = a.out_idx + (size_t)t * k;
-    float* osc = a.out_score ? a.out_score + (size_t)t * k : nullptr;
     uint64_t* rk = reinterpret_cast<uint64_t*>(sh + fin_words(a.nbins));        // [kRankMax]
     uint2* rent = reinterpret_cast<uint2*>(rk + kRankMax);                        // [kRankMax]
     uint64_t* sort_keys = reinterpret_cast<uint64_t*>(rent + kRankMax);
+    float* osc = score_row(a, t, reinterpret_cast<float*>(sort_keys + (a.sorted ? sort_p2(k) : 0)));
     if (tid == 0 && a.stats) {
         atomicAdd((unsigned long long*)&a.stats->cand_written, (unsigned long long)n);
         atomicMax(&a.stats->max_cand_per_query, n);
+        // stored candidates, this query's sample scores, its outputs
+        const uint64_t stored = (int64_t)n < a.ccap ? (uint64_t)n : (uint64_t)a.ccap;
+        const uint64_t b = 8ull * stored + 4ull * (uint64_t)(*a.nu) + 4ull * (uint64_t)k * (a.out_score ? 2u : 1u);
+        atomicAdd((unsigned long long*)&a.stats->bytes_written, (unsigned long long)b);
     }
     if ((int64_t)n > a.ccap) {   // the buffer overflowed: the fallback recomputes this row
         if (tid == 0) {
@@ -1005,6 +1021,10 @@ struct RescoreSource {
     }
 };
 
+__device__ __forceinline__ float* row_select_scores(const IdxArgs& a, int t, uint32_t* sh) {
+    return score_row(a, t, reinterpret_cast<float*>(sh + 256 + 2 * (a.sorted ? sort_p2(a.topk) : 0)));
+}
+
 // Indexer select: finalize, and for a row whose candidate buffer overflowed,
 // the exact select over re-computed scores in the same workgroup.
 template <int DT, int D, int HB>
@@ -1020,7 +1040,7 @@ __global__ __launch_bounds__(256) void select_kernel(IdxArgs a) {
     src.L = a.L;
     const int nvalid = max(min(a.pos[t], a.L - 1) + 1, 0);
     int32_t* out = a.out_idx + (size_t)t * a.topk;
-    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk : nullptr;
+    float* osc = row_select_scores(a, t, sh);
     select_row(src, nvalid, a.topk, out, osc, sh);
     if (a.sorted) sort_row_output(out, osc, a.topk, reinterpret_cast<uint64_t*>(sh + 256));
 }
@@ -1035,8 +1055,8 @@ __global__ __launch_bounds__(256) void unfused_score_kernel(IdxArgs a) {
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
     const int t = half ? tb : ta;
-    const int per = (((a.L + a.n_splits - 1) / a.n_splits) + 31) & ~31;
-    const int k_lo = split * per, k_hi = min(a.L, k_lo + per);
+    const KeyRange kr = split_range(a.L, a.n_splits, split, 32);
+    const int k_lo = kr.lo, k_hi = kr.hi;
     QueryRegs<DT, D, HB> ra, rb;
     load_query<DT, D, HB>(ra, a, ta);
     load_query<DT, D, HB>(rb, a, tb);
@@ -1057,7 +1077,7 @@ __global__ __launch_bounds__(256) void unfused_select_kernel(IdxArgs a) {
     MemSource src{a.S + (size_t)t * a.L};
     const int nvalid = max(min(a.pos[t], a.L - 1) + 1, 0);
     int32_t* out = a.out_idx + (size_t)t * a.topk;
-    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk : nullptr;
+    float* osc = row_select_scores(a, t, sh);
     select_row(src, nvalid, a.topk, out, osc, sh);
     if (a.sorted) sort_row_output(out, osc, a.topk, reinterpret_cast<uint64_t*>(sh + 256));
 }
@@ -1235,14 +1255,13 @@ static int scan_waves_per_query(int T, int nb) {
     return std::min(r, nb);
 }
 
+// sort keys of a sorted row, and its LDS scores when there is no out_score
 static size_t sort_lds(const IdxArgs& a) {
     if (!a.sorted) return 0;
-    int p2 = 1;
-    while (p2 < a.topk) p2 <<= 1;
-    return (size_t)p2 * 8;
+    return (size_t)sort_p2(a.topk) * 8 + (a.out_score ? 0 : (size_t)a.topk * 4);
 }
 
-// finalize_row's LDS: counters, the threshold bin's rank keys and positions, sort keys
+// finalize_row's LDS: counters, the threshold bin's rank keys and positions, sort keys and scores
 static size_t fin_lds_bytes(const IdxArgs& a) {
     return (size_t)fin_words(a.nbins) * 4 + (size_t)kRankMax * 16 + sort_lds(a);
 }
@@ -1322,7 +1341,7 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         }
         if (R == 1 && !launched) { launch_scan(ic<1>{}, std::false_type{}); launched = true; }
         if (!launched) { err = hipErrorInvalidValue; return; }
-        const size_t sel_lds = std::max(fin_lds_bytes(a), 256 * 4 + sort_lds(a));
+        const size_t sel_lds = std::max(fin_lds_bytes(a), row_select_lds(a.topk, a.sorted, a.out_score != nullptr));
         allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
         select_kernel<DT_, D_, HB_><<<a.T, 256, sel_lds, st>>>(a);
         err = hipGetLastError();
@@ -1348,7 +1367,7 @@ hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipSt
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
         unfused_score_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, 0, st>>>(a);
-        const size_t lds = 256 * 4 + sort_lds(a);
+        const size_t lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
         allow_lds(unfused_select_kernel, lds);
         unfused_select_kernel<<<a.T, 256, lds, st>>>(a);
         err = hipGetLastError();

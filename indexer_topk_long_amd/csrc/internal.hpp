@@ -6,12 +6,13 @@
 #include <stdint.h>
 
 #include "litetopk.h"
+#include "split.hpp"
 
 namespace ltk {
 
 constexpr int kQPG = 8;              // queries per workgroup (4 waves x 2 queries)
 constexpr int kStage = 128;          // staging entries per query in LDS (>= 64 + 32)
-constexpr int kFlush = 64;           // write-back batch (one wave64 of 8-byte entries)
+constexpr int kFlush = 64;           // default write-back batch (one wave64 of 8-byte entries)
 constexpr int kDefaultBins = 256;
 constexpr int kMaxBins = 1024;
 constexpr int64_t kDefaultCcap = 16384;
@@ -107,6 +108,7 @@ struct IdxArgs {
     int s_splits;            // sample splits per query group (sample pass)
     int refresh_every;       // <= 0: never
     int sorted;
+    int flush;               // candidates per write-back batch (32 or 64)
     int64_t ccap;
     // workspace
     uint32_t* tail;

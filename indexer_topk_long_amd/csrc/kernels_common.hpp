@@ -137,29 +137,40 @@ __device__ inline void block_sort_desc(uint64_t* keys, int n) {
     }
 }
 
-// Order the k outputs of one row by (score desc, index asc).
+// Power of two >= k: the sort keys of a sorted row.
+__host__ __device__ inline int sort_p2(int k) {
+    int p2 = 1;
+    while (p2 < k) p2 <<= 1;
+    return p2;
+}
+
+// LDS of an exact row select (select_row) followed by an optional sort:
+// 256 digit counters, the sort keys, and, for a sorted output without
+// out_score, an LDS row of the scores (the sort ranks by them).
+__host__ __device__ inline size_t row_select_lds(int topk, bool sorted, bool with_scores) {
+    if (!sorted) return 256 * 4;
+    return 256 * 4 + (size_t)sort_p2(topk) * 8 + (with_scores ? 0 : (size_t)topk * 4);
+}
+
+// Order the k outputs of one row by (score desc, index asc).  osc holds the
+// row's scores (the caller's output row, or an LDS row when the caller asked
+// for indices only) and is rewritten in the same order.
 __device__ inline void sort_row_output(int32_t* out, float* osc, int k, uint64_t* keys) {
     __syncthreads();
     for (int i = threadIdx.x; i < k; i += blockDim.x) {
         const int idx = out[i];
-        keys[i] = (idx >= 0) ? rank_key(osc ? osc[i] : 0.0f, idx) : 0ull;
+        keys[i] = (idx >= 0) ? rank_key(osc[i], idx) : 0ull;
     }
-    // without scores, order by index only
-    if (!osc)
-        for (int i = threadIdx.x; i < k; i += blockDim.x)
-            keys[i] = (out[i] >= 0) ? (uint64_t)(0xffffffffu - (uint32_t)out[i]) + 1ull : 0ull;
     __syncthreads();
     block_sort_desc(keys, k);
     for (int i = threadIdx.x; i < k; i += blockDim.x) {
         const uint64_t key = keys[i];
         if (key == 0ull) {
             out[i] = -1;
-            if (osc) osc[i] = __builtin_nanf("");
-        } else if (osc) {
+            osc[i] = __builtin_nanf("");
+        } else {
             out[i] = (int32_t)(0xffffffffu - (uint32_t)key);
             osc[i] = unord_f32((uint32_t)(key >> 32));
-        } else {
-            out[i] = (int32_t)(0xffffffffu - (uint32_t)(key - 1ull));
         }
     }
     __syncthreads();

@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int split = (slot / a.n_qgroups) * 8 + xcd, qgroup = slot % a.n_qgroups;
     if (split >= a.n_splits) return;
     const int q0 = qgroup * (kRetrWaves * kRetrQ) + wave * kRetrQ;
-    const int per = ((a.N + a.n_splits - 1) / a.n_splits + kRetrRows - 1) / kRetrRows * kRetrRows;
-    const int r_lo = split * per, r_hi = min(a.N, r_lo + per);
+    const KeyRange rr = split_range(a.N, a.n_splits, split, kRetrRows);
+    const int r_lo = rr.lo, r_hi = rr.hi;
     const int ntiles = (r_hi > r_lo) ? (r_hi - r_lo + kRetrRows - 1) / kRetrRows : 0;
     if (ntiles == 0) return;
 
@@ -441,7 +441,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     src.db = a.db;
     src.N = a.N;
     int32_t* out = a.out_idx + (size_t)t * a.topk;
-    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk : nullptr;
+    // a sorted row without out_score ranks by an LDS row of scores past the sort keys
+    float* osc = a.out_score ? a.out_score + (size_t)t * a.topk
+                             : (a.sorted ? reinterpret_cast<float*>(sh + 256 + 2 * sort_p2(a.topk)) : nullptr);
     select_row(src, a.N, a.topk, out, osc, sh);
     if (a.sorted) sort_row_output(out, osc, a.topk, reinterpret_cast<uint64_t*>(sh + 256));
 }
@@ -473,9 +475,7 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
     retr_compact_kernel<<<a.T, 256, compact_lds, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = launch_finalize(fin, st)) != hipSuccess) return e;
-    int p2 = 1;
-    while (p2 < a.topk) p2 <<= 1;
-    const size_t fb_lds = 256 * 4 + (a.sorted ? (size_t)p2 * 8 : 0);
+    const size_t fb_lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
     if (fb_lds > 65536)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_fallback_kernel<D>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)fb_lds);

@@ -20,6 +20,10 @@ def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
     (ties to the lower index; in no particular order), computed on the device
     by litetopk_next_sample."""
     import torch
+    if prev_idx.dim() != 2:
+        raise ValueError(f"prev_idx must be [T, k], got {tuple(prev_idx.shape)}")
+    if not 0 <= n_sample <= L:
+        raise ValueError(f"n_sample must lie in [0, L = {L}], got {n_sample}")
     _dev(prev_idx, "prev_idx", torch.int32)
     T, k = prev_idx.shape
     lib = library()
@@ -36,6 +40,26 @@ def next_sample(prev_idx, L: int, n_sample: int, workspace=None):
     return out
 
 
+def prefill_workspace_bytes(n_queries: int, chunk: int, H: int, D: int, L: int, topk: int, n_sample: int,
+                            dtype_code: int, opts=None) -> int:
+    """Workspace of `prefill_chunked`: the largest that any of its calls needs.
+    A short last chunk can need more than a full one (fewer query groups get
+    more key splits, which can switch on shared thresholds and a larger
+    candidate capacity), and the first chunk runs without a sample."""
+    from ._binding import KIND_SCORE_SELECT, workspace_bytes
+    sizes = {min(chunk, n_queries)}
+    if n_queries % chunk:
+        sizes.add(n_queries % chunk)
+    need = 0
+    for T in sizes:
+        for ns in (0, n_sample):
+            b = workspace_bytes(KIND_SCORE_SELECT, T, H, D, L, topk, ns, dtype_code, opts)
+            if b == 0:
+                raise ValueError("invalid prefill sizes")
+            need = max(need, b)
+    return need
+
+
 def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_sample: int | None = None,
                     k_scale=None, first_pos: int = 0, opts=None, keep_outputs: bool = False,
                     diagnostics: bool = True):
@@ -46,8 +70,9 @@ def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_
 
     `queries` is either (q [n_queries, H, D], w [n_queries, H], q_scale or None)
     or a function (c0, c1) -> that triple for the queries c0 .. c1-1, so a long
-    prefill need not hold every query at once.  One workspace, sized for a full
-    chunk over all L keys, serves every chunk.
+    prefill need not hold every query at once.  One workspace, sized for the
+    largest call (`prefill_workspace_bytes`), serves every chunk; the sample
+    size is clamped to L.
 
     Returns {"chunks": [per-chunk dict], "workspace_bytes": int, "last": int32
     [rows, topk] of the last chunk, "outputs": list of every chunk's indices if
@@ -58,10 +83,10 @@ def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_
     back with no host synchronisation between them.
     """
     import torch
-    from ._binding import KIND_SCORE_SELECT, _dtype_code, score_select, workspace_bytes
+    from ._binding import _dtype_code, score_select
 
     L = k.shape[0]
-    n_sample = 3 * topk if n_sample is None else n_sample
+    n_sample = min(3 * topk if n_sample is None else n_sample, L)
 
     def get(c0, c1):
         if callable(queries):
@@ -71,7 +96,7 @@ def prefill_chunked(queries, k, topk: int, n_queries: int, chunk: int = 8192, n_
 
     q0, _, _ = get(0, min(chunk, n_queries))
     H, D = q0.shape[1], q0.shape[2]
-    nbytes = workspace_bytes(KIND_SCORE_SELECT, chunk, H, D, L, topk, n_sample, _dtype_code(q0), opts)
+    nbytes = prefill_workspace_bytes(n_queries, chunk, H, D, L, topk, n_sample, _dtype_code(q0), opts)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
     ws_sample = torch.empty(next_sample_workspace_bytes(L), dtype=torch.uint8, device=k.device)
     records, outputs, prev = [], [], None

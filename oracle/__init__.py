@@ -9,6 +9,8 @@ from .oracle import (  # noqa: F401
     dsa_gather,
     dsa_pack,
     e4m3fn_table,
+    first_copy,
+    key_table,
     indexer_row_scores,
     indexer_scores,
     next_sample,

@@ -24,7 +24,8 @@ their selections and a membership bitmask per union entry.
 Inputs are the raw storage bits handed to the GPU (fp32 values, bf16 bit
 patterns, OCP e4m3fn bit patterns with fp32 per-token scales) and are decoded
 exactly to fp64; all arithmetic is fp64.  Ties are broken towards the lower
-index by a full lexicographic sort.
+index by a full lexicographic sort; bit-identical keys (or database rows)
+are scored once, at their first copy, so that they tie exactly.
 
 Parity status: every function here is pinned by the tests in
 tests/test_oracle.py (brute-force ranks, exhaustive subsets, hand-derived
@@ -109,6 +110,44 @@ def retrieval_scores(q: np.ndarray, db: np.ndarray) -> np.ndarray:
     return db @ q
 
 
+def first_copy(raw: np.ndarray, scale: np.ndarray | None = None) -> np.ndarray:
+    """For each stored row, the index of the first row with the same stored
+    bits (and the same per-row scale, when given).
+
+    A score is a function of the key's value, so bit-identical keys must get
+    bit-identical scores for ties to reach the index order.  A blocked BLAS
+    product does not guarantee that (rows in a block's tail or in another
+    thread's share can take a different rounding path), so the scoring
+    functions evaluate each distinct row once, at its first copy, and hand
+    that value to every copy.  Rows are grouped by a 64-bit hash of their
+    bytes and every grouping is then confirmed byte for byte; a row whose
+    bytes differ from its group's first row keeps itself.
+    """
+    n = raw.shape[0]
+    b = np.ascontiguousarray(raw).reshape(n, -1).view(np.uint8)
+    if scale is not None:
+        b = np.concatenate([b, np.ascontiguousarray(scale, dtype=np.float32).reshape(n, 1).view(np.uint8)], axis=1)
+    if b.shape[1] % 8:
+        b = np.concatenate([b, np.zeros((n, 8 - b.shape[1] % 8), np.uint8)], axis=1)
+    words = np.ascontiguousarray(b).view(np.uint64)
+    h = np.zeros(n, np.uint64)
+    with np.errstate(over="ignore"):
+        for j in range(words.shape[1]):
+            h = h * np.uint64(0x9E3779B97F4A7C15) + words[:, j]
+    _, first, inv = np.unique(h, return_index=True, return_inverse=True)
+    rep = first[inv.ravel()].astype(np.int64)
+    moved = np.nonzero(rep != np.arange(n))[0]
+    if len(moved):
+        same = np.all(words[moved] == words[rep[moved]], axis=1)
+        rep[moved[~same]] = moved[~same]
+    return rep
+
+
+def key_table(inp: dict):
+    """(decoded keys fp64 [L, D], first_copy of each key) of an indexer input."""
+    return decode(inp["k"], inp["dtype"], inp.get("k_scale")), first_copy(inp["k"], inp.get("k_scale"))
+
+
 # ---------------------------------------------------------------------------
 # selection
 # ---------------------------------------------------------------------------
@@ -130,16 +169,19 @@ def valid_keys(pos_t: int, L: int) -> np.ndarray:
     return np.arange(0, hi + 1, dtype=np.int64) if hi >= 0 else np.zeros(0, dtype=np.int64)
 
 
-def indexer_row_scores(inp: dict, t: int, kd: np.ndarray | None = None):
-    """(valid key indices, fp64 scores) of query t of an indexer input dict."""
+def indexer_row_scores(inp: dict, t: int, keys=None):
+    """(valid key indices, fp64 scores) of query t of an indexer input dict.
+
+    ``keys`` is ``key_table(inp)``, computed here when not given.  A key's
+    score is the score of its first bit-identical copy (``first_copy``)."""
     dt = inp["dtype"]
-    if kd is None:
-        kd = decode(inp["k"], dt, inp.get("k_scale"))
+    kd, rep = key_table(inp) if keys is None else keys
     qs = inp.get("q_scale")
     qd = decode(inp["q"][t : t + 1], dt, None if qs is None else qs[t : t + 1])[0]
     w = np.asarray(inp["w"][t], dtype=np.float32).astype(np.float64)
     v = valid_keys(inp["pos"][t], inp["L"])
-    return v, indexer_scores(qd, w, kd[: len(v)])   # V_t is the prefix 0..pos[t]
+    s = indexer_scores(qd, w, kd[: len(v)])           # V_t is the prefix 0..pos[t]
+    return v, s[rep[: len(v)]]                         # a first copy never lies after its copies
 
 
 def oracle_indexer(inp: dict, rows=None, with_scores: bool = True):
@@ -149,11 +191,11 @@ def oracle_indexer(inp: dict, rows=None, with_scores: bool = True):
     """
     T, k = inp["T"], inp["topk"]
     rows = np.arange(T) if rows is None else np.asarray(rows)
-    kd = decode(inp["k"], inp["dtype"], inp.get("k_scale"))
+    keys = key_table(inp)
     out_i = np.full((len(rows), k), -1, dtype=np.int32)
     out_s = np.full((len(rows), k), np.nan, dtype=np.float64)
     for r, t in enumerate(rows):
-        v, s = indexer_row_scores(inp, int(t), kd)
+        v, s = indexer_row_scores(inp, int(t), keys)
         out_i[r], out_s[r] = topk_row(s, v, k)
     return (out_i, out_s) if with_scores else out_i
 
@@ -173,6 +215,7 @@ def oracle_retrieval(q_raw: np.ndarray, db_raw: np.ndarray, k: int, rows=None, d
     for s0 in range(0, N, block):
         xd = decode(db_raw[s0 : s0 + block], dtype)      # [n, D]
         scores[:, s0 : s0 + len(xd)] = (xd @ qd.T).T
+    scores = scores[:, first_copy(db_raw)]               # bit-identical rows score alike
     idx = np.arange(N, dtype=np.int64)
     out_i = np.full((len(rows), k), -1, dtype=np.int32)
     out_s = np.full((len(rows), k), np.nan, dtype=np.float64)
@@ -182,14 +225,16 @@ def oracle_retrieval(q_raw: np.ndarray, db_raw: np.ndarray, k: int, rows=None, d
 
 
 def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t: int, dtype: str = "bf16",
-                         block: int = 1 << 18) -> np.ndarray:
-    """fp64 scores of query t against every database row."""
+                         block: int = 1 << 18, rep: np.ndarray | None = None) -> np.ndarray:
+    """fp64 scores of query t against every database row.  ``rep`` is
+    ``first_copy(db_raw)`` (computed here when not given): each row takes the
+    score of its first bit-identical copy."""
     qd = decode(q_raw[t : t + 1], dtype)[0]
     N = db_raw.shape[0]
     out = np.empty(N, dtype=np.float64)
     for s0 in range(0, N, block):
         out[s0 : s0 + block] = retrieval_scores(qd, decode(db_raw[s0 : s0 + block], dtype))
-    return out
+    return out[first_copy(db_raw) if rep is None else rep]
 
 
 def next_sample(prev_idx: np.ndarray, L: int, n: int) -> np.ndarray:

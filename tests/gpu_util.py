@@ -81,14 +81,28 @@ def check_row(g_idx, g_sc, v, s, k, dtype, where=""):
 
 def check_rows(inp, g_idx, g_sc, rows, where=""):
     """Acceptance rule on the given query rows (oracle scored on the CPU)."""
-    from oracle import decode, indexer_row_scores
-    kd = decode(inp["k"], inp["dtype"], inp.get("k_scale"))
+    from oracle import indexer_row_scores, key_table
+    keys = key_table(inp)
     swaps = 0
     for t in rows:
-        v, s = indexer_row_scores(inp, int(t), kd)
+        v, s = indexer_row_scores(inp, int(t), keys)
         swaps += check_row(g_idx[t], None if g_sc is None else g_sc[t], v, s, inp["topk"], inp["dtype"],
                            f"{where} row {t}") or 0
     return swaps
+
+
+def oracle_prev_chunk_sample(inp: dict) -> np.ndarray:
+    """The sample of an indexer chunk as the pages define it: the previous
+    chunk's top-k selections (from the oracle), ranked by how many of its rows
+    selected each key, the first 3k ("Sampling")."""
+    from oracle import next_sample, oracle_indexer
+    pidx = oracle_indexer(inp["prev"], with_scores=False)
+    return next_sample(pidx, inp["L"], 3 * inp["topk"])
+
+
+def spaced_rows(T: int, n: int = 64) -> list:
+    """n evenly spaced query rows plus the first two and the last two."""
+    return sorted(set(np.linspace(0, T - 1, n).round().astype(int).tolist() + [0, 1, T - 2, T - 1]))
 
 
 def canon(idx, sc=None):

@@ -344,6 +344,49 @@ def check_next_sample_brute_force(O, seed=14, trials=40):
         assert got.tolist() == sorted(taken, key=lambda s: (-counts[s], s))
 
 
+# --------------------------------------------------------------------------- identical keys
+
+
+def check_first_copy_brute_force(O, seed=15):
+    """first_copy against a dictionary from each row's bytes (and scale) to the
+    first index holding them, on small arrays full of repeated rows."""
+    g = np.random.default_rng(seed)
+    for dt, D in ((np.uint8, 5), (np.uint8, 16), (np.uint16, 3), (np.float32, 4)):
+        for with_scale in (False, True):
+            n = int(g.integers(1, 60))
+            src = g.integers(0, 7, size=(8, D)).astype(dt)
+            raw = src[g.integers(0, 8, size=n)]
+            sc = g.integers(1, 3, size=n).astype(np.float32) if with_scale else None
+            first = {}
+            want = []
+            for r in range(n):
+                key = raw[r].tobytes() + (sc[r].tobytes() if with_scale else b"")
+                want.append(first.setdefault(key, r))
+            got = O.first_copy(raw, sc)
+            assert got.tolist() == want, (dt, D, with_scale, got, want)
+
+
+def check_identical_keys_tie(O):
+    """Bit-identical key rows score bit-identically, so a tie group cut by the
+    k-th score gives its lowest key indices, whatever rounding path a blocked
+    product would take for each copy."""
+    from tests.tie_cases import tied_indexer_inputs
+    inp = tied_indexer_inputs(16, 6000, 64, 128, "bf16", 200, 37, tag=4)
+    k = inp["topk"]
+    keys = O.key_table(inp)
+    src = inp["src_of_key"]
+    for t in range(inp["T"]):
+        v, s = O.indexer_row_scores(inp, t, keys)
+        for u in np.unique(src[: len(v)]):
+            grp = s[src[: len(v)] == u]
+            assert np.all(grp == grp[0]), (t, u)
+        idx, _ = O.topk_row(s, v, k)
+        vk = np.sort(s)[::-1][k - 1]
+        need = k - int((s > vk).sum())
+        want = set(v[s > vk].tolist()) | set(v[s == vk][:need].tolist())
+        assert set(idx.tolist()) == want, t
+
+
 # --------------------------------------------------------------------------- LiteDSA packing
 
 
@@ -444,4 +487,5 @@ ALL_CHECKS = [
     check_brute_force_ranks, check_exhaustive_subsets, check_selection_special_cases, check_causal,
     check_retrieval_self_match, check_retrieval_row_scores_closed_form, check_retrieval_row_scores_self_match,
     check_next_sample_hand_example, check_next_sample_brute_force,
+    check_first_copy_brute_force, check_identical_keys_tie,
 ]

@@ -37,15 +37,16 @@ def test_header_is_c_and_matches_binding_layout(tmp_path):
         '#include <stdio.h>\n#include <stddef.h>\n#include "litetopk.h"\n'
         'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(ltk_opts), offsetof(ltk_opts, cand_capacity),'
         ' offsetof(ltk_opts, scan_event_stop), sizeof(ltk_stats), offsetof(ltk_stats, overflow_rows));'
-        ' printf("%zu\\n", offsetof(ltk_opts, shared_threshold)); return 0;}\n')
+        ' printf("%zu %zu %zu\\n", offsetof(ltk_opts, shared_threshold), offsetof(ltk_opts, flush_batch),'
+        ' offsetof(ltk_stats, bytes_written)); return 0;}\n')
     exe = tmp_path / "probe"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", B.INCLUDE, str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     from indexer_topk_long_amd._binding import _COpts
     assert got[0] == ctypes.sizeof(_COpts)
     assert got[1] == _COpts.cand_capacity.offset and got[2] == _COpts.scan_event_stop.offset
-    assert got[3] == 16 and got[4] == 12     # Stats: u64 + u32 + u32, read as two int64 by the binding
-    assert got[5] == _COpts.shared_threshold.offset
+    assert got[3] == 24 and got[4] == 20     # Stats: u64 + u64 + u32 + u32, read as three int64 by the binding
+    assert got[5] == _COpts.shared_threshold.offset and got[6] == _COpts.flush_batch.offset and got[7] == 8
 
 
 def test_strerror(L):
@@ -103,6 +104,8 @@ def _ss(L, **kw):
     (dict(ns=3), EINVAL), (dict(ns=-1), EINVAL), (dict(wsb=100), EWS),
     (dict(opts=ltk.Opts(nbins=1025)), EINVAL), (dict(opts=ltk.Opts(l_splits=-2)), EINVAL),
     (dict(opts=ltk.Opts(sorted_output=True), topk=9000), EINVAL), (dict(opts=ltk.Opts(cand_capacity=-5)), EINVAL),
+    (dict(opts=ltk.Opts(flush_batch=48)), EINVAL), (dict(opts=ltk.Opts(flush_batch=128)), EINVAL),
+    (dict(T=0, opts=ltk.Opts(flush_batch=32)), OK), (dict(T=0, opts=ltk.Opts(flush_batch=64)), OK),
     (dict(T=0), OK),
     # no queries: the per-query arrays (query scales included) may be NULL; key scales may not
     (dict(T=0, q=None, w=None, pos=None, out=None, dt=FP8, ks=A16), OK),
@@ -162,3 +165,125 @@ def test_dsa_argument_errors(L):
     assert ga(MIS, 100, 32, A16, A16, 4, 64, A16, None) == EINVAL           # misaligned key/value rows
     assert ga(A16, 100, 32, A16, A16, 4, 0, A16, None) == EINVAL
     assert ga(None, 100, 32, None, None, 0, 64, None, None) == OK
+
+
+# --------------------------------------------------------------------------- binding argument checks
+
+
+def _cpu(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _indexer_args(T=4, H=8, D=64, Lk=100, dtype="f32"):
+    import torch
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
+    a = dict(q=_cpu((T, H, D), tdt), k=_cpu((Lk, D), tdt), w=_cpu((T, H), torch.float32),
+             pos=_cpu((T,), torch.int32), q_scale=None, k_scale=None)
+    if dtype == "fp8":
+        a.update(q_scale=_cpu((T,), torch.float32), k_scale=_cpu((Lk,), torch.float32))
+    return a
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(k=((100, 128), "f32")), "k rows have 128"),               # q with D = 64, k with D = 128
+    (dict(w=((4, 7), "w")), r"w must be \[4, 8\]"),
+    (dict(w=((3, 8), "w")), r"w must be \[4, 8\]"),
+    (dict(pos=((5,), "pos")), r"pos must be \[4\]"),
+    (dict(k=((100, 64), "bf16")), "share one dtype"),
+    (dict(q=((4, 64), "f32")), r"q must be \[T, H, D\]"),
+    (dict(q_scale=((4,), "w")), "float8_e4m3fn inputs only"),
+])
+def test_binding_rejects_mismatched_indexer_arguments(change, match):
+    """Every size the kernels rely on is checked before the library is called
+    (on CPU tensors the checks run before the device check)."""
+    import torch
+    a = _indexer_args()
+    for name, (shape, kind) in change.items():
+        a[name] = _cpu(shape, {"f32": torch.float32, "bf16": torch.bfloat16, "w": torch.float32,
+                               "pos": torch.int32}[kind])
+    with pytest.raises(ValueError, match=match):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=a["q_scale"], k_scale=a["k_scale"])
+    with pytest.raises(ValueError, match=match):
+        ltk.unfused_score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=a["q_scale"], k_scale=a["k_scale"])
+
+
+def test_binding_rejects_bad_fp8_scales_and_sample():
+    import torch
+    a = _indexer_args(dtype="fp8")
+    with pytest.raises(ValueError, match=r"k_scale must be \[100\]"):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=a["q_scale"], k_scale=_cpu((99,), torch.float32))
+    with pytest.raises(ValueError, match=r"q_scale must be \[4\]"):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=_cpu((3,), torch.float32), k_scale=a["k_scale"])
+    with pytest.raises(ValueError, match="fp8 needs"):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8)
+    with pytest.raises(ValueError, match="sample must be int32"):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=a["q_scale"], k_scale=a["k_scale"],
+                         sample=_cpu((6,), torch.int64))
+    # consistent shapes on the CPU: only the device check is left
+    with pytest.raises(ValueError, match="device tensor"):
+        ltk.score_select(a["q"], a["k"], a["w"], a["pos"], 8, q_scale=a["q_scale"], k_scale=a["k_scale"])
+
+
+def test_binding_rejects_mismatched_retrieval_and_dsa_arguments():
+    import torch
+    q, db = _cpu((4, 128), torch.bfloat16), _cpu((1000, 64), torch.bfloat16)
+    with pytest.raises(ValueError, match="db rows have 64"):
+        ltk.retrieve(q, db, 8)
+    with pytest.raises(ValueError, match="share one dtype"):
+        ltk.retrieve(q, _cpu((1000, 128), torch.float32), 8)
+    with pytest.raises(ValueError, match=r"idx must be \[T, k\]"):
+        ltk.dsa_pack(_cpu((16,), torch.int32), 100, 4)
+    with pytest.raises(ValueError, match="lens"):
+        ltk.dsa_gather(_cpu((100, 16), torch.uint8), _cpu((3, 8), torch.int32), _cpu((2,), torch.int32))
+    with pytest.raises(ValueError, match="n_sample must lie"):
+        ltk.next_sample(_cpu((4, 8), torch.int32), 10, 11)
+
+
+def test_prefill_workspace_covers_a_short_last_chunk(L):
+    """A short last chunk gets more key splits, which switches on shared
+    thresholds and a larger capacity: the driver's one workspace must cover it,
+    and the first chunk's call without a sample."""
+    full = ltk.workspace_bytes(0, 1024, 64, 128, 1 << 20, 2048, 6144, FP8)
+    tail = ltk.workspace_bytes(0, 40, 64, 128, 1 << 20, 2048, 6144, FP8)
+    assert tail > full
+    need = ltk.prefill_workspace_bytes(1024 * 3 + 40, 1024, 64, 128, 1 << 20, 2048, 6144, FP8)
+    assert need >= max(full, tail, ltk.workspace_bytes(0, 40, 64, 128, 1 << 20, 2048, 0, FP8))
+    assert ltk.prefill_workspace_bytes(2048, 1024, 64, 128, 1 << 20, 2048, 6144, FP8) == max(
+        full, ltk.workspace_bytes(0, 1024, 64, 128, 1 << 20, 2048, 0, FP8))
+
+
+def test_split_ranges_at_the_key_limit(tmp_path):
+    """The scans' split arithmetic (csrc/split.hpp) in 64 bits: at L near the
+    2^31 - 256 key limit, with up to 4,096 splits of 32- to 512-key tiles, the
+    ranges partition [0, L) into tile-aligned, ordered, non-negative pieces."""
+    src = tmp_path / "split_check.cpp"
+    src.write_text(r"""
+#include <stdio.h>
+#include "split.hpp"
+int main() {
+    const long long ends[] = {1, 511, 512, 513, 1048576, 2147483647LL - 256 - 511, 2147483647LL - 256};
+    const int ns[] = {1, 2, 3, 7, 256, 4096};
+    const int tiles[] = {32, 64, 128, 256, 512};
+    long long bad = 0;
+    for (long long end : ends) for (int n : ns) for (int tile : tiles) {
+        long long next = 0;
+        for (int s = 0; s < n; ++s) {
+            const ltk::KeyRange r = ltk::split_range(end, n, s, tile);
+            if (r.lo < 0 || r.hi < r.lo || r.hi > end || r.lo != next) ++bad;
+            if (r.hi > r.lo && r.lo % tile != 0) ++bad;
+            next = r.hi;
+        }
+        if (next != end) ++bad;
+    }
+    if (!ltk::tile_inside(2147483647LL - 256 - 512, 512, 2147483647LL - 256)) ++bad;
+    if (ltk::tile_inside(2147483647LL - 256 - 100, 512, 2147483647LL - 256)) ++bad;
+    printf("%lld\n", bad);
+    return bad != 0;
+}
+""")
+    exe = tmp_path / "split_check"
+    csrc = os.path.join(os.path.dirname(B.INCLUDE), "indexer_topk_long_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-I", csrc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "0", r.stdout

@@ -3,7 +3,7 @@ CPU oracle, and bit-exact agreement of the GPU paths with each other."""
 import numpy as np
 import pytest
 
-from tests.gpu_util import canon, check_rows, say, to_dev
+from tests.gpu_util import canon, check_rows, oracle_prev_chunk_sample, say, to_dev
 from workloads import selection_rows, indexer_inputs, indexer_workload, random_sample
 
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,21 @@ def _run_unfused(lib, d, topk):
 
 @pytest.fixture(scope="module")
 def tiny():
-    return indexer_workload("tiny-4k-fp32")
+    """The tiny workload as stated: 64 queries at positions 4032..4095, sampled
+    by the top-768 of the previous 64-query chunk (positions 3968..4031)."""
+    inp = indexer_workload("tiny-4k-fp32", with_prev=True)
+    inp["sample"] = oracle_prev_chunk_sample(inp)
+    return inp
+
+
+def test_tiny_previous_chunk_sample(tiny):
+    """The previous chunk's top-768 covers most of this chunk's top-256."""
+    from oracle import oracle_indexer
+    ref = oracle_indexer(tiny, with_scores=False)
+    assert len(tiny["sample"]) == 768 and len(np.unique(tiny["sample"])) == 768
+    hit = np.isin(ref, tiny["sample"]).mean()
+    say("tiny: previous-chunk sample holds", hit, "of the top-k")
+    assert hit > 0.8
 
 
 def test_device_is_gfx950(lib):
@@ -119,6 +133,8 @@ def test_sample_bins_refresh_capacity_independence(lib, dt):
         cases.append((f"splits{sp}", d["sample"], ltk.Opts(l_splits=sp)))
     for cap in (1, 64, 250):
         cases.append((f"ccap{cap}", d["sample"], ltk.Opts(cand_capacity=cap)))
+    cases.append(("flush32", d["sample"], ltk.Opts(flush_batch=32)))
+    cases.append(("flush32_ccap250_refresh3", d["sample"], ltk.Opts(flush_batch=32, cand_capacity=250, refresh_every=3)))
     cases.append(("nbins1_ccap1_empty", torch.zeros(0, dtype=torch.int32, device="cuda"),
                   ltk.Opts(nbins=1, cand_capacity=1, refresh_every=-1)))
     for name, smp, o in cases:
@@ -155,6 +171,12 @@ def test_forced_overflow_reports_stats(lib):
                                  k_scale=d["k_scale"], return_stats=True)
     assert st2.overflow_rows == 0 and 64 * 16 <= st2.cand_written and st2.max_cand_per_query >= 64
     assert np.array_equal(canon(idx.cpu().numpy()), canon(idx2.cpu().numpy()))
+    # bytes written: 8 per stored candidate, 4 per (query, distinct sample key), 4 per output index
+    smp = np.asarray(inp["sample"])
+    nu = len(np.unique(smp[(smp >= 0) & (smp < inp["L"])]))
+    assert st2.bytes_written == 8 * st2.cand_written + 4 * nu * 16 + 4 * 64 * 16
+    # an overflowed row stores only its capacity (8 entries)
+    assert st.bytes_written == 8 * 8 * 16 + 4 * nu * 16 + 4 * 64 * 16
 
 
 def test_edge_positions_and_small_k(lib):
@@ -198,14 +220,20 @@ def test_degenerate_sizes(lib):
 
 
 def test_sorted_output(lib):
+    """Sorted rows, (score desc, index asc), with and without the scores
+    returned, through the finalize and through the overflow fallback."""
     import indexer_topk_long_amd as ltk
     inp = indexer_inputs(10, 3000, 64, 128, "bf16", 150, 200, tag=61, n_sample=450)
     d = to_dev(inp)
-    idx, sc = _run_fused(lib, d, 150, opts=ltk.Opts(sorted_output=True))
-    for t in range(10):
-        keys = list(zip(-sc[t].astype(np.float64), idx[t]))
-        assert keys == sorted(keys)
-    check_rows(inp, idx, sc, range(10), "sorted")
+    for cap in (0, 1):
+        o = ltk.Opts(sorted_output=True, cand_capacity=cap)
+        idx, sc = _run_fused(lib, d, 150, opts=o)
+        for t in range(10):
+            keys = list(zip(-sc[t].astype(np.float64), idx[t]))
+            assert keys == sorted(keys)
+        check_rows(inp, idx, sc, range(10), "sorted")
+        only = lib.score_select(d["q"], d["k"], d["w"], d["pos"], 150, sample=d["sample"], opts=o).cpu().numpy()
+        assert np.array_equal(only, idx), f"sorted without scores, capacity {cap}"
 
 
 def test_determinism(lib, tiny):

@@ -173,6 +173,10 @@ def _rrs_transposed(m):
     m.retrieval_row_scores = retrieval_row_scores
 
 
+def _no_first_copy(m):
+    m.first_copy = lambda raw, scale=None: np.arange(raw.shape[0], dtype=np.int64)
+
+
 MUTANTS = {
     "dsa_mask_bits_reversed": (_dsa_bits_reversed, [P.check_dsa_hand_example, P.check_dsa_membership]),
     "dsa_list_descending": (_dsa_descending, [P.check_dsa_hand_example, P.check_dsa_membership]),
@@ -193,6 +197,7 @@ MUTANTS = {
                                                               P.check_retrieval_row_scores_self_match]),
     "retrieval_row_scores_transposed": (_rrs_transposed, [P.check_retrieval_row_scores_closed_form,
                                                           P.check_retrieval_row_scores_self_match]),
+    "identical_keys_scored_apart": (_no_first_copy, [P.check_first_copy_brute_force]),
 }
 
 
