@@ -510,6 +510,52 @@ def bench_dsa(args):
     print(json.dumps(line), flush=True)
 
 
+def measure_peaks(torch, mfma_iters: int = 200, read_bytes: int = 4 << 30) -> dict:
+    """Achievable rates of this GPU from the peak microbenchmarks
+    (indexer_topk_long_amd/peak/peak.hip): fp8 and bf16 32x32 MFMA loops at
+    two waves per SIMD on every CU, alone and with 8 fp32 FMAs issued behind
+    each MFMA (the fused scan's head-sum density), and a streaming HBM read.
+    Each figure is the best of three timed launches (device events)."""
+    import ctypes
+    from indexer_topk_long_amd.build import peak_lib_path
+    lib = ctypes.CDLL(peak_lib_path())
+    lib.ltkpeak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.ltkpeak_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks = 256 * 4
+    seed = torch.arange(64, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(blocks * 8, dtype=torch.float32, device="cuda")
+
+    def timed(fn):
+        best = None
+        for i in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = fn()
+            e1.record()
+            e1.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"peak microbenchmark failed ({rc})")
+            if i > 0:
+                best = e0.elapsed_time(e1) if best is None else min(best, e0.elapsed_time(e1))
+        return best
+
+    out = {}
+    for kind, name, fl in ((0, "fp8", 131072.0), (1, "bf16", 32768.0)):
+        for vpm in (0, 8):
+            ms = timed(lambda: lib.ltkpeak_mfma(kind, vpm, blocks, mfma_iters, ctypes.c_void_p(seed.data_ptr()),
+                                                ctypes.c_void_p(sink.data_ptr()), stream))
+            flops = blocks * 8 * mfma_iters * 8 * fl
+            out[f"{name}_mfma_tflops" + ("" if vpm == 0 else f"_with_{vpm}_valu")] = round(flops / (ms * 1e-3) / 1e12, 1)
+    buf = torch.empty(read_bytes, dtype=torch.uint8, device="cuda")
+    ms = timed(lambda: lib.ltkpeak_read(ctypes.c_void_p(buf.data_ptr()), read_bytes, 256 * 8,
+                                        ctypes.c_void_p(sink.data_ptr()), stream))
+    out["hbm_read_gbps"] = round(read_bytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    return out
+
+
 def _cores() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -532,6 +578,8 @@ def main():
                     help="retrieval workload only: one line over these k, sample from an earlier batch's results")
     ap.add_argument("--sweep-sample", default="random", choices=["random", "earlier"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--peak", action="store_true", help="print the achievable-peak microbenchmarks and exit")
+    ap.add_argument("--no-peak", action="store_true", help="skip the achievable-peak microbenchmarks")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -554,6 +602,10 @@ def main():
     import torch
     import indexer_topk_long_amd as ltk
     from workloads import WORKLOADS, indexer_workload
+
+    if args.peak:
+        print(json.dumps(measure_peaks(torch)), flush=True)
+        return
 
     cfg = WORKLOADS[args.workload]
     if args.prefill_chunks >= 0:
@@ -615,13 +667,15 @@ def main():
 
     _, st = step(return_stats=True)
     cands = st.cand_written / T
-    bytes_q = (8.0 * st.cand_written + 4.0 * T * k) / T
+    bytes_q = st.bytes_written / T   # candidates, sample scores and the index output
     full_q = 4.0 * L
 
     # unfused baseline (full fp32 score matrix + radix select), same inputs
     unf = None
     if args.unfused_steps > 0:
-        uws = torch.empty((T * L * 4), dtype=torch.uint8, device="cuda")
+        uws = torch.empty(ltk.workspace_bytes(ltk.KIND_UNFUSED, T, H, D, L, k, 0,
+                                              {"f32": 0, "bf16": 1, "fp8": 2}[inp["dtype"]]),
+                          dtype=torch.uint8, device="cuda")
         uout = ltk.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
                                         k_scale=d["k_scale"], workspace=uws)
         torch.cuda.synchronize()
@@ -642,6 +696,11 @@ def main():
     if not args.no_cpu_baseline:
         log("  timing the CPU oracle ...")
         cpu = cpu_baseline(inp, args.cpu_rows)
+    peaks = None
+    if not args.no_peak:
+        log("  achievable-peak microbenchmarks ...")
+        peaks = measure_peaks(torch)
+    mkey = {"fp8": "fp8_mfma_tflops", "bf16": "bf16_mfma_tflops"}.get(inp["dtype"])
 
     ctx = "1M" if L == 1 << 20 else f"{L // 1024}K"
     line = {
@@ -666,7 +725,14 @@ def main():
                      "traffic": (SCAN_TRAFFIC["bytes"] if scan_source_digest() == SCAN_TRAFFIC["digest"]
                                  and args.workload == SCAN_TRAFFIC["workload"] else None),
                      "kernel": "scan_kernel (fused score + filter)", "kernel_ms": round(scan_ms, 4),
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": flops,
+                     # the same kernel against this GPU's measured MFMA rates
+                     # (peak microbenchmarks: MFMA alone, and with the 8 fp32
+                     # FMAs per MFMA that the head sum needs)
+                     "measured_peak": peaks[mkey] if peaks and mkey else None,
+                     "frac_of_measured": round(achieved / peaks[mkey], 4) if peaks and mkey else None,
+                     "measured_peak_with_head_sum_valu": peaks.get(mkey + "_with_8_valu") if peaks and mkey else None},
+        "measured_peaks": peaks,
         "bytes_written_per_query": round(bytes_q, 1),
         "full_matrix_bytes_per_query": full_q,
         "candidates_per_query": round(cands, 1),

@@ -98,7 +98,8 @@ typedef struct {
 
 /* Bytes of workspace a call of `kind` needs.  For LTK_KIND_RETRIEVE, H is
  * ignored and L is the database size N; for LTK_KIND_UNFUSED, topk, n_sample
- * and opts are ignored (it holds the full T x L fp32 score matrix); for
+ * and opts are ignored (it holds the full T x L fp32 score matrix and, for
+ * fp8, 4 D + 4 bytes per query of linear-term operands); for
  * LTK_KIND_NEXT_SAMPLE only L counts (4 * L bytes of key counts and a fixed
  * 69,888 bytes more).  Returns 0 for invalid sizes. */
 size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, int64_t L,
@@ -154,7 +155,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
  * decoupled pipeline writes the full score matrix to device memory, then
  * radix-selects each row, reading the matrix several times).  Same
  * arguments and result as litetopk_score_select without the sample; the
- * workspace holds the T x L fp32 score matrix. */
+ * workspace holds the T x L fp32 score matrix (and, for fp8, the per-query
+ * linear-term operands that every fp8 pass shares). */
 int litetopk_unfused_score_select(const void* q, const float* q_scale, const void* k,
                                   const float* k_scale, const float* w, const int32_t* pos,
                                   int32_t T, int32_t H, int32_t D, int64_t L, int32_t dtype,

@@ -177,7 +177,7 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
                                 int32_t n_sample, int32_t dtype, const ltk_opts* opts) {
     if (kind == LTK_KIND_UNFUSED) {
         if (T < 0 || L < 1) return 0;
-        return align_up((size_t)T * (size_t)L * 4, 256);
+        return unfused_ws_bytes(T, L, dtype == LTK_FP8_E4M3FN ? D : 0);
     }
     if (kind == LTK_KIND_NEXT_SAMPLE) {
         if (L < 1 || L > (int64_t)0x7fffff00) return 0;
@@ -185,7 +185,7 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     }
     if (kind != LTK_KIND_SCORE_SELECT && kind != LTK_KIND_RETRIEVE) return 0;
     if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
-    (void)H; (void)D;
+    (void)H;
     Opts o;
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? retrieve_default_ccap(topk) : kDefaultCcap, o) != LTK_OK)
         return 0;
@@ -193,7 +193,8 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
         return ws_layout(T, L, sample_slots(n_sample, topk, L), o.ccap,
                          retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
-    return ws_layout(T, L, sample_slots(n_sample, topk, L), p.ccap, p.shared ? (size_t)T * o.nbins : 0).total;
+    return ws_layout(T, L, sample_slots(n_sample, topk, L), p.ccap, p.shared ? (size_t)T * o.nbins : 0,
+                     dtype == LTK_FP8_E4M3FN ? D : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -213,7 +214,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
     const IdxPlan plan = indexer_plan(T, L, dtype, o);
     const int32_t n_slots = sample_slots(n_sample, topk, L);
-    const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0);
+    const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0, fp8 ? D : 0);
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -252,6 +253,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
     a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
     a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+    a.qlin = fp8 ? wsb + lay.qlin : nullptr;
+    a.qinv = fp8 ? reinterpret_cast<float*>(wsb + lay.qinv) : nullptr;
     a.out_idx = out_idx;
     a.out_score = out_score;
     a.stats = stats;
@@ -276,7 +279,7 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
     const bool fp8 = dtype == LTK_FP8_E4M3FN;
     if (fp8 && ((T > 0 && !q_scale) || !k_scale)) return LTK_EINVAL;   // no queries: no query scales
     if (!fp8 && (q_scale || k_scale)) return LTK_EINVAL;
-    if (ws_bytes < (size_t)T * (size_t)L * 4) return LTK_EWORKSPACE;
+    if (ws_bytes < unfused_ws_bytes(T, L, fp8 ? D : 0)) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
     IdxArgs a{};
@@ -296,6 +299,11 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
     a.out_idx = out_idx;
     a.out_score = out_score;
     a.S = static_cast<float*>(ws);
+    if (fp8) {
+        uint8_t* wsb = static_cast<uint8_t*>(ws);
+        a.qlin = wsb + unfused_matrix_bytes(T, L);
+        a.qinv = reinterpret_cast<float*>(a.qlin + align_up(qlin_bytes(T, D), 256));
+    }
     if (launch_indexer_unfused(dtype, D, head_blocks(H), a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LTK_EHIP;
     return LTK_OK;

@@ -25,6 +25,7 @@ namespace ltk {
 enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -131,6 +132,54 @@ __device__ __forceinline__ float relu_wsum(const v16f (&acc)[HB], const float (&
 #pragma unroll
         for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[m][r], relu_bits(acc[m][r]), p);
     return p;
+}
+
+// fp8 form of the head sum.  With w' the head weights,
+//   sum_h w'_h max(0, x_h) = 1/2 sum_h w'_h x_h + 1/2 sum_h w'_h |x_h|
+// for weights of either sign.  The second sum is one FMA per head (|x| is a
+// free source modifier); the first is linear in the query, sum_h w'_h x_h =
+// q''.k with q'' = sum_h w'_h q_h, and goes to the matrix cores (lin_* below).
+// Here w holds w'/2, so this returns the lane's share of 1/2 sum w'|x|.
+template <int HB>
+__device__ __forceinline__ float abs_wsum(const v16f (&acc)[HB], const float (&w)[HB][16]) {
+    float p = 0.0f;
+#pragma unroll
+    for (int m = 0; m < HB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[m][r], __builtin_fabsf(acc[m][r]), p);
+    return p;
+}
+
+// The linear term on the matrix cores.  q''/2 of a query is held as four
+// fp8 parts P_0..P_3 with q''/2 * S ~= P_0 + P_1/16 + P_2/256 + P_3/4096
+// (S a power of two per query; each part carries the rounding residue of the
+// ones before, scaled up by 16, so the four parts hold about 16 significant
+// bits).  One v_mfma_f32_16x16x128_f8f6f4 scores 16 keys against 16 rows:
+// four queries x four parts, row 4g + p = part p of query g.  Lane l holds
+// row / key (l & 15), dimensions [32 (l >> 4), 32 (l >> 4) + 32) of both
+// operands, and gets rows 4 (l >> 4) .. 4 (l >> 4) + 3 of key (l & 15): the
+// four part products of one query and one key.
+struct LinFrag {
+    u32x4 v[2];   // 32 fp8 values of one row (or key) of the operand
+};
+
+__device__ __forceinline__ v4f lin_mfma(const LinFrag& a, const LinFrag& b) {
+    const i32x8 av = __builtin_bit_cast(i32x8, __builtin_shufflevector(a.v[0], a.v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    const i32x8 bv = __builtin_bit_cast(i32x8, __builtin_shufflevector(b.v[0], b.v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0, 0, 0, 0);
+}
+
+// (q''/2 . k) * S from the four part products, in one fixed order.
+__device__ __forceinline__ float lin_combine(const v4f& c) {
+    float t = __builtin_fmaf(c[3], 0.0625f, c[2]);
+    t = __builtin_fmaf(t, 0.0625f, c[1]);
+    return __builtin_fmaf(t, 0.0625f, c[0]);
+}
+
+// fp8 score of one key: sigma_k * (1/2 q''.k + 1/2 sum w'|x|), the linear
+// term t scaled back by 1/S.
+__device__ __forceinline__ float lin_score(float t, float inv_s, float abs_half, float sk) {
+    return __builtin_fmaf(t, inv_s, abs_half) * sk;
 }
 
 // Partial head sums of two slots -> lanes 0-31 get slot a's full sum for key

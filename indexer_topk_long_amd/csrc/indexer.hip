@@ -185,7 +185,7 @@ struct QueryRegs {
 };
 
 // Q rows (heads) of query t for this lane and the lane's head weights
-// w'[h] = sigma_q[t] * w[t, h] (zero for padded heads / queries).
+// w'[h] = sigma_q[t] * w[t, h], halved for fp8 (zero for padded heads / queries).
 template <int DT, int D, int HB>
 __device__ __forceinline__ void load_query(QueryRegs<DT, D, HB>& r, const IdxArgs& a, int t) {
     const int lane = lane_id(), half = lane >> 5, row = lane & 31;
@@ -218,7 +218,9 @@ __device__ __forceinline__ void load_query(QueryRegs<DT, D, HB>& r, const IdxArg
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int hh = head_of(m, i, half);
-            r.w[m][i] = (tv && hh < a.H) ? sq * wv[i] : 0.0f;
+            // fp8 scores sum w'/2 |x| (abs_wsum): the halving is exact
+            const float wh = (DT == DT_FP8) ? (sq * wv[i]) * 0.5f : sq * wv[i];
+            r.w[m][i] = (tv && hh < a.H) ? wh : 0.0f;
         }
     }
 }
@@ -235,6 +237,11 @@ __device__ __forceinline__ float score_2slots(const QueryRegs<DT, D, HB>& qa, co
                                               const QueryRegs<DT, D, HB>& qb, const HalfRow<DT, D>& kb) {
     v16f acca[HB], accb[HB];
     mfma_2slots<DT, D, HB>(qa.q, ka, qb.q, kb, acca, accb);
+    if constexpr (DT == DT_FP8) {   // 1/2 sum w'|x|; the caller adds the linear term
+        const float pa = abs_wsum<HB>(acca, qa.w);
+        const float pb = abs_wsum<HB>(accb, qb.w);
+        return combine_halves(pa, pb);
+    }
     const float pa = relu_wsum<HB>(acca, qa.w);
     const float pb = relu_wsum<HB>(accb, qb.w);
     return combine_halves(pa, pb);
@@ -246,6 +253,126 @@ __device__ __forceinline__ int group_key_end(const IdxArgs& a, int t0) {
     const int t = t0 + (lane & 7);
     int e = (t < a.T) ? min(a.pos[t], a.L - 1) + 1 : 0;
     return wave_max_i32(max(e, 0));
+}
+
+
+// ---------------------------------------------------------------------------
+// fp8 linear term: operands per query, and its products outside the scan
+// ---------------------------------------------------------------------------
+
+// One wave per query: q''/2 = sum_h (w'_h / 2) q_h over the query's heads in
+// head order (w' = sigma_q w as the head sum uses it), then four fp8 parts of
+// (q''/2) * S with S = 2^(8 - e) putting the largest magnitude in [128, 256),
+// each part taking the residue of the ones before it times 16.  Every fp8
+// pass reads these same bytes, so all of them get the same linear term.
+template <int D>
+__global__ __launch_bounds__(64) void qlin_kernel(IdxArgs a) {
+    constexpr int DPL = D / 64;   // dimensions per lane
+    const int t = blockIdx.x, lane = lane_id();
+    const float sq = a.q_scale[t];
+    const uint8_t* q = a.q + (size_t)t * a.H * D;
+    const float* w = a.w + (size_t)t * a.H;
+    float acc[DPL];
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+    for (int h = 0; h < a.H; ++h) {
+        const float c = (sq * w[h]) * 0.5f;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+            acc[i] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)q[(size_t)h * D + lane + 64 * i], 0), acc[i]);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) mx = fmaxf(mx, fabsf(acc[i]));
+    mx = wave_max_f32(mx);
+    int e = 0;
+    if (mx > 0.0f) frexpf(mx, &e);   // mx in [2^(e-1), 2^e)
+    e = max(-100, min(e, 100));      // keeps S and 1/S finite and normal
+    const float S = ldexpf(1.0f, 8 - e);
+    uint8_t* out = a.qlin + (size_t)t * 4 * D;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+        float r = acc[i] * S;   // exact: a power of two
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false) & 0xffu;
+            out[p * D + lane + 64 * i] = (uint8_t)code;
+            r = (r - __builtin_amdgcn_cvt_f32_fp8((int)code, 0)) * 16.0f;   // exact residue, scaled
+        }
+    }
+    if (lane == 0) a.qinv[t] = ldexpf(1.0f, e - 8);
+}
+
+// 32 fp8 values of row `row` (D bytes), dimensions [32 ks, 32 ks + 32); zero
+// past D (D = 64 uses half of the instruction's 128 dimensions).
+template <int D>
+__device__ __forceinline__ void load_lin_frag(LinFrag& f, const uint8_t* row, int ks) {
+    if (32 * ks < D) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + 32 * ks);
+        f.v[0] = p[0];
+        f.v[1] = p[1];
+    } else {
+        f.v[0] = f.v[1] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Linear-term operands of two queries ta (results in lanes 0-31) and tb
+// (lanes 32-63) against one 32-key block, in the lane layout of
+// score_2slots: two instructions, keys 0-15 with ta in rows 0-3 and tb in
+// rows 8-11, keys 16-31 with ta in rows 4-7 and tb in rows 12-15, so that
+// lane l finds its own (query, key) in one of the two results.  inv is 1/S
+// of the lane's query.
+struct LinPair {
+    LinFrag a0, a1;
+    float inv;
+};
+
+template <int D>
+__device__ __forceinline__ void load_lin_pair(LinPair& p, const IdxArgs& a, int ta, int tb) {
+    const int lane = lane_id(), r = lane & 15, ks = lane >> 4;
+    auto part = [&](LinFrag& f, int t, int pp) {
+        if (t < a.T) load_lin_frag<D>(f, a.qlin + ((size_t)t * 4 + pp) * D, ks);
+        else f.v[0] = f.v[1] = u32x4{0u, 0u, 0u, 0u};
+    };
+    const int g = r >> 2, pp = r & 3;   // row group and part of this lane's operand row
+    part(p.a0, g == 0 ? ta : g == 2 ? tb : a.T, pp);
+    part(p.a1, g == 1 ? ta : g == 3 ? tb : a.T, pp);
+    const int t = (lane < 32) ? ta : tb;
+    p.inv = (t < a.T) ? a.qinv[t] : 0.0f;
+}
+
+// (q''/2 . k) * S for the lane's query of the pair and key row kA (lanes
+// with (lane >> 4) even) or kB (odd): kA/kB hold the keys of columns
+// (lane & 15) and 16 + (lane & 15) of the block.
+template <int D>
+__device__ __forceinline__ float lin_pair_t(const LinPair& p, const uint8_t* k, int kA, int kB) {
+    const int ks = lane_id() >> 4;
+    LinFrag b0, b1;
+    load_lin_frag<D>(b0, k + (size_t)kA * D, ks);
+    load_lin_frag<D>(b1, k + (size_t)kB * D, ks);
+    const v4f c0 = lin_mfma(p.a0, b0), c1 = lin_mfma(p.a1, b1);
+    return lin_combine((ks & 1) ? c1 : c0);
+}
+
+// One query against 64 consecutive keys (lane l: key base + l): the query's
+// four parts in every row group, four instructions of 16 keys each.
+template <int D>
+__device__ __forceinline__ void load_lin_one(LinFrag& f, const IdxArgs& a, int t) {
+    const int lane = lane_id();
+    load_lin_frag<D>(f, a.qlin + ((size_t)t * 4 + (lane & 3)) * D, lane >> 4);
+}
+template <int D>
+__device__ __forceinline__ float lin_one64_t(const LinFrag& aq, const uint8_t* k, int base, int L) {
+    const int lane = lane_id(), ks = lane >> 4;
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        LinFrag b;
+        load_lin_frag<D>(b, k + (size_t)min(base + 16 * i + (lane & 15), L - 1) * D, ks);
+        const float ti = lin_combine(lin_mfma(aq, b));
+        t = (ks == i) ? ti : t;
+    }
+    return t;
 }
 
 // ---------------------------------------------------------------------------
@@ -267,6 +394,8 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
     load_query<DT, D, HB>(ra, a, ta);
     load_query<DT, D, HB>(rb, a, tb);
     const int t = half ? tb : ta;
+    LinPair lp;
+    if constexpr (DT == DT_FP8) load_lin_pair<D>(lp, a, ta, tb);
     if constexpr (HalfRow<DT, D>::NV > 4) {
         // wide fragments: no room for a second one
         for (int blk = b0; blk < b1; ++blk) {
@@ -292,6 +421,7 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
         const int j = blk * 32 + (lane & 31);
         const HalfRow<DT, D> cur = kf;
         const float cks = ks;
+        const int ckey = key;
         if (blk + 1 < b1) {
             key = key2;
             load_key<DT, D>(kf, a.k, key);
@@ -299,7 +429,11 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
             if (blk + 2 < b1) key2 = key_at(blk + 2);
         }
         float I = score_2slots<DT, D, HB>(ra, cur, rb, cur);
-        if constexpr (DT == DT_FP8) I = I * cks;
+        if constexpr (DT == DT_FP8) {
+            // the block's keys of columns (lane & 15) and 16 + (lane & 15)
+            const int kA = __shfl(ckey, lane & 15), kB = __shfl(ckey, 16 + (lane & 15));
+            I = lin_score(lin_pair_t<D>(lp, a.k, kA, kB), lp.inv, I, cks);
+        }
         if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
     }
 }
@@ -394,18 +528,28 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
 // ---------------------------------------------------------------------------
 //
 // One workgroup = 8 waves sharing K tiles that are streamed into LDS with
-// direct global->LDS loads (32 KB tiles in three stages, four at decode
-// shape: one scored while the others load), so the eight waves read each key
-// from device memory once.  Each wave owns one query (at decode shape two or
-// four waves share one) and scores it against 32-key slots.  Two waves per
-// SIMD let one wave's VALU epilogue overlap the other's MFMAs.
+// direct global->LDS loads (one tile scored while the next ones load), so
+// the eight waves read each key from device memory once.  Each wave owns one
+// query (at decode shape two or four waves share one) and scores it against
+// 32-key slots.  Two waves per SIMD let one wave's VALU epilogue overlap the
+// other's MFMAs.
+//
+// fp8 scores use the abs form of the head sum (abs_wsum) plus the linear
+// term q''/2 . k on the matrix cores.  Each wave loads whole 16-key blocks of
+// every tile; as soon as its own loads have landed it scores its blocks
+// against the linear-term parts of all the workgroup's queries (four queries
+// per v_mfma_f32_16x16x128_f8f6f4) and writes the results to an LDS row per
+// query; the tile's barrier then publishes them to the query owners.
 
 constexpr int kScanWaves = 8;
-constexpr int kTileBytes = 32768;      // key bytes per tile at decode shape (R > 1) and for narrow rows
-constexpr int kTileBytesWide = 65536;  // one wave per query, rows of 128 bytes or more
-constexpr int kScanStagesWide = 2;     // 64 KB tiles: one scored while the next loads
-constexpr int kScanStages = 3;         // 32 KB tiles, one wave per query: one scored, two loading
-constexpr int kScanStagesFew = 4;      // at decode shape (R > 1), where the key stream bounds the scan
+constexpr int kTileBytes = 32768;          // key bytes per tile at decode shape (R > 1) and for narrow rows
+constexpr int kTileBytesWide = 65536;      // one wave per query, rows of 128 bytes or more
+constexpr int kTileBytesWideFp8 = 49152;   // fp8: 384 keys, so that two stages and the linear-term rows fit
+constexpr int kScanStagesWide = 2;         // wide tiles: one scored while the next loads
+constexpr int kScanStages = 3;             // 32 KB tiles, one wave per query: one scored, two loading
+constexpr int kScanStagesFew = 4;          // at decode shape (R > 1), where the key stream bounds the scan
+constexpr int kLinPad = 16;                // floats of padding per linear-term row (spreads LDS banks)
+constexpr int kSlotValuPerMfma = 8;        // fp8 prefill slots: head-sum VALU instructions issued behind each MFMA
 
 template <int DT, int D, int TB = kTileBytes>
 struct TileGeom {
@@ -421,22 +565,38 @@ struct TileGeom {
     static_assert(TK % 64 == 0, "per-key scales load in whole 64-lane wave loads");
     static constexpr int SCALE_INST = (DT == DT_FP8) ? TK / 64 : 0;       // wave loads of scales per tile
     static_assert(SCALE_INST <= kScanWaves, "at most one scale load per wave");
+    // fp8 linear term: each wave loads (and then scores) whole 16-key blocks
+    static constexpr bool LIN = DT == DT_FP8;
+    static constexpr int IPB = (16 * RB >= 1024) ? 16 * RB / 1024 : 1;    // 1 KB loads per 16-key block
+    static constexpr int LBW = TK / (16 * kScanWaves);                    // 16-key blocks per wave and tile
+    static constexpr int LROW = TK + kLinPad;                              // floats per linear-term row
+    static_assert(!LIN || (16 * RB >= 1024 && PER_WAVE % IPB == 0 && TK % (16 * kScanWaves) == 0),
+                  "fp8 tiles split into whole 16-key blocks per wave");
 };
 
-// Tile size and stages of a scan with R waves per query.  At one wave per
-// query (prefill shape) the MFMA/VALU work bounds the scan, and each tile
-// ends in a workgroup barrier that drains the wave's software pipeline:
-// 64 KB tiles halve those (measured 1.5 % faster than 32 KB tiles with three
-// stages).  WIDE needs rows of at least 128 bytes (at most 512 keys, whose
-// scales take one wave load each) and the LDS for two such stages, which the
-// launch checks against the bin count.  Decode shapes keep 32 KB tiles and
-// four stages in flight.
+// Tile size of a scan with R waves per query.  At one wave per query
+// (prefill shape) the MFMA/VALU work bounds the scan, and each tile ends in a
+// workgroup barrier that drains the wave's software pipeline, so the tiles
+// are as large as two stages allow (64 KB, measured 1.5 % faster than 32 KB
+// tiles with three stages; 48 KB for fp8, whose linear-term rows take LDS
+// too).  WIDE needs rows of at least 128 bytes (at most 512 keys, whose
+// scales take one wave load each) and LDS for two such stages, which the
+// launch checks against the bin count.  Decode shapes keep 32 KB tiles.
 template <int DT, int D, int R, bool WIDE>
 struct ScanShape {
     static_assert(!WIDE || (R == 1 && D * DTraits<DT>::ESZ >= 128), "wide tiles: one wave per query, rows >= 128 B");
-    static constexpr int TB = WIDE ? kTileBytesWide : kTileBytes;
-    static constexpr int NST = (R > 1) ? kScanStagesFew : (WIDE ? kScanStagesWide : kScanStages);
+    static constexpr int TB = WIDE ? (DT == DT_FP8 ? kTileBytesWideFp8 : kTileBytesWide) : kTileBytes;
 };
+
+// Index of the wave's j-th 1 KB load of a tile.  fp8: wave w loads the rows
+// of the 16-key blocks w, w + 8, w + 16, ... (IPB consecutive loads each), so
+// that it can score them once its own loads have landed; otherwise the loads
+// of the waves interleave.
+template <class G>
+__device__ __forceinline__ int load_inst(int wave, int j) {
+    if constexpr (G::LIN) return G::IPB * (kScanWaves * (j / G::IPB) + wave) + j % G::IPB;
+    else return wave + j * kScanWaves;
+}
 
 // Per-lane byte offsets, inside a tile, of the wave's share of the tile's
 // direct loads (fixed for the whole kernel: row r of the tile, swizzled chunk).
@@ -450,7 +610,7 @@ __device__ __forceinline__ void tile_offsets(TileOffsets<DT, D, TB>& o, int wave
     using G = TileGeom<DT, D, TB>;
 #pragma unroll
     for (int j = 0; j < G::PER_WAVE; ++j) {
-        const int p = (wave + j * kScanWaves) * 64 + lane;
+        const int p = load_inst<G>(wave, j) * 64 + lane;
         const int r = p / G::CPR, pc = p % G::CPR;
         o.key[j] = (uint32_t)(r * G::RB + (pc ^ chunk_swz<G::RB, G::CPR>(r)) * 16);
     }
@@ -470,7 +630,7 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT
         const uint8_t* tb = a.k + (size_t)key0 * G::RB;
 #pragma unroll
         for (int j = 0; j < G::PER_WAVE; ++j) {
-            uint8_t* dst = st + (wave + j * kScanWaves) * 1024;
+            uint8_t* dst = st + load_inst<G>(wave, j) * 1024;
             if constexpr (ASYNC) lds_direct16_async(tb, to.key[j], dst);
             else lds_direct16(tb + to.key[j], dst);
         }
@@ -486,7 +646,7 @@ __device__ __forceinline__ void load_tile(const IdxArgs& a, const TileOffsets<DT
     }
 #pragma unroll
     for (int j = 0; j < G::PER_WAVE; ++j) {
-        const int inst = wave + j * kScanWaves;
+        const int inst = load_inst<G>(wave, j);
         const int p = inst * 64 + lane;
         const int r = p / G::CPR, pc = p % G::CPR;
         const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
@@ -515,24 +675,81 @@ __device__ __forceinline__ void read_frag(HalfRow<DT, D>& f, const uint8_t* st, 
     }
 }
 
+// Linear-term operands of the workgroup's queries in LDS: NG groups of four
+// queries x four parts, 16 rows of 128 bytes each (zero past D and for
+// missing queries), rows 144 bytes apart: the 16 rows a fragment read touches
+// then fall on distinct banks (a 128-byte stride put eight of them on one).
+constexpr int kLinRowBytes = 144;
+constexpr int kLinGroupBytes = 16 * kLinRowBytes;
+
+// The linear term of the wave's own 16-key blocks of a tile (rows it loaded
+// itself, so only its own loads need to have landed) for every query of the
+// workgroup, into the LDS rows lb[query][key in tile].
+template <int DT, int D, int TB, int QPG>
+__device__ __forceinline__ void lin_phase(const uint8_t* st, const uint8_t* apart, float* lb, int wave, int lane) {
+    using G = TileGeom<DT, D, TB>;
+    constexpr int NG = (QPG + 3) / 4;
+    const int r = lane & 15, ks = lane >> 4;
+    LinFrag af[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(apart + g * kLinGroupBytes + r * kLinRowBytes + ks * 32);
+        af[g].v[0] = p[0];
+        af[g].v[1] = p[1];
+    }
+#pragma unroll
+    for (int b = 0; b < G::LBW; ++b) {
+        const int row = 16 * (wave + kScanWaves * b) + r;
+        LinFrag bf;
+        if (32 * ks < D) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int c = 2 * ks + i;
+                bf.v[i] = *reinterpret_cast<const u32x4*>(st + row * G::RB + ((c ^ chunk_swz<G::RB, G::CPR>(row)) * 16));
+            }
+        } else {
+            bf.v[0] = bf.v[1] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float tl = lin_combine(lin_mfma(af[g], bf));
+            const int q = 4 * g + ks;
+            if (q < QPG) lb[q * G::LROW + row] = tl;
+        }
+    }
+}
+
+// LDS the fused scan needs beyond its tile stages: per-wave histograms and
+// staging lists, and for fp8 the linear-term operands and two buffers of
+// linear-term rows.
+template <int DT, int D, int TB, int QPG>
+constexpr size_t scan_extra_lds(int nbins) {
+    using G = TileGeom<DT, D, TB>;
+    const size_t fixed = (size_t)kScanWaves * nbins * 4 + (size_t)kScanWaves * kStage * 8;
+    if constexpr (!G::LIN) return fixed;
+    return fixed + (size_t)((QPG + 3) / 4) * kLinGroupBytes + (size_t)2 * QPG * G::LROW * 4;
+}
+
 // R waves per query: a workgroup holds kScanWaves / R queries, and the R
 // waves of a query take every R-th 64-key block of each tile.  R = 1 at
 // prefill shape; a decode step of one to four queries uses R = 4 or 2, so
 // that the waves score real queries instead of empty slots.
-template <int DT, int D, int HB, int R, bool WIDE>
+template <int DT, int D, int HB, int R, bool WIDE, int NST>
 __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     using SS = ScanShape<DT, D, R, WIDE>;
     using G = TileGeom<DT, D, SS::TB>;
-    constexpr int NST = SS::NST;                                           // tile stages
     constexpr bool ASYNC = true;   // loads as inline assembly from a uniform base (no per-load VALU)
     constexpr int QPG = kScanWaves / R;
     constexpr int NB = G::TK / 64;                                         // 64-key blocks per tile
+    constexpr int NG = (QPG + 3) / 4;                                      // linear-term query groups
     static_assert(R >= 1 && NB % R == 0, "a tile's blocks split evenly over a query's waves");
     extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
     const int nbins = a.nbins;
     uint8_t* tiles = shm;                                                  // NST stages
     uint32_t* hist = reinterpret_cast<uint32_t*>(shm + NST * G::STAGE_BYTES);  // [waves][nbins]
     uint2* stage = reinterpret_cast<uint2*>(hist + kScanWaves * nbins);    // [waves][kStage]
+    uint8_t* apart = reinterpret_cast<uint8_t*>(stage + kScanWaves * kStage);      // fp8: [NG][16][128]
+    float* lbuf = reinterpret_cast<float*>(apart + NG * kLinGroupBytes);            // fp8: [2][QPG][LROW]
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int t0 = qg * QPG;
@@ -566,7 +783,21 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
 
     QueryRegs<DT, D, HB> ra;
     load_query<DT, D, HB>(ra, a, t);
+    float inv_own = 0.0f;   // fp8: 1/S of the query's linear-term parts
+    if constexpr (G::LIN) {
+        // the workgroup's linear-term operands into LDS, 16 bytes per thread
+        for (int i = threadIdx.x; i < NG * 16 * 8; i += kScanWaves * 64) {
+            const int g = i / 128, r = (i / 8) % 16, c = i % 8;
+            const int ql = 4 * g + (r >> 2), tq = t0 + ql;
+            u32x4 v{0u, 0u, 0u, 0u};
+            if (ql < QPG && tq < a.T && 16 * c < D)
+                v = *reinterpret_cast<const u32x4*>(a.qlin + ((size_t)tq * 4 + (r & 3)) * D + 16 * c);
+            *reinterpret_cast<u32x4*>(apart + g * kLinGroupBytes + r * kLinRowBytes + 16 * c) = v;
+        }
+        if (tv) inv_own = a.qinv[t];
+    }
     if constexpr (ASYNC) drain_vm_loads();   // the loop's waits then cover tile loads only
+    if constexpr (G::LIN) __syncthreads();   // operands in LDS before the first linear-term phase
 
     int cnt = 0;   // staged entries (wave-uniform)
     int fl = 0;    // batches written back
@@ -614,13 +845,18 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         }
     };
 
-    auto process = [&](float I, int key) {
-        const bool pass = (key <= my_pos) && (I >= tau);
-        const uint64_t mask = __ballot(pass);
+    // Gate of 64 consecutive keys, lane l holding key base + l.  The causal
+    // bound is a scalar lane mask (keys past the query's position), so the
+    // common case costs one compare and a scalar AND.
+    const int pos_u = __builtin_amdgcn_readfirstlane(my_pos);
+    auto process = [&](float I, int base) {
+        const int lim = pos_u - base;   // lanes 0..lim are causal
+        const uint64_t causal = lim >= 63 ? ~0ull : (lim < 0 ? 0ull : ((2ull << lim) - 1ull));
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(I >= tau) & causal;
         if (mask) {
-            if (pass) {
+            if ((mask >> lane) & 1ull) {
                 atomicAdd(&hl[bin_of(I, m.smin, m.delta, nbins)], 1u);
-                stg[cnt + mbcnt(mask)] = make_uint2((uint32_t)key, __float_as_uint(I));
+                stg[cnt + mbcnt(mask)] = make_uint2((uint32_t)(base + lane), __float_as_uint(I));
             }
             cnt += __popcll(mask);
             while (cnt >= fb) flush();   // twice at most, with batches of 32
@@ -645,15 +881,18 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         } else {
             if (NST == 4 && later >= 2) wait_vm<2 * LPW_LO>(); else if (later >= 1) wait_vm<LPW_LO>(); else wait_vm<0>();
         }
+        const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
+        float* lrow = lbuf + (size_t)(it & 1) * QPG * G::LROW;   // this tile's linear-term rows
+        if constexpr (G::LIN) lin_phase<DT, D, SS::TB, QPG>(st, apart, lrow, wave, lane);
         __syncthreads();
         if (it + NST - 1 < ntiles) {   // into the stage every wave finished scoring before the barrier
             const int nb = (sbuf + NST - 1) % NST;
             load_tile<DT, D, SS::TB, ASYNC>(a, toff, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
         }
         const int key0 = k_lo + it * G::TK;
-        const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
         sbuf = (sbuf + 1) % NST;
         const float* sks = reinterpret_cast<const float*>(st + SS::TB);
+        const float* lq = lrow + (wave / R) * G::LROW;                  // the wave's query's linear terms
         if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
         if constexpr (DT == DT_F32) {
             // fp32: a whole fragment is 16 registers per 16 dimensions and
@@ -685,7 +924,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                                 acc[mm], 0, 0, 0);
                 }
                 const float p = relu_wsum<HB>(acc, ra.w);
-                if (sl & 1) process(combine_halves(pprev, p), key0 + r0 - 32 + lane);
+                if (sl & 1) process(combine_halves(pprev, p), key0 + r0 - 32);
                 else pprev = p;
             }
         } else if constexpr (HalfRow<DT, D>::NV > 4) {
@@ -711,9 +950,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 const float p = relu_wsum<HB>(accC, ra.w);
                 if (sl & 1) {
                     const int r0 = row0(sl - 1);
-                    float I = combine_halves(pprev, p);
-                    if constexpr (DT == DT_FP8) I = I * sks[r0 + lane];
-                    process(I, key0 + r0 + lane);
+                    process(combine_halves(pprev, p), key0 + r0);
                 } else {
                     pprev = p;
                 }
@@ -722,14 +959,98 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                     for (int mm = 0; mm < HB; ++mm) accC[mm] = accN[mm];
                 }
             }
+        } else if constexpr (DT == DT_FP8 && R == 1) {
+            // fp8 at prefill shape: the pipeline below, with each pair's gate
+            // deferred into the next slot, just behind that slot's first
+            // MFMA.  The gate's dependent chain (half exchange, linear term,
+            // key scale, compare, ballot, branch) then runs while the matrix
+            // core works, instead of leaving it idle at the end of every
+            // other slot (which a wave running alone, after its SIMD
+            // partner reached the tile's barrier, otherwise exposes).  A
+            // gate one slot later sees a threshold at most one refresh
+            // staler: still safe.
+            constexpr int NS = G::TK / 32;
+            constexpr int KS = HalfRow<DT, D>::KSTEPS;
+            constexpr int VPM = kSlotValuPerMfma;
+            auto row0 = [&](int j) { return 64 * (j >> 1) + 32 * (j & 1); };
+            HalfRow<DT, D> kf[2];
+            v16f accC[HB], accN[HB];
+            read_frag<DT, D>(kf[0], st, row0(0), lane);
+            mfma_1slot<DT, D, HB>(ra.q, kf[0], accC);
+            if (NS > 1) read_frag<DT, D>(kf[1], st, row0(1), lane);
+            float pprev = 0.0f;
+            float ga = 0.0f, gb = 0.0f, glin = 0.0f, gsk = 0.0f;   // the pair waiting for its gate
+            int gr0 = 0;
+            bool gpend = false;
+#pragma unroll
+            for (int sl = 0; sl < NS; ++sl) {
+                const HalfRow<DT, D>& kn = kf[(sl + 1) & 1];
+                if (sl + 1 < NS) {
+                    accN[0] = v16f{};
+                    mfma_step<DT, D>(ra.q[0], kn, 0, accN[0]);
+                }
+                if (gpend) {
+                    // the gate's chain starts here, not at the end of the
+                    // previous slot: a region boundary behind the MFMA, and an
+                    // empty asm that the chain's inputs pass through
+                    __builtin_amdgcn_sched_barrier(0);
+                    asm volatile("" : "+v"(ga), "+v"(gb), "+v"(glin), "+v"(gsk));
+                    process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), key0 + gr0);
+                    gpend = false;
+                }
+                if (sl & 1) {   // this pair's linear terms and key scales, read early
+                    gr0 = row0(sl - 1);
+                    glin = lq[gr0 + lane];
+                    gsk = sks[gr0 + lane];
+                }
+                if (sl + 1 < NS) {
+#pragma unroll
+                    for (int mm = 1; mm < HB; ++mm) {
+                        accN[mm] = v16f{};
+                        mfma_step<DT, D>(ra.q[mm], kn, 0, accN[mm]);
+                    }
+#pragma unroll
+                    for (int j = 1; j < KS; ++j)
+#pragma unroll
+                        for (int mm = 0; mm < HB; ++mm) mfma_step<DT, D>(ra.q[mm], kn, j, accN[mm]);
+                    if (sl + 2 < NS) read_frag<DT, D>(kf[sl & 1], st, row0(sl + 2), lane);
+                }
+                const float p = abs_wsum<HB>(accC, ra.w);
+                if (sl + 1 < NS) {
+                    // issue order after the gate: the fragment reads two slots
+                    // ahead, then VPM head-sum VALU instructions behind each of
+                    // the slot's remaining MFMAs
+                    if (sl & 1 || sl == 0) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // first MFMA
+                    if (sl + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, HalfRow<DT, D>::NV, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+#pragma unroll
+                    for (int g = 1; g < HB * KS; ++g) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+                    }
+                }
+                if (sl & 1) {
+                    ga = pprev;
+                    gb = p;
+                    gpend = true;
+                } else {
+                    pprev = p;
+                }
+                if (sl + 1 < NS) {
+#pragma unroll
+                    for (int mm = 0; mm < HB; ++mm) accC[mm] = accN[mm];
+                }
+                __builtin_amdgcn_sched_barrier(0);   // each slot its own scheduling region
+            }
+            if (gpend) process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), key0 + gr0);
         } else {
             // 32-key slots, software-pipelined: the MFMAs of slot s+1 are issued
-            // before the ReLU*w reduction of slot s, so the matrix core and the
-            // VALU of one wave overlap; two slots make one 64-key block.  The
-            // wave's slot j is half (j & 1) of block sub + R * (j / 2).  Key
-            // fragments are double-buffered: slot s+2's LDS reads go out after
-            // slot s+1's MFMAs and land during slot s's reduction (0.5 %
-            // faster than reading each fragment just before its MFMAs).
+            // before the head sum of slot s, so the matrix core and the VALU of
+            // one wave overlap; two slots make one 64-key block.  The wave's
+            // slot j is half (j & 1) of block sub + R * (j / 2).  Key fragments
+            // are double-buffered: slot s+2's LDS reads go out after slot s+1's
+            // MFMAs and land during slot s's reduction (0.5 % faster than
+            // reading each fragment just before its MFMAs).
             constexpr int NS = G::TK / 32 / R;
             auto row0 = [&](int j) { return 64 * (sub + R * (j >> 1)) + 32 * (j & 1); };
             HalfRow<DT, D> kf[2];
@@ -744,32 +1065,33 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                     mfma_1slot<DT, D, HB>(ra.q, kf[(sl + 1) & 1], accN);
                     if (sl + 2 < NS) read_frag<DT, D>(kf[sl & 1], st, row0(sl + 2), lane);
                 }
-                const float p = relu_wsum<HB>(accC, ra.w);
+                float p;
+                if constexpr (DT == DT_FP8) p = abs_wsum<HB>(accC, ra.w);
+                else p = relu_wsum<HB>(accC, ra.w);
                 if constexpr (DT == DT_FP8 && R == 1) {
                     // issue order of the slot: its first MFMA, the LDS reads
-                    // of the fragment two slots ahead, then 14 VALU
-                    // instructions of the head sum behind each MFMA.  Left to
-                    // itself the scheduler sinks half of those reads to just
-                    // before their MFMA, which then waits on LDS (0.8-1 %
-                    // slower at 1M context; 12 and 16 per MFMA measured about
-                    // the same as 14, 8 and 10 slower; no gain at decode shape)
+                    // of the fragment two slots ahead, then the head sum's VALU
+                    // instructions spread behind the MFMAs.  Left to itself the
+                    // scheduler sinks half of those reads to just before their
+                    // MFMA, which then waits on LDS
                     if (sl + 1 < NS) {
                         constexpr int NM = HB * HalfRow<DT, D>::KSTEPS;
+                        constexpr int VPM = kSlotValuPerMfma;
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
                         if (sl + 2 < NS) __builtin_amdgcn_sched_group_barrier(0x100, HalfRow<DT, D>::NV, 0);   // LDS reads
-                        __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // VALU
 #pragma unroll
                         for (int g = 1; g < NM; ++g) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
                         }
                     }
                 }
                 if (sl & 1) {
                     const int r0 = row0(sl - 1);
                     float I = combine_halves(pprev, p);
-                    if constexpr (DT == DT_FP8) I = I * sks[r0 + lane];
-                    process(I, key0 + r0 + lane);
+                    if constexpr (DT == DT_FP8) I = lin_score(lq[r0 + lane], inv_own, I, sks[r0 + lane]);
+                    process(I, key0 + r0);
                 } else {
                     pprev = p;
                 }
@@ -777,6 +1099,10 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
 #pragma unroll
                     for (int mm = 0; mm < HB; ++mm) accC[mm] = accN[mm];
                 }
+                // each slot is its own scheduling region: otherwise the head sum
+                // of slot s+1 (no branch separates an even slot from the next)
+                // is hoisted right behind its own MFMAs and waits for them
+                if constexpr (DT == DT_FP8 && R == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -1005,6 +1331,8 @@ __global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
 template <int DT, int D, int HB>
 struct RescoreSource {
     QueryRegs<DT, D, HB> r;
+    LinFrag lq;   // fp8: the query's linear-term parts in every row group
+    float inv;
     const uint8_t* k;
     const float* ks;
     int L;
@@ -1016,7 +1344,7 @@ struct RescoreSource {
         load_key<DT, D>(kbf, k, min(kb0 + 32 + (lane & 31), L - 1));
         I = score_2slots<DT, D, HB>(r, ka, r, kbf);
         key = kb0 + lane;
-        if constexpr (DT == DT_FP8) I = I * ks[min(key, L - 1)];
+        if constexpr (DT == DT_FP8) I = lin_score(lin_one64_t<D>(lq, k, kb0, L), inv, I, ks[min(key, L - 1)]);
         valid = key < nvalid;
     }
 };
@@ -1035,6 +1363,10 @@ __global__ __launch_bounds__(256) void select_kernel(IdxArgs a) {
     const int t = blockIdx.x;
     RescoreSource<DT, D, HB> src;
     load_query<DT, D, HB>(src.r, a, t);
+    if constexpr (DT == DT_FP8) {
+        load_lin_one<D>(src.lq, a, t);
+        src.inv = a.qinv[t];
+    }
     src.k = a.k;
     src.ks = a.k_scale;
     src.L = a.L;
@@ -1060,13 +1392,17 @@ __global__ __launch_bounds__(256) void unfused_score_kernel(IdxArgs a) {
     QueryRegs<DT, D, HB> ra, rb;
     load_query<DT, D, HB>(ra, a, ta);
     load_query<DT, D, HB>(rb, a, tb);
+    LinPair lp;
+    if constexpr (DT == DT_FP8) load_lin_pair<D>(lp, a, ta, tb);
     const int my_pos = (t < a.T) ? a.pos[t] : -1;
     for (int kb = k_lo; kb < k_hi; kb += 32) {
         const int key = kb + (lane & 31);
         HalfRow<DT, D> kf;
         load_key<DT, D>(kf, a.k, min(key, a.L - 1));
         float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-        if constexpr (DT == DT_FP8) I = I * a.k_scale[min(key, a.L - 1)];
+        if constexpr (DT == DT_FP8)
+            I = lin_score(lin_pair_t<D>(lp, a.k, min(kb + (lane & 15), a.L - 1), min(kb + 16 + (lane & 15), a.L - 1)),
+                          lp.inv, I, a.k_scale[min(key, a.L - 1)]);
         if (t < a.T && key < k_hi) a.S[(size_t)t * a.L + key] = (key <= my_pos) ? I : -INFINITY;
     }
 }
@@ -1308,38 +1644,58 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
+        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
-        const size_t scan_fixed = (size_t)kScanWaves * a.nbins * 4 + (size_t)kScanWaves * kStage * 8;
         constexpr int NB = TileGeom<DT_, D_>::TK / 64;
-        auto launch_scan = [&](auto Rc, auto Wc) {
-            constexpr int R_ = decltype(Rc)::value;
+        // LDS of a scan variant: R waves per query, wide tiles, NST stages
+        auto scan_lds = [&](auto Rc, auto Wc, auto Nc) -> size_t {
+            constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
+            constexpr bool W_ = decltype(Wc)::value;
+            using SS = ScanShape<DT_, D_, R_, W_>;
+            return (size_t)N_ * TileGeom<DT_, D_, SS::TB>::STAGE_BYTES +
+                   scan_extra_lds<DT_, D_, SS::TB, kScanWaves / R_>(a.nbins);
+        };
+        auto launch_scan = [&](auto Rc, auto Wc, auto Nc) {
+            constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
             constexpr bool W_ = decltype(Wc)::value;
             constexpr int QPG = kScanWaves / R_;
-            using SS = ScanShape<DT_, D_, R_, W_>;
-            const size_t scan_lds = SS::NST * (size_t)TileGeom<DT_, D_, SS::TB>::STAGE_BYTES + scan_fixed;
-            allow_lds(scan_kernel<DT_, D_, HB_, R_, W_>, scan_lds);
+            const size_t lds = scan_lds(Rc, Wc, Nc);
+            allow_lds(scan_kernel<DT_, D_, HB_, R_, W_, N_>, lds);
             if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-            scan_kernel<DT_, D_, HB_, R_, W_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, scan_lds, st>>>(a);
+            scan_kernel<DT_, D_, HB_, R_, W_, N_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, lds, st>>>(a);
             if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
         };
-        // the decode-shape variants need room for four tile stages
-        const bool few_fits = kScanStagesFew * (size_t)TileGeom<DT_, D_>::STAGE_BYTES + scan_fixed <= kMaxLds;
-        const int R = few_fits ? scan_waves_per_query(a.T, NB) : 1;
+        // decode shapes (R > 1) need room for four tile stages, else one wave per query
+        const int Rw = scan_waves_per_query(a.T, NB);
         bool launched = false;
         if constexpr (NB % 4 == 0) {
-            if (R == 4) { launch_scan(ic<4>{}, std::false_type{}); launched = true; }
+            if (!launched && Rw == 4 && scan_lds(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
+                launch_scan(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{});
+                launched = true;
+            }
         }
         if constexpr (NB % 2 == 0) {
-            if (R == 2) { launch_scan(ic<2>{}, std::false_type{}); launched = true; }
+            if (!launched && Rw == 2 && scan_lds(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
+                launch_scan(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{});
+                launched = true;
+            }
         }
         // (fp32 at D = 128 keeps 32 KB tiles: its wide variant spills registers)
         if constexpr (TileGeom<DT_, D_>::RB >= 128 && !(DT_ == DT_F32 && D_ >= 128)) {
-            constexpr size_t wide_stages =
-                kScanStagesWide * (size_t)TileGeom<DT_, D_, kTileBytesWide>::STAGE_BYTES;
-            if (R == 1 && wide_stages + scan_fixed <= kMaxLds) { launch_scan(ic<1>{}, std::true_type{}); launched = true; }
+            if (!launched && scan_lds(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{}) <= kMaxLds) {
+                launch_scan(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{});
+                launched = true;
+            }
         }
-        if (R == 1 && !launched) { launch_scan(ic<1>{}, std::false_type{}); launched = true; }
+        if (!launched && scan_lds(ic<1>{}, std::false_type{}, ic<kScanStages>{}) <= kMaxLds) {
+            launch_scan(ic<1>{}, std::false_type{}, ic<kScanStages>{});
+            launched = true;
+        }
+        if (!launched && scan_lds(ic<1>{}, std::false_type{}, ic<2>{}) <= kMaxLds) {
+            launch_scan(ic<1>{}, std::false_type{}, ic<2>{});
+            launched = true;
+        }
         if (!launched) { err = hipErrorInvalidValue; return; }
         const size_t sel_lds = std::max(fin_lds_bytes(a), row_select_lds(a.topk, a.sorted, a.out_score != nullptr));
         allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
@@ -1366,6 +1722,7 @@ hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipSt
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
+        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
         unfused_score_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, 0, st>>>(a);
         const size_t lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
         allow_lds(unfused_select_kernel, lds);

@@ -49,8 +49,12 @@ inline int sample_chunks(int64_t L) {
 // by the first kernel of every call.
 struct WsLayout {
     size_t tail, flags, hist, bitmap, ccount, zero_begin, zero_end;
-    size_t nu, meta, sample_u, sscore, cand, total;
+    size_t nu, meta, sample_u, sscore, qlin, qinv, cand, total;
 };
+
+// Per-query linear-term operands of the fp8 score (four fp8 parts of D bytes
+// and one fp32 scale per query; lin_d = D for fp8 inputs, else 0).
+inline size_t qlin_bytes(int32_t T, int lin_d) { return (size_t)T * 4 * (size_t)lin_d; }
 
 // Samples of at most this many entries are de-duplicated in one workgroup's
 // LDS hash table, with no key bitmap (the bitmap and its chunk counts, the
@@ -71,7 +75,8 @@ inline int32_t sample_slots(int32_t n_sample, int32_t topk, int64_t L) {
 // hist_words: 32-bit counters of the histograms shared across workgroups
 // (retrieval: T x (nbins + super-bins) + T x splits; indexer: T x nbins when
 // its splits share thresholds, else 0).
-inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0) {
+inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0,
+                          int lin_d = 0) {
     WsLayout w{};
     size_t o = 0;
     // cleared by the sample preparation of every call
@@ -89,6 +94,8 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, 
     w.meta = o;     o = align_up(o + (size_t)T * sizeof(int32_t) * 4, 256);
     w.sample_u = o; o = align_up(o + (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
     w.sscore = o;   o = align_up(o + (size_t)T * (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
+    w.qlin = o;     o = align_up(o + qlin_bytes(T, lin_d), 256);
+    w.qinv = o;     o = align_up(o + (lin_d ? (size_t)T * 4 : 0), 256);
     w.cand = o;     o = align_up(o + (size_t)T * (size_t)ccap * 8, 256);
     w.total = o;
     return w;
@@ -120,6 +127,8 @@ struct IdxArgs {
     int32_t* sample_u;
     float* sscore;
     uint2* cand;
+    uint8_t* qlin;           // fp8: [T][4][D] parts of each query's q''/2 (linear term), else null
+    float* qinv;             // fp8: [T] 1/S of those parts
     // outputs
     int32_t* out_idx;
     float* out_score;
@@ -158,6 +167,11 @@ hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_
                                  uint8_t* ws, hipStream_t st);   // n_sample == 0: the library's own (a.n_sample keys)
 hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
 hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
+// Unfused workspace: the T x L fp32 score matrix, then (fp8) the linear-term parts.
+inline size_t unfused_matrix_bytes(int32_t T, int64_t L) { return align_up((size_t)T * (size_t)L * 4, 256); }
+inline size_t unfused_ws_bytes(int32_t T, int64_t L, int lin_d) {
+    return unfused_matrix_bytes(T, L) + align_up(qlin_bytes(T, lin_d), 256) + align_up(lin_d ? (size_t)T * 4 : 0, 256);
+}
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st);
 hipError_t launch_finalize(const IdxArgs& a, hipStream_t st);
 hipError_t launch_retrieve(int D, const RetrArgs& a, const IdxArgs& fin, hipStream_t st);

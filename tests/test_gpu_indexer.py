@@ -290,3 +290,26 @@ def test_no_sample_draws_its_own(lib):
     say("no sample: candidates/query", st.cand_written / T, "overflow rows", st.overflow_rows)
     assert st.overflow_rows == 0
     check_rows(inp, idx.cpu().numpy(), None, [0, 11, T - 1], "no sample")
+
+
+@pytest.mark.parametrize("H,D", [(64, 128), (33, 64)], ids=["H64_D128", "H33_D64"])
+def test_fp8_score_precision(lib, H, D):
+    """fp8 scores carry the linear term as four fp8 parts (about 16
+    significant bits): every returned score is within 1e-4 of the row's
+    largest |score| of the oracle's fp64 value, far inside the 2e-2 fp8
+    tolerance, so a part dropped or mis-scaled fails here first."""
+    from oracle import indexer_row_scores, key_table
+    inp = indexer_inputs(40, 6000, H, D, "fp8", 150, 300, drift=True, w_range=(-0.2, 1.0), tag=47, n_sample=450)
+    d = to_dev(inp)
+    idx, sc = _run_fused(lib, d, 150)
+    uidx, usc = _run_unfused(lib, d, 150)
+    keys = key_table(inp)
+    worst = 0.0
+    for t in range(40):
+        v, s = indexer_row_scores(inp, t, keys)
+        for gi, gs in ((idx[t], sc[t]), (uidx[t], usc[t])):
+            m = gi >= 0
+            err = np.abs(gs[m].astype(np.float64) - s[gi[m]]) / np.abs(s).max()
+            worst = max(worst, float(err.max()))
+    say("fp8 worst score error / max|I|:", worst)
+    assert worst <= 1e-4
