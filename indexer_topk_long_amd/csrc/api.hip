@@ -253,6 +253,13 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
     a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
     a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
+    a.thr_fin = reinterpret_cast<int*>(wsb + lay.thrf);
+    a.ovf_list = reinterpret_cast<int*>(wsb + lay.ovfl);
+    a.ovf_count = reinterpret_cast<uint32_t*>(wsb + lay.ovfc);
+    // a row can overflow only when its buffer cannot hold every key: then the
+    // overflowed rows are rescanned once, gated at their first pass's final
+    // threshold bin
+    a.pass = (plan.ccap < L) ? 1 : 0;
     a.qlin = fp8 ? wsb + lay.qlin : nullptr;
     a.qinv = fp8 ? reinterpret_cast<float*>(wsb + lay.qinv) : nullptr;
     a.out_idx = out_idx;

@@ -13,8 +13,9 @@
 //             go straight out; an exact top-k runs only inside that bin
 //   (overflow) fallback_kernel -- exact re-scoring radix select for rows whose
 //             candidate buffer overflowed (not on the pages; keeps exactness)
-// Unfused baseline (pages, "Problem statement"): unfused_score_kernel writes
-// the full T x L score matrix, unfused_select_kernel radix-selects each row.
+// Unfused baseline (pages, "Problem statement"): the fused scan's scoring loop
+// in its FULL form writes the whole T x L score matrix, then
+// unfused_select_kernel radix-selects each row.
 #include <math.h>
 
 #include <algorithm>
@@ -734,7 +735,9 @@ constexpr size_t scan_extra_lds(int nbins) {
 // waves of a query take every R-th 64-key block of each tile.  R = 1 at
 // prefill shape; a decode step of one to four queries uses R = 4 or 2, so
 // that the waves score real queries instead of empty slots.
-template <int DT, int D, int HB, int R, bool WIDE, int NST>
+// FULL: the unfused baseline's scoring, the same loop writing every causal
+// score to the T x L matrix instead of gating it.
+template <int DT, int D, int HB, int R, bool WIDE, int NST, bool FULL = false>
 __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     using SS = ScanShape<DT, D, R, WIDE>;
     using G = TileGeom<DT, D, SS::TB>;
@@ -753,7 +756,11 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = lane_id();
     const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
     const int t0 = qg * QPG;
-    const int t = t0 + wave / R;                                           // the wave's query
+    // the rescan pass takes its queries from the list of overflowed rows
+    const int n_rows = (a.pass == 2) ? (int)__builtin_amdgcn_readfirstlane(*a.ovf_count) : a.T;
+    if (t0 >= n_rows) return;                                             // the whole workgroup
+    auto qmap = [&](int i) { return (a.pass == 2) ? (i < n_rows ? a.ovf_list[i] : a.T) : i; };
+    const int t = qmap(t0 + wave / R);                                     // the wave's query
     TileOffsets<DT, D, SS::TB> toff;
     tile_offsets<DT, D, SS::TB>(toff, wave, lane);
     const int sub = wave % R;                                              // its blocks: sub, sub + R, ...
@@ -766,7 +773,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     // keys any query of the group can see, split into tile-aligned ranges
     int e = 0;
     for (int i = lane; i < QPG; i += 64) {
-        const int tt = t0 + i;
+        const int tt = qmap(t0 + i);
         if (tt < a.T) e = max(e, min(a.pos[tt], a.L - 1) + 1);
     }
     const int kend = __builtin_amdgcn_readfirstlane(wave_max_i32(e));   // uniform: every lane holds the max
@@ -777,9 +784,12 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     const int my_pos = tv ? min(a.pos[t], a.L - 1) : -1;
     const int wave_end = min(k_hi, my_pos + 1);
     Meta m{0.0f, 1.0f, 0, 0};
-    if (tv) m = reinterpret_cast<const Meta*>(a.meta)[t];
+    if (tv && !FULL) m = reinterpret_cast<const Meta*>(a.meta)[t];
     int thr = m.thr0;
-    float tau = tv ? initial_gate(thr, m, nbins, a.topk) : -INFINITY;
+    // rescan: gate at the first pass's final threshold bin (a refresh result,
+    // so at most the true one)
+    if (a.pass == 2 && tv) thr = max(thr, a.thr_fin[t]);
+    float tau = (tv && !FULL) ? initial_gate(thr, m, nbins, a.topk) : -INFINITY;
 
     QueryRegs<DT, D, HB> ra;
     load_query<DT, D, HB>(ra, a, t);
@@ -788,7 +798,7 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         // the workgroup's linear-term operands into LDS, 16 bytes per thread
         for (int i = threadIdx.x; i < NG * 16 * 8; i += kScanWaves * 64) {
             const int g = i / 128, r = (i / 8) % 16, c = i % 8;
-            const int ql = 4 * g + (r >> 2), tq = t0 + ql;
+            const int ql = 4 * g + (r >> 2), tq = qmap(t0 + ql);
             u32x4 v{0u, 0u, 0u, 0u};
             if (ql < QPG && tq < a.T && 16 * c < D)
                 v = *reinterpret_cast<const u32x4*>(a.qlin + ((size_t)tq * 4 + (r & 3)) * D + 16 * c);
@@ -850,6 +860,10 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
     // common case costs one compare and a scalar AND.
     const int pos_u = __builtin_amdgcn_readfirstlane(my_pos);
     auto process = [&](float I, int base) {
+        if constexpr (FULL) {   // unfused: every causal score to the matrix
+            if (base + lane <= pos_u) a.S[(size_t)t * a.L + base + lane] = I;
+            return;
+        }
         const int lim = pos_u - base;   // lanes 0..lim are causal
         const uint64_t causal = lim >= 63 ? ~0ull : (lim < 0 ? 0ull : ((2ull << lim) - 1ull));
         const uint64_t mask = __builtin_amdgcn_ballot_w64(I >= tau) & causal;
@@ -1116,6 +1130,8 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
             if ((int64_t)base + lane < a.ccap) a.cand[(size_t)t * a.ccap + base + lane] = en;
         }
     }
+    // first of two passes: the query's final threshold bin, for a rescan
+    if (a.pass == 1 && tv && lane == 0) atomicMax(&a.thr_fin[t], thr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1140,10 +1156,10 @@ __device__ __forceinline__ float* score_row(const IdxArgs& a, int t, float* lds_
 // must be recomputed.  LDS (sh): fin_words(nbins) counters, then kRankMax
 // rank keys and candidate entries, then the sort keys of a sorted output and,
 // without out_score, its scores.
-__device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
+__device__ bool finalize_row(const IdxArgs& a, int t, uint32_t* sh) {
     __shared__ int s_pick;
     __shared__ uint32_t s_above, s_cnt, s_ocnt, s_mcnt;
-    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
+    const int tid = threadIdx.x, wave = tid >> 6, lane = lane_id();
     const int k = a.topk;
     const uint32_t n = a.tail[t];
     int32_t* out = a.out_idx + (size_t)t * k;
@@ -1154,15 +1170,19 @@ __device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
     if (tid == 0 && a.stats) {
         atomicAdd((unsigned long long*)&a.stats->cand_written, (unsigned long long)n);
         atomicMax(&a.stats->max_cand_per_query, n);
-        // stored candidates, this query's sample scores, its outputs
-        const uint64_t stored = (int64_t)n < a.ccap ? (uint64_t)n : (uint64_t)a.ccap;
-        const uint64_t b = 8ull * stored + 4ull * (uint64_t)(*a.nu) + 4ull * (uint64_t)k * (a.out_score ? 2u : 1u);
+        // stored candidates (every pass), this query's sample scores (once),
+        // its outputs (by the pass that writes them: not a first pass whose
+        // overflowed row is rescanned)
+        const bool ovf = (int64_t)n > a.ccap;
+        const uint64_t stored = ovf ? (uint64_t)a.ccap : (uint64_t)n;
+        const uint64_t b = 8ull * stored + (a.pass != 2 ? 4ull * (uint64_t)(*a.nu) : 0ull) +
+                           ((ovf && a.pass == 1) ? 0ull : 4ull * (uint64_t)k * (a.out_score ? 2u : 1u));
         atomicAdd((unsigned long long*)&a.stats->bytes_written, (unsigned long long)b);
     }
-    if ((int64_t)n > a.ccap) {   // the buffer overflowed: the fallback recomputes this row
+    if ((int64_t)n > a.ccap) {   // the buffer overflowed: a rescan or the fallback recomputes this row
         if (tid == 0) {
             a.flags[t] = 1u;
-            if (a.stats) atomicAdd(&a.stats->overflow_rows, 1u);
+            if (a.stats && a.pass != 2) atomicAdd(&a.stats->overflow_rows, 1u);
         }
         return true;
     }
@@ -1318,7 +1338,7 @@ __device__ bool finalize_row(const IdxArgs& a, uint32_t* sh) {
 // Retrieval select (its own fallback kernel re-scores overflowed rows).
 __global__ __launch_bounds__(256) void finalize_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];
-    finalize_row(a, sh);
+    finalize_row(a, blockIdx.x, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1353,14 +1373,27 @@ __device__ __forceinline__ float* row_select_scores(const IdxArgs& a, int t, uin
     return score_row(a, t, reinterpret_cast<float*>(sh + 256 + 2 * (a.sorted ? sort_p2(a.topk) : 0)));
 }
 
-// Indexer select: finalize, and for a row whose candidate buffer overflowed,
-// the exact select over re-computed scores in the same workgroup.
+// Indexer select: finalize.  A row whose candidate buffer overflowed is, in a
+// first pass of two, listed for the rescan (its buffer emptied); in the rescan
+// pass (rows taken from that list) or a single pass, it takes the exact
+// select over re-computed scores in the same workgroup.
 template <int DT, int D, int HB>
 __global__ __launch_bounds__(256) void select_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];
-    if (!finalize_row(a, sh)) return;
-    __syncthreads();
-    const int t = blockIdx.x;
+    int t = blockIdx.x;
+    if (a.pass == 2) {
+        if (blockIdx.x >= *a.ovf_count) return;
+        t = a.ovf_list[blockIdx.x];
+    }
+    if (!finalize_row(a, t, sh)) return;
+    __syncthreads();   // every thread has read the row's candidate count
+    if (a.pass == 1) {
+        if (threadIdx.x == 0) {
+            a.ovf_list[atomicAdd(a.ovf_count, 1u)] = t;
+            a.tail[t] = 0u;
+        }
+        return;
+    }
     RescoreSource<DT, D, HB> src;
     load_query<DT, D, HB>(src.r, a, t);
     if constexpr (DT == DT_FP8) {
@@ -1380,32 +1413,6 @@ __global__ __launch_bounds__(256) void select_kernel(IdxArgs a) {
 // ---------------------------------------------------------------------------
 // Unfused baseline
 // ---------------------------------------------------------------------------
-
-template <int DT, int D, int HB>
-__global__ __launch_bounds__(256) void unfused_score_kernel(IdxArgs a) {
-    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
-    const int qg = blockIdx.x / a.n_splits, split = blockIdx.x % a.n_splits;
-    const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
-    const int t = half ? tb : ta;
-    const KeyRange kr = split_range(a.L, a.n_splits, split, 32);
-    const int k_lo = kr.lo, k_hi = kr.hi;
-    QueryRegs<DT, D, HB> ra, rb;
-    load_query<DT, D, HB>(ra, a, ta);
-    load_query<DT, D, HB>(rb, a, tb);
-    LinPair lp;
-    if constexpr (DT == DT_FP8) load_lin_pair<D>(lp, a, ta, tb);
-    const int my_pos = (t < a.T) ? a.pos[t] : -1;
-    for (int kb = k_lo; kb < k_hi; kb += 32) {
-        const int key = kb + (lane & 31);
-        HalfRow<DT, D> kf;
-        load_key<DT, D>(kf, a.k, min(key, a.L - 1));
-        float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-        if constexpr (DT == DT_FP8)
-            I = lin_score(lin_pair_t<D>(lp, a.k, min(kb + (lane & 15), a.L - 1), min(kb + 16 + (lane & 15), a.L - 1)),
-                          lp.inv, I, a.k_scale[min(key, a.L - 1)]);
-        if (t < a.T && key < k_hi) a.S[(size_t)t * a.L + key] = (key <= my_pos) ? I : -INFINITY;
-    }
-}
 
 __global__ __launch_bounds__(256) void unfused_select_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];
@@ -1639,6 +1646,64 @@ hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_
 }
 
 
+// Launches the fused scan variant that fits: decode shapes (R > 1 waves per
+// query) need room for four tile stages; else one wave per query, with wide
+// tiles where they fit.  FULL (the unfused baseline) always takes one wave
+// per query.  Returns false when no variant fits the LDS.
+template <int DT_, int D_, int HB_, bool FULL>
+static bool run_scan_variant(const IdxArgs& args, hipStream_t st) {
+    constexpr int NB = TileGeom<DT_, D_>::TK / 64;
+    auto scan_lds = [&](auto Rc, auto Wc, auto Nc) -> size_t {
+        constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
+        constexpr bool W_ = decltype(Wc)::value;
+        using SS = ScanShape<DT_, D_, R_, W_>;
+        return (size_t)N_ * TileGeom<DT_, D_, SS::TB>::STAGE_BYTES +
+               scan_extra_lds<DT_, D_, SS::TB, kScanWaves / R_>(args.nbins);
+    };
+    auto launch_scan = [&](auto Rc, auto Wc, auto Nc) {
+        constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
+        constexpr bool W_ = decltype(Wc)::value;
+        constexpr int QPG = kScanWaves / R_;
+        const size_t lds = scan_lds(Rc, Wc, Nc);
+        allow_lds(scan_kernel<DT_, D_, HB_, R_, W_, N_, FULL>, lds);
+        if (args.ev_scan_start) (void)hipEventRecord(args.ev_scan_start, st);
+        scan_kernel<DT_, D_, HB_, R_, W_, N_, FULL>
+            <<<((args.T + QPG - 1) / QPG) * args.n_splits, kScanWaves * 64, lds, st>>>(args);
+        if (args.ev_scan_stop) (void)hipEventRecord(args.ev_scan_stop, st);
+    };
+    if constexpr (!FULL) {
+        const int Rw = scan_waves_per_query(args.T, NB);
+        if constexpr (NB % 4 == 0) {
+            if (Rw == 4 && scan_lds(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
+                launch_scan(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{});
+                return true;
+            }
+        }
+        if constexpr (NB % 2 == 0) {
+            if (Rw == 2 && scan_lds(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
+                launch_scan(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{});
+                return true;
+            }
+        }
+    }
+    // (fp32 at D = 128 keeps 32 KB tiles: its wide variant spills registers)
+    if constexpr (TileGeom<DT_, D_>::RB >= 128 && !(DT_ == DT_F32 && D_ >= 128)) {
+        if (scan_lds(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{}) <= kMaxLds) {
+            launch_scan(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{});
+            return true;
+        }
+    }
+    if (scan_lds(ic<1>{}, std::false_type{}, ic<kScanStages>{}) <= kMaxLds) {
+        launch_scan(ic<1>{}, std::false_type{}, ic<kScanStages>{});
+        return true;
+    }
+    if (scan_lds(ic<1>{}, std::false_type{}, ic<2>{}) <= kMaxLds) {
+        launch_scan(ic<1>{}, std::false_type{}, ic<2>{});
+        return true;
+    }
+    return false;
+}
+
 hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
     const int nqg = (a.T + kQPG - 1) / kQPG;
     hipError_t err = hipSuccess;
@@ -1647,59 +1712,22 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
-        constexpr int NB = TileGeom<DT_, D_>::TK / 64;
-        // LDS of a scan variant: R waves per query, wide tiles, NST stages
-        auto scan_lds = [&](auto Rc, auto Wc, auto Nc) -> size_t {
-            constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
-            constexpr bool W_ = decltype(Wc)::value;
-            using SS = ScanShape<DT_, D_, R_, W_>;
-            return (size_t)N_ * TileGeom<DT_, D_, SS::TB>::STAGE_BYTES +
-                   scan_extra_lds<DT_, D_, SS::TB, kScanWaves / R_>(a.nbins);
-        };
-        auto launch_scan = [&](auto Rc, auto Wc, auto Nc) {
-            constexpr int R_ = decltype(Rc)::value, N_ = decltype(Nc)::value;
-            constexpr bool W_ = decltype(Wc)::value;
-            constexpr int QPG = kScanWaves / R_;
-            const size_t lds = scan_lds(Rc, Wc, Nc);
-            allow_lds(scan_kernel<DT_, D_, HB_, R_, W_, N_>, lds);
-            if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-            scan_kernel<DT_, D_, HB_, R_, W_, N_><<<((a.T + QPG - 1) / QPG) * a.n_splits, kScanWaves * 64, lds, st>>>(a);
-            if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
-        };
-        // decode shapes (R > 1) need room for four tile stages, else one wave per query
-        const int Rw = scan_waves_per_query(a.T, NB);
-        bool launched = false;
-        if constexpr (NB % 4 == 0) {
-            if (!launched && Rw == 4 && scan_lds(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
-                launch_scan(ic<4>{}, std::false_type{}, ic<kScanStagesFew>{});
-                launched = true;
-            }
-        }
-        if constexpr (NB % 2 == 0) {
-            if (!launched && Rw == 2 && scan_lds(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{}) <= kMaxLds) {
-                launch_scan(ic<2>{}, std::false_type{}, ic<kScanStagesFew>{});
-                launched = true;
-            }
-        }
-        // (fp32 at D = 128 keeps 32 KB tiles: its wide variant spills registers)
-        if constexpr (TileGeom<DT_, D_>::RB >= 128 && !(DT_ == DT_F32 && D_ >= 128)) {
-            if (!launched && scan_lds(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{}) <= kMaxLds) {
-                launch_scan(ic<1>{}, std::true_type{}, ic<kScanStagesWide>{});
-                launched = true;
-            }
-        }
-        if (!launched && scan_lds(ic<1>{}, std::false_type{}, ic<kScanStages>{}) <= kMaxLds) {
-            launch_scan(ic<1>{}, std::false_type{}, ic<kScanStages>{});
-            launched = true;
-        }
-        if (!launched && scan_lds(ic<1>{}, std::false_type{}, ic<2>{}) <= kMaxLds) {
-            launch_scan(ic<1>{}, std::false_type{}, ic<2>{});
-            launched = true;
-        }
-        if (!launched) { err = hipErrorInvalidValue; return; }
+        auto run_scan = [&](const IdxArgs& args) { return run_scan_variant<DT_, D_, HB_, false>(args, st); };
+        if (!run_scan(a)) { err = hipErrorInvalidValue; return; }
         const size_t sel_lds = std::max(fin_lds_bytes(a), row_select_lds(a.topk, a.sorted, a.out_score != nullptr));
         allow_lds(select_kernel<DT_, D_, HB_>, sel_lds);
         select_kernel<DT_, D_, HB_><<<a.T, 256, sel_lds, st>>>(a);
+        if (a.pass == 1) {
+            // rescan of the rows whose buffer overflowed, gated at their first
+            // pass's final threshold bin; without the shared histograms, whose
+            // first-pass counts would otherwise be counted twice
+            IdxArgs b = a;
+            b.pass = 2;
+            b.hist_g = nullptr;
+            b.ev_scan_start = b.ev_scan_stop = nullptr;
+            if (!run_scan(b)) { err = hipErrorInvalidValue; return; }
+            select_kernel<DT_, D_, HB_><<<a.T, 256, sel_lds, st>>>(b);
+        }
         err = hipGetLastError();
     });
     return ok ? err : hipErrorInvalidValue;
@@ -1718,12 +1746,11 @@ hipError_t launch_finalize(const IdxArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
-    const int nqg = (a.T + kQPG - 1) / kQPG;
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
         if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
-        unfused_score_kernel<DT_, D_, HB_><<<nqg * a.n_splits, 256, 0, st>>>(a);
+        if (!run_scan_variant<DT_, D_, HB_, true>(a, st)) { err = hipErrorInvalidValue; return; }
         const size_t lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
         allow_lds(unfused_select_kernel, lds);
         unfused_select_kernel<<<a.T, 256, lds, st>>>(a);

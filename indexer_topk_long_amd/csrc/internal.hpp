@@ -48,8 +48,8 @@ inline int sample_chunks(int64_t L) {
 // Workspace of one fused call.  The [zero_begin, zero_end) range is cleared
 // by the first kernel of every call.
 struct WsLayout {
-    size_t tail, flags, hist, bitmap, ccount, zero_begin, zero_end;
-    size_t nu, meta, sample_u, sscore, qlin, qinv, cand, total;
+    size_t tail, flags, thrf, ovfc, hist, bitmap, ccount, zero_begin, zero_end;
+    size_t nu, meta, sample_u, sscore, qlin, qinv, ovfl, cand, total;
 };
 
 // Per-query linear-term operands of the fp8 score (four fp8 parts of D bytes
@@ -83,6 +83,8 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, 
     w.zero_begin = o;
     w.tail = o;   o = align_up(o + (size_t)T * 4, 256);
     w.flags = o;  o = align_up(o + (size_t)T * 4, 256);
+    w.thrf = o;   o = align_up(o + (size_t)T * 4, 256);
+    w.ovfc = o;   o = align_up(o + 64, 256);
     w.hist = o;   o = align_up(o + hist_words * 4, 256);
     w.bitmap = o; o = align_up(o + (size_t)((L + 31) / 32) * 4, 256);
     w.ccount = o; o = align_up(o + (size_t)sample_chunks(L) * 4, 256);
@@ -96,6 +98,7 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, 
     w.sscore = o;   o = align_up(o + (size_t)T * (size_t)(n_sample > 0 ? n_sample : 1) * 4, 256);
     w.qlin = o;     o = align_up(o + qlin_bytes(T, lin_d), 256);
     w.qinv = o;     o = align_up(o + (lin_d ? (size_t)T * 4 : 0), 256);
+    w.ovfl = o;     o = align_up(o + (size_t)T * 4, 256);
     w.cand = o;     o = align_up(o + (size_t)T * (size_t)ccap * 8, 256);
     w.total = o;
     return w;
@@ -116,6 +119,9 @@ struct IdxArgs {
     int refresh_every;       // <= 0: never
     int sorted;
     int flush;               // candidates per write-back batch (32 or 64)
+    int pass;                // 0: one pass (an overflowed row takes the exact fallback);
+                             // 1: first pass of two (overflowed rows are listed for a rescan);
+                             // 2: the rescan of the listed rows
     int64_t ccap;
     // workspace
     uint32_t* tail;
@@ -127,6 +133,9 @@ struct IdxArgs {
     int32_t* sample_u;
     float* sscore;
     uint2* cand;
+    int* thr_fin;            // [T] final threshold bin of the first pass (max over the query's waves)
+    int* ovf_list;           // [T] rows whose first-pass buffer overflowed
+    uint32_t* ovf_count;     // number of them
     uint8_t* qlin;           // fp8: [T][4][D] parts of each query's q''/2 (linear term), else null
     float* qinv;             // fp8: [T] 1/S of those parts
     // outputs
