@@ -137,6 +137,27 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
                           int32_t n_sample, int32_t* out_idx, float* out_score, void* ws,
                           size_t ws_bytes, const ltk_opts* opts, ltk_stats* stats, void* stream);
 
+/* litetopk_score_select for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops such as decode steps,
+ * harnesses that forbid hipMalloc): the same arguments, checks, kernels and
+ * results, without a workspace argument.  The workspace is a static device
+ * array of the library, 96 MiB per GPU (held by each GPU the library runs on
+ * until the process ends), shared by every call of this entry point on that
+ * GPU: calls that may overlap on one GPU (other streams, other host threads)
+ * race and must be serialised by the caller.  Each call clears what must
+ * start at zero with its own kernels (no memset node).  Returns
+ * LTK_EWORKSPACE, before enqueuing anything, when
+ * litetopk_workspace_bytes(LTK_KIND_SCORE_SELECT, ...) exceeds 96 MiB: e.g.
+ * a decode or speculative-decode step (T <= 8) over up to 1M keys fits, a
+ * 1M-context 8,192-query prefill chunk does not.  The first call on a
+ * device looks up the array's device address (hipGetSymbolAddress); no
+ * call allocates. */
+int litetopk_score_select_static(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                 const float* w, const int32_t* pos, int32_t T, int32_t H, int32_t D,
+                                 int64_t L, int32_t dtype, int32_t topk, const int32_t* sample,
+                                 int32_t n_sample, int32_t* out_idx, float* out_score,
+                                 const ltk_opts* opts, ltk_stats* stats, void* stream);
+
 /* Fused inner-product retrieval top-k (LiteTopK pages: the same primitive
  * serves vector retrieval; "Large-scale retrieval", k from 1,024).
  *

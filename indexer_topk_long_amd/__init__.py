@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     library,
     retrieve,
     score_select,
+    score_select_static,
     strerror,
     unfused_score_select,
     workspace_bytes,
@@ -35,5 +36,5 @@ from .prefill import next_sample, prefill_chunked, prefill_workspace_bytes  # no
 __all__ = [
     "score_select", "retrieve", "unfused_score_select", "workspace_bytes", "strerror", "device_check",
     "Opts", "Stats", "LtkError", "next_sample", "prefill_chunked", "library", "exported_symbols",
-    "dsa_pack", "dsa_gather", "prefill_workspace_bytes",
+    "dsa_pack", "dsa_gather", "prefill_workspace_bytes", "score_select_static",
 ]

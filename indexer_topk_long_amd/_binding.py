@@ -74,6 +74,10 @@ def library() -> ctypes.CDLL:
         lib.litetopk_score_select.restype = ctypes.c_int
         lib.litetopk_score_select.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i64,
                                               _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p, _c_p, _c_p]
+        lib.litetopk_score_select_static.restype = ctypes.c_int
+        lib.litetopk_score_select_static.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                                     _c_i64, _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p, _c_p,
+                                                     _c_p]
         lib.litetopk_unfused_score_select.restype = ctypes.c_int
         lib.litetopk_unfused_score_select.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                                                       _c_i64, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_sz, _c_p]
@@ -238,6 +242,39 @@ def score_select(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=Non
                                    _ptr(st), _stream())
     if rc != 0:
         raise LtkError(rc, "litetopk_score_select")
+    res = [out]
+    if return_scores:
+        res.append(osc)
+    if return_stats:
+        res.append(_read_stats(st))
+    return res[0] if len(res) == 1 else tuple(res)
+
+
+def score_select_static(q, k, w, pos, topk: int, sample=None, q_scale=None, k_scale=None, opts: Opts | None = None,
+                        return_scores: bool = False, return_stats: bool = False, out=None, out_score=None):
+    """litetopk_score_select_static: score_select on the library's static
+    workspace (no workspace allocation).  With `out` (and `out_score`) given,
+    the call allocates nothing at all: the caller owns every buffer."""
+    import torch
+    T, H, D, L, dt = _check_indexer_args(q, k, w, pos, q_scale, k_scale, sample)
+    ns = 0 if sample is None else sample.numel()
+    if out is None:
+        out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    _expect(tuple(out.shape) == (T, topk), f"out must be [{T}, {topk}]")
+    _dev(out, "out", torch.int32)
+    osc = out_score
+    if return_scores and osc is None:
+        osc = torch.empty((T, topk), dtype=torch.float32, device=q.device)
+    if osc is not None:
+        _expect(tuple(osc.shape) == (T, topk), f"out_score must be [{T}, {topk}]")
+        _dev(osc, "out_score", torch.float32)
+    st = _stats_buf(q.device) if return_stats else None
+    o = opts.c() if opts is not None else None
+    rc = library().litetopk_score_select_static(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(pos),
+                                                T, H, D, L, dt, topk, _ptr(sample), ns, _ptr(out), _ptr(osc),
+                                                ctypes.byref(o) if o is not None else None, _ptr(st), _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_score_select_static")
     res = [out]
     if return_scores:
         res.append(osc)

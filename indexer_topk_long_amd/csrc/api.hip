@@ -10,6 +10,29 @@ namespace ltk {
 
 static std::atomic<int> g_arch_ok[64];   // 0 unknown, 1 gfx950, -1 other
 
+// Workspace of litetopk_score_select_static: a file-scope device array (each
+// GPU the library runs on holds its own copy until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address comes from hipGetSymbolAddress, once per device, and only
+// that address is ever passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static std::atomic<void*> g_scratch[64];
+
+// Device address of this device's `scratch` (looked up on the first call on
+// the device, with that device current).
+static int static_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LTK_EHIP;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LTK_EHIP;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return LTK_OK;
+}
+
 static int device_check() {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return LTK_EHIP;
@@ -273,6 +296,35 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     if (launch_prepare_sample(a, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;
     if (launch_indexer_fused(dtype, D, head_blocks(H), a, s) != hipSuccess) return LTK_EHIP;
     return LTK_OK;
+}
+
+int litetopk_score_select_static(const void* q, const float* q_scale, const void* k, const float* k_scale,
+                                 const float* w, const int32_t* pos, int32_t T, int32_t H, int32_t D, int64_t L,
+                                 int32_t dtype, int32_t topk, const int32_t* sample, int32_t n_sample,
+                                 int32_t* out_idx, float* out_score, const ltk_opts* opts, ltk_stats* stats,
+                                 void* stream) {
+    // the same checks and kernels as litetopk_score_select, on the static
+    // workspace: a call that needs more than it holds is rejected before
+    // anything is enqueued
+    const size_t need = litetopk_workspace_bytes(LTK_KIND_SCORE_SELECT, T, H, D, L, topk, n_sample, dtype, opts);
+    if (need == 0) {
+        const int st = check_indexer_sizes(T, H, D, L, dtype, topk);
+        return st != LTK_OK ? st : LTK_EINVAL;
+    }
+    if (need > kStaticScratchBytes) return LTK_EWORKSPACE;
+    if (T == 0) {
+        // no queries: litetopk_score_select checks the arguments and returns
+        // before it touches any workspace (this aligned host word stands in)
+        alignas(256) static unsigned char no_work[256];
+        return litetopk_score_select(q, q_scale, k, k_scale, w, pos, T, H, D, L, dtype, topk, sample, n_sample,
+                                     out_idx, out_score, no_work, need, opts, stats, stream);
+    }
+    int st = device_check();
+    if (st != LTK_OK) return st;
+    void* ws = nullptr;
+    if ((st = static_scratch(&ws)) != LTK_OK) return st;
+    return litetopk_score_select(q, q_scale, k, k_scale, w, pos, T, H, D, L, dtype, topk, sample, n_sample, out_idx,
+                                 out_score, ws, kStaticScratchBytes, opts, stats, stream);
 }
 
 int litetopk_unfused_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale,

@@ -26,7 +26,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = ltk.exported_symbols()
-    assert len(names) == 9
+    assert len(names) == 10
     for n in names:
         assert hasattr(L, n), n
 
