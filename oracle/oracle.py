@@ -106,7 +106,8 @@ def indexer_scores(q: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray
 
 
 def retrieval_scores(q: np.ndarray, db: np.ndarray) -> np.ndarray:
-    """Inner products q . x[s] of one query against a block of rows, in fp64."""
+    """Inner products q . x[s] of one query ([D]) against a block of rows, in
+    fp64 ([n]); with queries as columns ([D, R]), one column per query ([n, R])."""
     return db @ q
 
 
@@ -130,10 +131,14 @@ def first_copy(raw: np.ndarray, scale: np.ndarray | None = None) -> np.ndarray:
     if b.shape[1] % 8:
         b = np.concatenate([b, np.zeros((n, 8 - b.shape[1] % 8), np.uint8)], axis=1)
     words = np.ascontiguousarray(b).view(np.uint64)
-    h = np.zeros(n, np.uint64)
+    # hash: sum of the row's 64-bit words times fixed odd multipliers, mod
+    # 2^64 (rows taken in blocks, so that large tables stream through memory
+    # once); a collision only costs the byte comparison below
+    mult = (np.arange(words.shape[1], dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)) | np.uint64(1)
+    h = np.empty(n, np.uint64)
     with np.errstate(over="ignore"):
-        for j in range(words.shape[1]):
-            h = h * np.uint64(0x9E3779B97F4A7C15) + words[:, j]
+        for r0 in range(0, n, 1 << 14):
+            h[r0 : r0 + (1 << 14)] = (words[r0 : r0 + (1 << 14)] * mult).sum(axis=1, dtype=np.uint64)
     _, first, inv = np.unique(h, return_index=True, return_inverse=True)
     rep = first[inv.ravel()].astype(np.int64)
     moved = np.nonzero(rep != np.arange(n))[0]
@@ -224,17 +229,22 @@ def oracle_retrieval(q_raw: np.ndarray, db_raw: np.ndarray, k: int, rows=None, d
     return out_i, out_s
 
 
-def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t: int, dtype: str = "bf16",
+def retrieval_row_scores(q_raw: np.ndarray, db_raw: np.ndarray, t, dtype: str = "bf16",
                          block: int = 1 << 18, rep: np.ndarray | None = None) -> np.ndarray:
-    """fp64 scores of query t against every database row.  ``rep`` is
-    ``first_copy(db_raw)`` (computed here when not given): each row takes the
-    score of its first bit-identical copy."""
-    qd = decode(q_raw[t : t + 1], dtype)[0]
+    """fp64 scores of query t against every database row ([N]); for a
+    sequence of query indices, one row of scores per query ([len(t), N]).
+    ``rep`` is ``first_copy(db_raw)`` (computed here when not given): each row
+    takes the score of its first bit-identical copy."""
+    many = not np.isscalar(t)
+    rows = np.atleast_1d(np.asarray(t, dtype=np.int64))
+    qd = decode(q_raw[rows], dtype)                      # [R, D]
     N = db_raw.shape[0]
-    out = np.empty(N, dtype=np.float64)
+    out = np.empty((len(rows), N), dtype=np.float64)
     for s0 in range(0, N, block):
-        out[s0 : s0 + block] = retrieval_scores(qd, decode(db_raw[s0 : s0 + block], dtype))
-    return out[first_copy(db_raw) if rep is None else rep]
+        xd = decode(db_raw[s0 : s0 + block], dtype)      # [n, D]
+        out[:, s0 : s0 + len(xd)] = retrieval_scores(qd.T, xd).T   # [n, R] -> [R, n]
+    out = out[:, first_copy(db_raw) if rep is None else rep]
+    return out if many else out[0]
 
 
 def next_sample(prev_idx: np.ndarray, L: int, n: int) -> np.ndarray:

@@ -275,11 +275,16 @@ def check_retrieval_row_scores_closed_form(O):
         return torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
     xb, qb = bits(x), bits(q)
-    for t in range(2):
-        ref = np.array([float(c[s]) * float(q[t, (7 * s) % D]) for s in range(N)])
-        for blk in (5, 1 << 18):
+    refs = [np.array([float(c[s]) * float(q[t, (7 * s) % D]) for s in range(N)]) for t in range(2)]
+    for blk in (5, 1 << 18):
+        for t in range(2):
             got = O.retrieval_row_scores(qb, xb, t, block=blk)
-            assert got.shape == (N,) and np.array_equal(got, ref), (t, blk, got, ref)
+            assert got.shape == (N,) and np.array_equal(got, refs[t]), (t, blk, got, refs[t])
+        # several queries in one call: one row of scores per query, in the order asked
+        got = O.retrieval_row_scores(qb, xb, [1, 0, 0], block=blk)
+        assert got.shape == (3, N), got.shape
+        for i, t in enumerate([1, 0, 0]):
+            assert np.array_equal(got[i], refs[t]), (i, t, blk)
 
 
 def check_retrieval_row_scores_self_match(O, seed=13):

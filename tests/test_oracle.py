@@ -158,18 +158,29 @@ def _ns_counts_invalid(m):
 def _rrs_block_offset(m):
     orig = m.retrieval_row_scores
 
-    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18):
-        out = orig(q_raw, db_raw, t, dtype, block)
-        for s0 in range(0, len(out), block):
-            out[s0:s0 + block] = np.roll(out[s0:s0 + block], 1)
+    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18, rep=None):
+        out = orig(q_raw, db_raw, t, dtype, block, rep)
+        for s0 in range(0, out.shape[-1], block):
+            out[..., s0:s0 + block] = np.roll(out[..., s0:s0 + block], 1, axis=-1)
         return out
     m.retrieval_row_scores = retrieval_row_scores
 
 
 def _rrs_transposed(m):
-    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18):
-        qd = m.decode(q_raw[t:t + 1], dtype)[0]
-        return m.decode(db_raw, dtype)[:, ::-1] @ qd
+    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18, rep=None):
+        qd = m.decode(q_raw[np.atleast_1d(t)], dtype)
+        out = (m.decode(db_raw, dtype)[:, ::-1] @ qd.T).T
+        return out if not np.isscalar(t) else out[0]
+    m.retrieval_row_scores = retrieval_row_scores
+
+
+def _rrs_rows_swapped(m):
+    # several queries at once: the score rows come back in the wrong order
+    orig = m.retrieval_row_scores
+
+    def retrieval_row_scores(q_raw, db_raw, t, dtype="bf16", block=1 << 18, rep=None):
+        out = orig(q_raw, db_raw, t, dtype, block, rep)
+        return out[::-1].copy() if not np.isscalar(t) else out
     m.retrieval_row_scores = retrieval_row_scores
 
 
@@ -197,6 +208,7 @@ MUTANTS = {
                                                               P.check_retrieval_row_scores_self_match]),
     "retrieval_row_scores_transposed": (_rrs_transposed, [P.check_retrieval_row_scores_closed_form,
                                                           P.check_retrieval_row_scores_self_match]),
+    "retrieval_row_scores_rows_swapped": (_rrs_rows_swapped, [P.check_retrieval_row_scores_closed_form]),
     "identical_keys_scored_apart": (_no_first_copy, [P.check_first_copy_brute_force]),
 }
 
