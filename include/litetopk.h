@@ -164,7 +164,8 @@ int litetopk_score_select_static(const void* q, const float* q_scale, const void
  *  q [T, D] queries, db [N, D] database rows, both dtype (LTK_BF16 only),
  *  D in {64, 128, 256, 512, 768}, 1 <= N <= 2^31 - 256; sample [n_sample] database
  *  rows used to estimate the score range (duplicates and out-of-range
- *  entries ignored).  opts->l_splits sets the number of database splits.
+ *  entries ignored).  opts->l_splits sets the number of database splits
+ *  (LTK_EINVAL if a split would hold more than 2^26 rows).
  *  Other arguments as above.
  */
 int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype,

@@ -135,12 +135,15 @@ static IdxPlan indexer_plan(int32_t T, int64_t L, int32_t dtype, const Opts& o) 
 
 // Shared retrieval histograms: nbins fine counters + one per 16-bin super-bin, per query.
 // Retrieval database splits: the caller's count, else about 2048 workgroups
-// (4 waves x 32 queries each) of at least 2048 rows.
-static int retr_splits(int32_t T, int64_t N, int l_splits) {
+// (4 waves x 64 queries each) of at least 2048 rows.
+// A split holds at most 2^26 rows (the scan packs a row's offset in its
+// split into 26 bits); a caller's count that leaves more is rejected.
+constexpr int64_t kRetrMaxSplitRows = (int64_t)1 << 26;
+static int retr_splits(int32_t T, int32_t D, int64_t N, int l_splits) {
     if (l_splits > 0) return l_splits;
-    const int64_t nqg = (T + 127) / 128;
+    const int64_t nqg = (T + retr_group_queries(D) - 1) / retr_group_queries(D);
     int ns = 1;
-    while (nqg * ns < 2048 && N / ((int64_t)ns * 2) >= 2048) ns *= 2;
+    while ((nqg * ns < 2048 && N / ((int64_t)ns * 2) >= 2048) || (N + ns - 1) / ns > kRetrMaxSplitRows) ns *= 2;
     return ns;
 }
 // Zeroed shared counters of the retrieval scan: fine and super-bin
@@ -214,7 +217,7 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
         return 0;
     if (kind == LTK_KIND_RETRIEVE)
         return ws_layout(T, L, sample_slots(n_sample, topk, L), o.ccap,
-                         retr_hist_words(T, o.nbins, retr_splits(T, L, o.l_splits))).total;
+                         retr_hist_words(T, o.nbins, retr_splits(T, D, L, o.l_splits))).total;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
     return ws_layout(T, L, sample_slots(n_sample, topk, L), p.ccap, p.shared ? (size_t)T * o.nbins : 0,
                      dtype == LTK_FP8_E4M3FN ? D : 0).total;
@@ -396,7 +399,8 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     int st;
     if ((st = resolve_opts(opts, retrieve_default_ccap(topk), o)) != LTK_OK) return st;
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
-    const int ns = retr_splits(T, N, o.l_splits);
+    const int ns = retr_splits(T, D, N, o.l_splits);
+    if ((N + ns - 1) / ns > kRetrMaxSplitRows) return LTK_EINVAL;
     const int32_t n_slots = sample_slots(n_sample, topk, N);
     const WsLayout lay = ws_layout(T, N, n_slots, o.ccap, retr_hist_words(T, o.nbins, ns));
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
@@ -436,7 +440,7 @@ int litetopk_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64
     r.nbins = o.nbins;
     r.nsuper = (o.nbins + 15) / 16;
     r.n_sample = f.n_sample;
-    r.n_qgroups = (T + 127) / 128;   // 4 waves x 32 queries per workgroup
+    r.n_qgroups = (T + retr_group_queries(D) - 1) / retr_group_queries(D);
     r.n_splits = ns;
     r.cap_s = o.ccap / ns;
     r.sorted = o.sorted;

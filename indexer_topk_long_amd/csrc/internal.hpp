@@ -146,13 +146,19 @@ struct IdxArgs {
     hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch
 };
 
+// Waves per workgroup of the retrieval scan (32 queries each, two waves per
+// SIMD): 8, or 4 when a tile of 32 rows is fewer than 8 wave-wide 1 KB loads
+// (D = 64).
+constexpr int retr_waves(int D) { return (D / 16) % 8 == 0 ? 8 : 4; }
+constexpr int retr_group_queries(int D) { return retr_waves(D) * 32; }
+
 // Everything a kernel of the fused retrieval path needs.
 struct RetrArgs {
     const uint8_t* q;        // [T, D] bf16
     const uint8_t* db;       // [N, D] bf16
     int T, N, topk, nbins, nsuper;
     int n_sample;            // row stride of sscore
-    int n_splits, n_qgroups; // database splits x query groups of 256
+    int n_splits, n_qgroups; // database splits x query groups (retr_group_queries(D) queries)
     int sorted;
     int64_t ccap;
     uint32_t* tail;

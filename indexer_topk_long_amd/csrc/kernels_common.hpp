@@ -16,6 +16,27 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// wait_vm<N + e> for a wave-uniform run-time count `extra` of further vector
+// memory instructions known to have been issued after the awaited ones:
+// e is the largest step of {0, 4, 8, 16, 32} not above extra (and with
+// N + e <= 63), so the wait never allows more than extra beyond N.
+template <int N>
+__device__ __forceinline__ void wait_vm_plus(int extra) {
+    if constexpr (N + 32 <= 63) {
+        if (extra >= 32) { wait_vm<N + 32>(); return; }
+    }
+    if constexpr (N + 16 <= 63) {
+        if (extra >= 16) { wait_vm<N + 16>(); return; }
+    }
+    if constexpr (N + 8 <= 63) {
+        if (extra >= 8) { wait_vm<N + 8>(); return; }
+    }
+    if constexpr (N + 4 <= 63) {
+        if (extra >= 4) { wait_vm<N + 4>(); return; }
+    }
+    wait_vm<N>();
+}
+
 // Wait, visibly to the compiler, until every vector-memory load issued so far
 // has landed (s_waitcnt vmcnt(0); expcnt and lgkmcnt untouched).  Used once
 // after the per-wave register loads that precede a streaming loop: the

@@ -4,11 +4,12 @@
 // "Methodology"; the pages apply the primitive to vector retrieval), with
 // the score I[t, s] = q[t] . x[s] of bf16 vectors (fp32 accumulation) and no
 // causal mask.  Queries sit on the MFMA M dimension: one wave holds 32
-// queries in registers and scores them against 32 database rows per tile,
-// so every accumulator register is a (query, row) score and no head
-// reduction is needed.  Database rows stream through LDS in 48 KB tiles
-// (direct global->LDS loads, double-buffered) shared by the 4 waves of a
-// workgroup (128 queries).
+// queries in registers and scores them against 32 database rows per tile, so
+// every accumulator register is a (query, row) score and no head reduction
+// is needed.  Database rows stream through LDS in tiles (direct global->LDS
+// loads) shared by the 8 waves of a workgroup (256 queries), two waves per
+// SIMD, so that one wave's candidate handling and refreshes overlap the
+// other's MFMAs (4 waves at D = 64, whose tile is 4 loads).
 //
 // The database is split across workgroups.  Their per-query histograms are
 // one shared array in device memory: every kept candidate adds to it with an
@@ -29,14 +30,15 @@
 
 namespace ltk {
 
-constexpr int kRetrWaves = 4;             // waves per workgroup (one per SIMD: 32 queries of
-                                          // D = 768 take 192 registers per lane)
 constexpr int kRetrQ = 32;                // queries per wave (one MFMA M block)
+constexpr int kRetrQB = 1;                // query blocks per wave
 constexpr int kRetrRows = 32;             // database rows per LDS tile
 constexpr int kRetrRefreshCands = 64;     // candidates a wave adds before it refreshes
 constexpr int kSuperBins = 16;            // fine bins per super-bin of the shared histogram
 
 constexpr int kRetrStashRegs = 8;         // accumulator registers staged per rare-path round
+constexpr int kRetrQueue = 128;           // candidate queue entries per wave (flushed 64 at a time)
+constexpr int kRetrSplitRowsLog2 = 26;    // a split's rows fit 26 bits of a queue entry
 
 template <int D>
 struct RetrGeom {
@@ -44,13 +46,18 @@ struct RetrGeom {
     static constexpr int CPR = RB / 16;                    // 16-byte chunks per row
     static constexpr int TILE = kRetrRows * RB;            // bytes per tile
     static constexpr int NINST = kRetrRows * CPR / 64;     // wave-wide 1 KB loads per tile
-    static constexpr int LPW = NINST / kRetrWaves;         // loads per wave per tile
+    static constexpr int W = retr_waves(D);                // waves per workgroup (two per SIMD)
+    static_assert(W * kRetrQ == retr_group_queries(D), "query group size as the host computes it");
+    static constexpr int LPW = NINST / W;                  // loads per wave per tile
     static constexpr int KSTEPS = D / 16;                  // v_mfma_f32_32x32x16_bf16 steps
-    static_assert(NINST % kRetrWaves == 0, "tile loads split evenly over the waves");
-    // per wave: thresholds, candidate counts, bin-map origin and scale of its 32 queries; score stash
-    static constexpr size_t FIXED_LDS = (size_t)kRetrWaves * kRetrQ * 4 * 4 + (size_t)kRetrWaves * kRetrStashRegs * 64 * 4;
-    // tile stages: as many as fit (at most 4), so tiles are requested two or
-    // three tiles ahead of their use (one tile of MFMA work is ~0.7 us at D = 768)
+    static_assert(NINST % W == 0, "tile loads split evenly over the waves");
+    // per wave: thresholds, candidate counts, bin-map origin and scale of its queries; score
+    // stash; candidate queue
+    static constexpr size_t FIXED_LDS = (size_t)W * kRetrQB * kRetrQ * 4 * 4 +
+                                        (size_t)W * kRetrStashRegs * 64 * 4 + (size_t)W * kRetrQueue * 8;
+    // tile stages: as many as fit (at most 4), so tiles are requested one to
+    // three tiles ahead of their use (two at D = 768, where a tile of MFMA
+    // work for the 8 waves takes ~2 us)
     static constexpr int NST = ((kMaxLds - FIXED_LDS) / TILE) < 4 ? (int)((kMaxLds - FIXED_LDS) / TILE) : 4;
     static_assert(NST >= 2, "at least double buffering");
     static constexpr size_t LDS = (size_t)NST * TILE + FIXED_LDS;
@@ -106,22 +113,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Filter: the fused scan over the database
 // ---------------------------------------------------------------------------
 
-// This wave's j-th 1 KB direct load of the tile starting at row0 (16-byte
-// chunk p = 64*inst + lane holds chunk (p % CPR) ^ swz(row) of row p / CPR).
+// Byte offset, within a tile, of this lane's 16-byte chunk in the wave's
+// j-th 1 KB direct load (chunk p = 64*inst + lane holds chunk
+// (p % CPR) ^ swz(row) of row p / CPR); the same for every tile.
 template <int D>
-__device__ __forceinline__ void retr_load_part(const RetrArgs& a, int row0, uint8_t* st, int wave, int lane, int j) {
+__device__ __forceinline__ uint32_t retr_part_off(int wave, int lane, int j) {
     using G = RetrGeom<D>;
-    const int inst = wave + j * kRetrWaves;
+    const int inst = wave + j * RetrGeom<D>::W;
     const int p = inst * 64 + lane;
     const int r = p / G::CPR, pc = p % G::CPR;
-    const int c = pc ^ chunk_swz<G::RB, G::CPR>(r);
-    const int row = min(row0 + r, a.N - 1);
-    lds_direct16_async(a.db + (size_t)row * G::RB + c * 16, st + inst * 1024);
+    return (uint32_t)(r * G::RB + (pc ^ chunk_swz<G::RB, G::CPR>(r)) * 16);
+}
+// Source of the tile starting at row0: a wave-uniform base row and the
+// largest in-bounds chunk offset from it.  Clamping a lane's offset to `lim`
+// leaves every chunk of a row below N where it is (its offset is at most
+// lim) and sends those of rows past the end (a ragged last tile, tiles
+// requested past a split's last one) to the database's last chunk.
+struct TileSrc {
+    const uint8_t* base;
+    uint32_t lim;
+};
+template <int D>
+__device__ __forceinline__ TileSrc retr_tile_src(const RetrArgs& a, int row0) {
+    const int r0 = min(row0, a.N - 1);
+    const int64_t lim = (int64_t)(a.N - r0) * RetrGeom<D>::RB - 16;
+    return {a.db + (size_t)r0 * RetrGeom<D>::RB, (uint32_t)min<int64_t>(lim, (int64_t)0xffffffffu)};
 }
 template <int D>
-__device__ __forceinline__ void retr_load_tile(const RetrArgs& a, int row0, uint8_t* st, int wave, int lane) {
-#pragma unroll
-    for (int j = 0; j < RetrGeom<D>::LPW; ++j) retr_load_part<D>(a, row0, st, wave, lane, j);
+__device__ __forceinline__ void retr_load_part(const TileSrc& src, uint32_t off, uint8_t* st, int wave, int j) {
+    lds_direct16_async(src.base, min(off, src.lim), st + (wave + j * RetrGeom<D>::W) * 1024);
 }
 
 // Coherent (device-scope) read of a shared counter.
@@ -130,15 +150,19 @@ __device__ __forceinline__ uint32_t load_shared_count(const uint32_t* p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void retr_scan_kernel(RetrArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void retr_scan_kernel(RetrArgs a) {
     using G = RetrGeom<D>;
+    constexpr int QW = kRetrQB * kRetrQ;                                  // queries per wave
+    constexpr int NR = kRetrQB * 16;                                      // score registers per lane and tile
     extern __shared__ __attribute__((aligned(16))) uint8_t shm[];
     uint8_t* tiles = shm;                                                 // G::NST stages
-    float* tau_l = reinterpret_cast<float*>(shm + G::NST * G::TILE);      // [waves][32 queries]
-    uint32_t* cnt_l = reinterpret_cast<uint32_t*>(tau_l + kRetrWaves * kRetrQ);   // [waves][32]
-    float* smin_l = reinterpret_cast<float*>(cnt_l + kRetrWaves * kRetrQ);        // [waves][32]
-    float* delta_l = smin_l + kRetrWaves * kRetrQ;                                 // [waves][32]
-    float* stash = delta_l + kRetrWaves * kRetrQ;                          // [waves][8][64] scores
+    float* tau_l = reinterpret_cast<float*>(shm + G::NST * G::TILE);      // [waves][QW queries]
+    uint32_t* cnt_l = reinterpret_cast<uint32_t*>(tau_l + G::W * QW);   // [waves][QW]
+    float* smin_l = reinterpret_cast<float*>(cnt_l + G::W * QW);        // [waves][QW]
+    float* delta_l = smin_l + G::W * QW;                                 // [waves][QW]
+    float* stash = delta_l + G::W * QW;                              // [waves][8][64] scores
+    uint2* queue = reinterpret_cast<uint2*>(stash + G::W * kRetrStashRegs * 64);   // [waves][kRetrQueue]
+    static_assert(QW <= 64, "a queue entry holds the query in 6 bits");
     const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
 
     // (split, query group) from the block index so that the query groups of
@@ -147,120 +171,190 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
     const int split = (slot / a.n_qgroups) * 8 + xcd, qgroup = slot % a.n_qgroups;
     if (split >= a.n_splits) return;
-    const int q0 = qgroup * (kRetrWaves * kRetrQ) + wave * kRetrQ;
+    const int q0 = qgroup * (G::W * QW) + wave * QW;
     const KeyRange rr = split_range(a.N, a.n_splits, split, kRetrRows);
     const int r_lo = rr.lo, r_hi = rr.hi;
     const int ntiles = (r_hi > r_lo) ? (r_hi - r_lo + kRetrRows - 1) / kRetrRows : 0;
     if (ntiles == 0) return;
 
-    HalfRow<DT_BF16, D> qf;
-    load_qblock<D>(qf, a, q0);
+    // the wave's query blocks: every database-row fragment read from LDS feeds
+    // one MFMA per block
+    HalfRow<DT_BF16, D> qf[kRetrQB];
+#pragma unroll
+    for (int b = 0; b < kRetrQB; ++b) load_qblock<D>(qf[b], a, q0 + b * kRetrQ);
     drain_vm_loads();
     const Meta* meta = reinterpret_cast<const Meta*>(a.meta);
 
-    // thresholds of the wave's 32 queries: lane i < 32 owns query q0 + i
+    // thresholds of the wave's queries: lane i owns query q0 + i
     int thr_own = 0;
     Meta m_own{0.0f, 1.0f, 0, 0};
-    const bool own_valid = lane < 32 && q0 + lane < a.T;
+    const bool own_lane = lane < QW;
+    const bool own_valid = own_lane && q0 + lane < a.T;
     if (own_valid) {
         m_own = meta[q0 + lane];
         thr_own = m_own.thr0;
     }
-    float* my_tau = tau_l + wave * kRetrQ;
-    uint32_t* my_cnt = cnt_l + wave * kRetrQ;
-    if (lane < 32) {
+    float* my_tau = tau_l + wave * QW;
+    uint32_t* my_cnt = cnt_l + wave * QW;
+    if (own_lane) {
         my_tau[lane] = own_valid ? initial_gate(thr_own, m_own, a.nbins, a.topk) : INFINITY;
         my_cnt[lane] = 0u;
-        smin_l[wave * kRetrQ + lane] = m_own.smin;
-        delta_l[wave * kRetrQ + lane] = m_own.delta;
+        smin_l[wave * QW + lane] = m_own.smin;
+        delta_l[wave * QW + lane] = m_own.delta;
     }
     uint2* cand_base = a.cand + (size_t)split * a.cap_s;   // + q * ccap: this split's slice of query q
-    float tau[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) tau[r] = my_tau[reg_query(0, r, half)];
+    // query (of the wave) of score register R: block R / 16, row of register R % 16
+    auto rq = [&](int R) { return (R >> 4) * kRetrQ + reg_query(0, R & 15, half); };
     int added = 0;   // candidates this wave added since its last refresh (wave-uniform)
 
+    uint32_t loff[G::LPW];
+#pragma unroll
+    for (int j = 0; j < G::LPW; ++j) loff[j] = retr_part_off<D>(wave, lane, j);
     constexpr int LEAD = G::NST - 1;   // tiles requested ahead of the one computed
 #pragma unroll
-    for (int j = 0; j < LEAD; ++j)
-        if (j < ntiles) retr_load_tile<D>(a, r_lo + j * kRetrRows, tiles + j * G::TILE, wave, lane);
+    for (int t = 0; t < LEAD; ++t)
+        if (t < ntiles) {
+            const TileSrc src = retr_tile_src<D>(a, r_lo + t * kRetrRows);
+#pragma unroll
+            for (int j = 0; j < G::LPW; ++j) retr_load_part<D>(src, loff[j], tiles + t * G::TILE, wave, j);
+        }
+    // The wave's queued candidates: each lane takes one entry, claims a slot
+    // of the query's slice with an LDS atomic, writes it and adds to the
+    // shared histograms without waiting for a reply.
+    uint2* my_q = queue + wave * kRetrQueue;
+    int qn = 0;       // queued entries (wave-uniform)
+    int vm_now = 0;   // vector-memory instructions the flushes of this tile issued (a lower bound)
+    auto flush = [&]() {
+        for (int b0 = 0; b0 < qn; b0 += 64) {
+            if (b0 + lane < qn) {
+                const uint2 e = my_q[b0 + lane];
+                const int ql = (int)(e.y & 63u);
+                const int q = q0 + ql;
+                const uint32_t p = atomicAdd(&my_cnt[ql], 1u);
+                if ((int64_t)p < a.cap_s) cand_base[(size_t)q * a.ccap + p] = make_uint2((uint32_t)r_lo + (e.y >> 6), e.x);
+                const int b = bin_of(__uint_as_float(e.x), smin_l[wave * QW + ql], delta_l[wave * QW + ql], a.nbins);
+                atomicAdd(&a.hist_g[(size_t)q * a.nbins + b], 1u);
+                atomicAdd(&a.hist_c[(size_t)q * a.nsuper + b / kSuperBins], 1u);
+            }
+            vm_now += 2;   // two atomics per round (some lane is active)
+        }
+        qn = 0;
+    };
     int sbuf = 0;   // stage of tile `it`
+    int vm_prev1 = 0, vm_prev2 = 0;   // vector-memory instructions of the last two tiles' candidate paths
     for (int it = 0; it < ntiles; ++it) {
-        // tiles it+1 .. it+LEAD-1 (those that exist) may still be loading
+        // Wait for this tile's loads only: the loads of tiles it+1 .. it+LEAD-1
+        // (those that exist) may still be in flight, and so may the
+        // vector-memory instructions the last two tiles' candidate flushes
+        // issued after this tile's loads (vm_prev1 + vm_prev2 is a lower bound
+        // of their count).
         const int later = min(LEAD - 1, ntiles - 1 - it);
         if (later <= 0) wait_vm<0>();
-        else if (later == 1) wait_vm<G::LPW>();
-        else wait_vm<2 * G::LPW>();
+        else if (later == 1) wait_vm_plus<G::LPW>(vm_prev1 + vm_prev2);
+        else wait_vm_plus<2 * G::LPW>(vm_prev1 + vm_prev2);
         __syncthreads();   // every wave's share of tile `it` has landed; the stage of tile it-1 is free
         // the loads of tile it+LEAD go out spread over this tile's MFMAs (below):
         // issued back to back they hold the wave at the memory pipe before its
         // MFMAs.  They go out unconditionally (no branch between the MFMAs): past
         // the last tile they re-read clamped rows into a stage nothing reads, and
         // being the newest loads they never loosen the waits above.
-        const int row_next = r_lo + (it + LEAD) * kRetrRows;
+        const TileSrc src_next = retr_tile_src<D>(a, r_lo + (it + LEAD) * kRetrRows);
         uint8_t* st_next = tiles + ((sbuf + LEAD) % G::NST) * G::TILE;
         const uint8_t* st = tiles + sbuf * G::TILE;
         sbuf = (sbuf + 1) % G::NST;
-        const int rr = lane & 31;
-        const int row = r_lo + it * kRetrRows + rr;
-        // B fragments read from LDS four steps ahead of their MFMA; the
-        // scheduling barriers keep the compiler from hoisting every read (the
-        // 32 query rows already hold 2*D bytes of registers per lane)
-        const uint8_t* rowp = st + rr * G::RB;
-        const int sw = chunk_swz<G::RB, G::CPR>(rr);
+        const int rrow = lane & 31;
+        const int row = r_lo + it * kRetrRows + rrow;
+        // B fragments read from LDS two steps ahead of their MFMAs (the other
+        // wave of the SIMD covers the rest of the latency); the
+        // scheduling barriers keep the compiler from hoisting every read
+        const uint8_t* rowp = st + rrow * G::RB;
+        const int sw = chunk_swz<G::RB, G::CPR>(rrow);
+        // When the half-row offset is a multiple of the swizzle span, the XOR
+        // only touches the low bits of s: one XOR with a constant per read and
+        // an immediate offset.  The XOR is opaque to the compiler (volatile
+        // asm), which would otherwise keep one address register per step.
+        constexpr int SPAN = G::CPR < 16 ? G::CPR : 16;
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+        const uint32_t lbase =
+            (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(rowp + half * (G::CPR / 2) * 16);
+        const uint32_t sw16 = (uint32_t)sw * 16u;
         auto rd = [&](int s) {
-            return *reinterpret_cast<const u32x4*>(rowp + (((half * (G::CPR / 2) + s) ^ sw) * 16));
+            if constexpr ((G::CPR / 2) % SPAN == 0) {
+                uint32_t x;
+                asm volatile("v_xor_b32 %0, %1, %2" : "=v"(x) : "n"((s & (SPAN - 1)) * 16), "v"(sw16));
+                return *(reinterpret_cast<lds_u32x4*>((uintptr_t)(lbase + x)) + (s & ~(SPAN - 1)));
+            } else {
+                return *reinterpret_cast<const u32x4*>(rowp + (((half * (G::CPR / 2) + s) ^ sw) * 16));
+            }
         };
-        constexpr int PF = G::KSTEPS < 4 ? G::KSTEPS : 4;
+        constexpr int PF = G::KSTEPS < 2 ? G::KSTEPS : 2;
         u32x4 bq[PF];
 #pragma unroll
         for (int s = 0; s < PF; ++s) bq[s] = rd(s);
-        v16f acc = v16f{};
+        v16f acc[kRetrQB];
+#pragma unroll
+        for (int b = 0; b < kRetrQB; ++b) acc[b] = v16f{};
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
-            constexpr int LSTEP = G::KSTEPS / G::LPW;   // MFMAs between this wave's tile loads
-            if (s % LSTEP == 0 && s / LSTEP < G::LPW) retr_load_part<D>(a, row_next, st_next, wave, lane, s / LSTEP);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf.v[s]),
-                                                          __builtin_bit_cast(bf16x8, bq[s % PF]), acc, 0, 0, 0);
+            constexpr int LSTEP = G::KSTEPS / G::LPW;   // MFMA steps between this wave's tile loads
+            if (s % LSTEP == 0 && s / LSTEP < G::LPW)
+            {
+                int ln;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+                retr_load_part<D>(src_next, retr_part_off<D>(wave, ln, s / LSTEP), st_next, wave, s / LSTEP);
+            }
+#pragma unroll
+            for (int b = 0; b < kRetrQB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qf[b].v[s]),
+                                                                 __builtin_bit_cast(bf16x8, bq[s % PF]), acc[b], 0, 0, 0);
             if (s + PF < G::KSTEPS) bq[s % PF] = rd(s + PF);
             if (s % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
         }
-        // gate: bit r of pm is set when the score in accumulator register r
-        // reaches its query's threshold
         // gate: one compare per register into a wave mask (scalar ORs); the
-        // per-lane mask of passing registers (bit r of pm) only when some pass
+        // per-lane mask of passing registers (bit R of pm) only when some pass
+        // (thresholds read from LDS: four queries' in one 16-byte read)
+        float tau[NR];
+#pragma unroll
+        for (int R = 0; R < NR; R += 4) {
+            const float4 t4 = *reinterpret_cast<const float4*>(my_tau + rq(R));
+            tau[R] = t4.x; tau[R + 1] = t4.y; tau[R + 2] = t4.z; tau[R + 3] = t4.w;
+        }
+        vm_now = 0;
         uint64_t any = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) any |= __ballot(acc[r] >= tau[r]);
-        if (any & __ballot(row < r_hi)) {
+        for (int R = 0; R < NR; ++R) any |= __builtin_amdgcn_ballot_w64(acc[R >> 4][R & 15] >= tau[R]);
+        if (any & __builtin_amdgcn_ballot_w64(row < r_hi)) {
             const bool rv = row < r_hi;
             uint32_t pm = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) pm |= (rv && acc[r] >= tau[r]) ? (1u << r) : 0u;
-            // candidates (most tiles hold one or two): every lane walks only its
-            // own passing registers, reading their scores back from a wave-private
-            // LDS copy (dynamic register index), taking a slot of the query's
-            // slice with an LDS atomic and adding to the shared histograms
-            // without waiting for a reply
+            for (int R = 0; R < NR; ++R) pm |= (rv && acc[R >> 4][R & 15] >= tau[R]) ? (1u << R) : 0u;
+            // candidates (a few per tile once the thresholds have risen): each
+            // round every lane with passing registers appends its lowest one
+            // to the wave's queue in LDS (score read back from a wave-private
+            // copy of 8 registers, position from the round's ballot); full
+            // queues are flushed 64 entries per instruction, so the vector-memory
+            // traffic per tile stays a few instructions, not three per candidate
             float* sv = stash + wave * kRetrStashRegs * 64;
 #pragma unroll
-            for (int rb = 0; rb < 16; rb += kRetrStashRegs) {
+            for (int rb = 0; rb < NR; rb += kRetrStashRegs) {
                 uint32_t pr = (pm >> rb) & ((1u << kRetrStashRegs) - 1u);
                 if (__ballot(pr != 0u)) {
 #pragma unroll
-                    for (int r = 0; r < kRetrStashRegs; ++r) sv[r * 64 + lane] = acc[rb + r];
-                    while (pr) {
-                        const int reg = rb + __ffs(pr) - 1;
-                        pr &= pr - 1u;
-                        const float I = sv[(reg - rb) * 64 + lane];
-                        const int ql = reg_query(0, reg, half);
-                        const int q = q0 + ql;
-                        const uint32_t p = atomicAdd(&my_cnt[ql], 1u);
-                        if ((int64_t)p < a.cap_s)
-                            cand_base[(size_t)q * a.ccap + p] = make_uint2((uint32_t)row, __float_as_uint(I));
-                        const int b = bin_of(I, smin_l[wave * kRetrQ + ql], delta_l[wave * kRetrQ + ql], a.nbins);
-                        atomicAdd(&a.hist_g[(size_t)q * a.nbins + b], 1u);
-                        atomicAdd(&a.hist_c[(size_t)q * a.nsuper + b / kSuperBins], 1u);
+                    for (int r = 0; r < kRetrStashRegs; ++r) sv[r * 64 + lane] = acc[(rb + r) >> 4][(rb + r) & 15];
+                    while (true) {
+                        const uint64_t m = __ballot(pr != 0u);
+                        if (!m) break;
+                        const int n = __popcll(m);
+                        if (qn + n > kRetrQueue) flush();
+                        if (pr) {
+                            const int reg = rb + __ffs(pr) - 1;
+                            pr &= pr - 1u;
+                            const uint32_t pos = (uint32_t)qn + __builtin_amdgcn_mbcnt_hi(
+                                (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                            my_q[pos] = make_uint2(__float_as_uint(sv[(reg - rb) * 64 + lane]),
+                                                   ((uint32_t)(row - r_lo) << 6) | (uint32_t)rq(reg));
+                        }
+                        qn += n;
                     }
                 }
             }
@@ -272,6 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // the wave's thresholds -- plain stores that can only raise them.
         // Every counter read is at most the number of real rows in its bin, so
         // the new threshold bin is at most the true one.
+        if (qn >= 64 || (qn > 0 && added >= kRetrRefreshCands)) flush();
         if (added >= kRetrRefreshCands) {
             added = 0;
             int nt = thr_own;
@@ -317,11 +412,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     thr_own = nt;
                     my_tau[lane] = tau_of(thr_own, m_own.smin, m_own.delta, a.nbins);
                 }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tau[r] = my_tau[reg_query(0, r, half)];
             }
         }
+        vm_prev2 = vm_prev1;
+        vm_prev1 = min(vm_now, 64);
     }
+    flush();
     wait_vm<0>();   // loads issued past the last tile land before the workgroup ends
     // candidates this split found for each of the wave's queries (may exceed the slice)
     if (own_valid) a.seg_cnt[(size_t)(q0 + lane) * a.n_splits + split] = my_cnt[lane];
@@ -466,7 +562,7 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int nsplit_pad = (a.n_splits + 7) / 8 * 8;
     if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-    retr_scan_kernel<D><<<nsplit_pad * a.n_qgroups, kRetrWaves * 64, lds, st>>>(a);
+    retr_scan_kernel<D><<<nsplit_pad * a.n_qgroups, G::W * 64, lds, st>>>(a);
     if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t compact_lds = (size_t)kCompactStage * 8 + ((size_t)a.n_splits + 1) * 4;
