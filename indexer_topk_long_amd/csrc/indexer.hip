@@ -261,47 +261,60 @@ __device__ __forceinline__ int group_key_end(const IdxArgs& a, int t0) {
 // fp8 linear term: operands per query, and its products outside the scan
 // ---------------------------------------------------------------------------
 
-// One wave per query: q''/2 = sum_h (w'_h / 2) q_h over the query's heads in
-// head order (w' = sigma_q w as the head sum uses it), then four fp8 parts of
+// One workgroup of 256 threads per query: q''/2 = sum_h (w'_h / 2) q_h over
+// the query's heads (w' = sigma_q w as the head sum uses it), each thread
+// summing 4 dimensions over every (256 / (D/4))-th head from one 32-bit load
+// per head, the head groups then added in LDS; then four fp8 parts of
 // (q''/2) * S with S = 2^(8 - e) putting the largest magnitude in [128, 256),
 // each part taking the residue of the ones before it times 16.  Every fp8
 // pass reads these same bytes, so all of them get the same linear term.
 template <int D>
-__global__ __launch_bounds__(64) void qlin_kernel(IdxArgs a) {
-    constexpr int DPL = D / 64;   // dimensions per lane
-    const int t = blockIdx.x, lane = lane_id();
+__global__ __launch_bounds__(256) void qlin_kernel(IdxArgs a) {
+    constexpr int NQ = D / 4;          // 4-dimension groups
+    constexpr int HG = 256 / NQ;       // head groups
+    __shared__ float part[HG][D];
+    __shared__ float wmax[4];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int dq = tid % NQ, hg = tid / NQ;
     const float sq = a.q_scale[t];
     const uint8_t* q = a.q + (size_t)t * a.H * D;
     const float* w = a.w + (size_t)t * a.H;
-    float acc[DPL];
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
-    for (int h = 0; h < a.H; ++h) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int h = hg; h < a.H; h += HG) {
         const float c = (sq * w[h]) * 0.5f;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i)
-            acc[i] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)q[(size_t)h * D + lane + 64 * i], 0), acc[i]);
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(q + (size_t)h * D + 4 * dq);
+        acc[0] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 0), acc[0]);
+        acc[1] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 1), acc[1]);
+        acc[2] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 2), acc[2]);
+        acc[3] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 3), acc[3]);
     }
-    float mx = 0.0f;
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) mx = fmaxf(mx, fabsf(acc[i]));
-    mx = wave_max_f32(mx);
+    for (int i = 0; i < 4; ++i) part[hg][4 * dq + i] = acc[i];
+    __syncthreads();
+    float x = 0.0f;
+    if (tid < D) {
+#pragma unroll
+        for (int g = 0; g < HG; ++g) x += part[g][tid];
+    }
+    float mx = wave_max_f32(tid < D ? fabsf(x) : 0.0f);
+    if (lane == 0) wmax[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     int e = 0;
     if (mx > 0.0f) frexpf(mx, &e);   // mx in [2^(e-1), 2^e)
     e = max(-100, min(e, 100));      // keeps S and 1/S finite and normal
-    const float S = ldexpf(1.0f, 8 - e);
-    uint8_t* out = a.qlin + (size_t)t * 4 * D;
-#pragma unroll
-    for (int i = 0; i < DPL; ++i) {
-        float r = acc[i] * S;   // exact: a power of two
+    if (tid < D) {
+        uint8_t* out = a.qlin + (size_t)t * 4 * D;
+        float r = x * ldexpf(1.0f, 8 - e);   // exact: a power of two
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false) & 0xffu;
-            out[p * D + lane + 64 * i] = (uint8_t)code;
+            out[p * D + tid] = (uint8_t)code;
             r = (r - __builtin_amdgcn_cvt_f32_fp8((int)code, 0)) * 16.0f;   // exact residue, scaled
         }
     }
-    if (lane == 0) a.qinv[t] = ldexpf(1.0f, e - 8);
+    if (tid == 0) a.qinv[t] = ldexpf(1.0f, e - 8);
 }
 
 // 32 fp8 values of row `row` (D bytes), dimensions [32 ks, 32 ks + 32); zero
@@ -380,71 +393,12 @@ __device__ __forceinline__ float lin_one64_t(const LinFrag& aq, const uint8_t* k
 // Sample: score the de-duplicated sample keys
 // ---------------------------------------------------------------------------
 
-template <int DT, int D, int HB>
-__global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
-    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
-    const int qg = blockIdx.x / a.s_splits, sp = blockIdx.x % a.s_splits;
-    const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
-    const int nu = (int)*a.nu;
-    if (nu == 0) return;
-    const int nblk = (nu + 31) / 32;
-    const int per = (nblk + a.s_splits - 1) / a.s_splits;
-    const int b0 = sp * per, b1 = min(nblk, b0 + per);
-    if (b0 >= b1) return;
-    QueryRegs<DT, D, HB> ra, rb;
-    load_query<DT, D, HB>(ra, a, ta);
-    load_query<DT, D, HB>(rb, a, tb);
-    const int t = half ? tb : ta;
-    LinPair lp;
-    if constexpr (DT == DT_FP8) load_lin_pair<D>(lp, a, ta, tb);
-    if constexpr (HalfRow<DT, D>::NV > 4) {
-        // wide fragments: no room for a second one
-        for (int blk = b0; blk < b1; ++blk) {
-            const int j = blk * 32 + (lane & 31);
-            const int key = a.sample_u[min(j, nu - 1)];
-            HalfRow<DT, D> kf;
-            load_key<DT, D>(kf, a.k, key);
-            float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
-            if constexpr (DT == DT_FP8) I = I * a.k_scale[key];
-            if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
-        }
-        return;
-    }
-    // the next block's key rows (and the one after's key indices) are in
-    // flight while a block is scored
-    auto key_at = [&](int blk) { return a.sample_u[min(blk * 32 + (lane & 31), nu - 1)]; };
-    int key = key_at(b0);
-    int key2 = (b0 + 1 < b1) ? key_at(b0 + 1) : key;
-    HalfRow<DT, D> kf;
-    load_key<DT, D>(kf, a.k, key);
-    float ks = (DT == DT_FP8) ? a.k_scale[key] : 1.0f;
-    for (int blk = b0; blk < b1; ++blk) {
-        const int j = blk * 32 + (lane & 31);
-        const HalfRow<DT, D> cur = kf;
-        const float cks = ks;
-        const int ckey = key;
-        if (blk + 1 < b1) {
-            key = key2;
-            load_key<DT, D>(kf, a.k, key);
-            if constexpr (DT == DT_FP8) ks = a.k_scale[key];
-            if (blk + 2 < b1) key2 = key_at(blk + 2);
-        }
-        float I = score_2slots<DT, D, HB>(ra, cur, rb, cur);
-        if constexpr (DT == DT_FP8) {
-            // the block's keys of columns (lane & 15) and 16 + (lane & 15)
-            const int kA = __shfl(ckey, lane & 15), kB = __shfl(ckey, 16 + (lane & 15));
-            I = lin_score(lin_pair_t<D>(lp, a.k, kA, kB), lp.inv, I, cks);
-        }
-        if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
-    }
-}
-
-// Sample statistics of one query: valid sample keys (<= pos), range, delta,
-// histogram and the initial threshold bin.
-__global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
-    extern __shared__ uint32_t sh[];  // [nbins]
+// Sample statistics of query t: valid sample keys (<= pos), range, delta,
+// histogram and the initial threshold bin.  All 256 threads of the
+// workgroup call it together (it synchronises them); sh holds nbins words.
+__device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
     __shared__ float s_min[4], s_max[4];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     const int nu = (int)*a.nu;
     __shared__ uint32_t s_nv[4];
     const int pos_t = a.pos ? min(a.pos[t], a.L - 1) : a.L - 1;   // no positions: every key is valid
@@ -522,6 +476,76 @@ __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
             reinterpret_cast<Meta*>(a.meta)[t] = m;
         }
     }
+    __syncthreads();   // sh and the partials are free for the next query
+}
+
+__global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
+    extern __shared__ uint32_t sh[];  // [nbins]
+    sample_stats_query(a, blockIdx.x, sh);
+}
+
+template <int DT, int D, int HB>
+__device__ __forceinline__ void sample_score_part(const IdxArgs& a, int qg, int sp) {
+    const int wave = threadIdx.x >> 6, lane = lane_id(), half = lane >> 5;
+    const int ta = qg * kQPG + 2 * wave, tb = ta + 1;
+    const int nu = (int)*a.nu;
+    if (nu == 0) return;
+    const int nblk = (nu + 31) / 32;
+    const int per = (nblk + a.s_splits - 1) / a.s_splits;
+    const int b0 = sp * per, b1 = min(nblk, b0 + per);
+    if (b0 >= b1) return;
+    QueryRegs<DT, D, HB> ra, rb;
+    load_query<DT, D, HB>(ra, a, ta);
+    load_query<DT, D, HB>(rb, a, tb);
+    const int t = half ? tb : ta;
+    LinPair lp;
+    if constexpr (DT == DT_FP8) load_lin_pair<D>(lp, a, ta, tb);
+    if constexpr (HalfRow<DT, D>::NV > 4) {
+        // wide fragments: no room for a second one
+        for (int blk = b0; blk < b1; ++blk) {
+            const int j = blk * 32 + (lane & 31);
+            const int key = a.sample_u[min(j, nu - 1)];
+            HalfRow<DT, D> kf;
+            load_key<DT, D>(kf, a.k, key);
+            float I = score_2slots<DT, D, HB>(ra, kf, rb, kf);
+            if constexpr (DT == DT_FP8) I = I * a.k_scale[key];
+            if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
+        }
+        return;
+    }
+    // the next block's key rows (and the one after's key indices) are in
+    // flight while a block is scored
+    auto key_at = [&](int blk) { return a.sample_u[min(blk * 32 + (lane & 31), nu - 1)]; };
+    int key = key_at(b0);
+    int key2 = (b0 + 1 < b1) ? key_at(b0 + 1) : key;
+    HalfRow<DT, D> kf;
+    load_key<DT, D>(kf, a.k, key);
+    float ks = (DT == DT_FP8) ? a.k_scale[key] : 1.0f;
+    for (int blk = b0; blk < b1; ++blk) {
+        const int j = blk * 32 + (lane & 31);
+        const HalfRow<DT, D> cur = kf;
+        const float cks = ks;
+        const int ckey = key;
+        if (blk + 1 < b1) {
+            key = key2;
+            load_key<DT, D>(kf, a.k, key);
+            if constexpr (DT == DT_FP8) ks = a.k_scale[key];
+            if (blk + 2 < b1) key2 = key_at(blk + 2);
+        }
+        float I = score_2slots<DT, D, HB>(ra, cur, rb, cur);
+        if constexpr (DT == DT_FP8) {
+            // the block's keys of columns (lane & 15) and 16 + (lane & 15)
+            const int kA = __shfl(ckey, lane & 15), kB = __shfl(ckey, 16 + (lane & 15));
+            I = lin_score(lin_pair_t<D>(lp, a.k, kA, kB), lp.inv, I, cks);
+        }
+        if (t < a.T && j < nu) a.sscore[(size_t)t * a.n_sample + j] = I;
+    }
+}
+
+// Sample scores of a query group's queries, split over s_splits workgroups.
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
+    sample_score_part<DT, D, HB>(a, blockIdx.x / a.s_splits, blockIdx.x % a.s_splits);
 }
 
 // ---------------------------------------------------------------------------
@@ -1709,7 +1733,7 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
-        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
+        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
         sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
         sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
         auto run_scan = [&](const IdxArgs& args) { return run_scan_variant<DT_, D_, HB_, false>(args, st); };
@@ -1749,7 +1773,7 @@ hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipSt
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
-        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 64, 0, st>>>(a);
+        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
         if (!run_scan_variant<DT_, D_, HB_, true>(a, st)) { err = hipErrorInvalidValue; return; }
         const size_t lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
         allow_lds(unfused_select_kernel, lds);
