@@ -127,6 +127,32 @@ def _retrieval_run(ltk, torch, q, db, k, smp, steps, warmup):
     return ms, scan_ms, st
 
 
+def retrieval_cpu_baseline(r, db, topk: int, n_rows: int = 256, n_db: int = 1 << 20):
+    """The CPU oracle, as it stands, on n_rows evenly spaced queries against
+    the first n_db database rows (copied to the host); the pairs/s rate
+    extrapolates to the whole workload."""
+    import torch
+    from oracle import oracle_retrieval
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    T = r["T"]
+    n_db = min(n_db, db.shape[0])
+    rows = np.linspace(0, T - 1, n_rows).astype(np.int64)
+    dbh = db[:n_db].view(torch.int16).cpu().numpy().view(np.uint16)
+    qh = np.ascontiguousarray(r["q"][rows])
+    t0 = time.perf_counter()
+    oracle_retrieval(qh, dbh, topk)
+    dt = time.perf_counter() - t0
+    pairs = n_rows * n_db
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} of {T} queries (evenly spaced) against the first {n_db} of {db.shape[0]} "
+                      f"database rows: {pairs} pairs in {dt:.2f} s, fp64 numpy including the fp64 decode; "
+                      f"extrapolated to the workload"}
+
+
 def bench_retrieval(args):
     """Separate line: the 8M x 768 bf16 retrieval workload (k = 1,024, random 3,072-row sample).
 
@@ -181,6 +207,9 @@ def bench_retrieval(args):
                                           if args.sweep_sample == "earlier" else "3k seeded-random rows"),
                            "pairs": T * N},
                 "roofline": best["roofline"], "sweep": rows, "cpu_baseline": None}
+        if not args.no_cpu_baseline:
+            log("  timing the CPU oracle ...")
+            line["cpu_baseline"] = retrieval_cpu_baseline(r, r["db"], rows[-1]["topk"])
         print(json.dumps(line), flush=True)
         return
 
@@ -198,6 +227,28 @@ def bench_retrieval(args):
             "roofline": roofline(scan_ms, traffic),
             "candidates_per_query": round(st.cand_written / T, 1), "max_candidates": st.max_cand_per_query,
             "overflow_rows": st.overflow_rows, "cpu_baseline": None}
+    if args.unfused_steps > 0:
+        # the unfused comparison path: the full T x N fp32 matrix, then a radix select per row
+        log(f"  unfused retrieval ({T * N * 4 / 1e9:.1f} GB score matrix) ...")
+        uws = torch.empty(ltk.workspace_bytes(ltk.KIND_UNFUSED_RETRIEVE, T, 1, D, N, k, 0, 1), dtype=torch.uint8,
+                          device="cuda")
+        uout = ltk.unfused_retrieve(q, r["db"], k, workspace=uws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.unfused_steps):
+            ltk.unfused_retrieve(q, r["db"], k, workspace=uws)
+        torch.cuda.synchronize()
+        ums = (time.perf_counter() - t0) * 1e3 / args.unfused_steps
+        fout = ltk.retrieve(q, r["db"], k, sample=smp)
+        same = bool(torch.equal(torch.sort(uout, dim=1).values, torch.sort(fout, dim=1).values))
+        line["unfused_baseline"] = {"ms_per_step": round(ums, 3), "value": pairs / (ums * 1e-3), "unit": "pairs/s",
+                                    "speedup_of_fused": round(ums / ms, 2), "bytes_written": T * N * 4 + T * k * 4,
+                                    "same_index_sets_as_fused": same}
+        log(f"  unfused: {ums:.3f} ms/step ({ums / ms:.2f}x the fused step), same sets: {same}")
+        del uws, uout, fout
+    if not args.no_cpu_baseline:
+        log("  timing the CPU oracle ...")
+        line["cpu_baseline"] = retrieval_cpu_baseline(r, r["db"], k)
     print(json.dumps(line), flush=True)
 
 

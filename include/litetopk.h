@@ -61,7 +61,8 @@ typedef enum {
     LTK_KIND_SCORE_SELECT = 0,   /* litetopk_score_select */
     LTK_KIND_RETRIEVE = 1,       /* litetopk_retrieve */
     LTK_KIND_UNFUSED = 2,        /* litetopk_unfused_score_select */
-    LTK_KIND_NEXT_SAMPLE = 3     /* litetopk_next_sample */
+    LTK_KIND_NEXT_SAMPLE = 3,    /* litetopk_next_sample */
+    LTK_KIND_UNFUSED_RETRIEVE = 4  /* litetopk_unfused_retrieve */
 } ltk_kind;
 
 /* Tuning options (HOST struct).  Pass NULL for the defaults; a zero field
@@ -184,6 +185,19 @@ int litetopk_unfused_score_select(const void* q, const float* q_scale, const voi
                                   int32_t T, int32_t H, int32_t D, int64_t L, int32_t dtype,
                                   int32_t topk, int32_t* out_idx, float* out_score, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Unfused comparison path of retrieval (the same decoupled pipeline as
+ * litetopk_unfused_score_select, for the inner-product score): the T x N
+ * fp32 score matrix is written to the workspace, then each row is
+ * radix-selected.  Arguments and result as litetopk_retrieve without the
+ * sample and statistics; opts may set sorted_output and l_splits (others are
+ * ignored).  ws_bytes >= litetopk_workspace_bytes(LTK_KIND_UNFUSED_RETRIEVE,
+ * T, 1, D, N, topk, 0, dtype, NULL) = 4 T N bytes rounded up to 256 (33 GB
+ * for 1,024 queries over 8M rows).  The scores are bit-identical to the
+ * fused path's (same products in the same order). */
+int litetopk_unfused_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N,
+                              int32_t dtype, int32_t topk, int32_t* out_idx, float* out_score,
+                              void* ws, size_t ws_bytes, const ltk_opts* opts, void* stream);
 
 /* Sample for the next chunk (LiteTopK pages, "Sampling": the previous
  * chunk's top-3k tokens are reused as the next chunk's sample).  Ranks the

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     KIND_RETRIEVE,
     KIND_SCORE_SELECT,
     KIND_UNFUSED,
+    KIND_UNFUSED_RETRIEVE,
     HipEvents,
     LtkError,
     Opts,
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     score_select,
     score_select_static,
     strerror,
+    unfused_retrieve,
     unfused_score_select,
     workspace_bytes,
 )
@@ -36,5 +38,5 @@ from .prefill import next_sample, prefill_chunked, prefill_workspace_bytes  # no
 __all__ = [
     "score_select", "retrieve", "unfused_score_select", "workspace_bytes", "strerror", "device_check",
     "Opts", "Stats", "LtkError", "next_sample", "prefill_chunked", "library", "exported_symbols",
-    "dsa_pack", "dsa_gather", "prefill_workspace_bytes", "score_select_static",
+    "dsa_pack", "dsa_gather", "prefill_workspace_bytes", "score_select_static", "unfused_retrieve",
 ]

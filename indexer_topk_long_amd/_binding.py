@@ -8,7 +8,7 @@ from dataclasses import dataclass
 
 from .build import INCLUDE, lib_path
 
-KIND_SCORE_SELECT, KIND_RETRIEVE, KIND_UNFUSED, KIND_NEXT_SAMPLE = 0, 1, 2, 3
+KIND_SCORE_SELECT, KIND_RETRIEVE, KIND_UNFUSED, KIND_NEXT_SAMPLE, KIND_UNFUSED_RETRIEVE = 0, 1, 2, 3, 4
 _STATUS = {0: "LTK_OK", -1: "LTK_EINVAL", -2: "LTK_EUNSUPPORTED", -3: "LTK_EWORKSPACE", -4: "LTK_EHIP"}
 
 _c_i32, _c_i64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
@@ -84,6 +84,9 @@ def library() -> ctypes.CDLL:
         lib.litetopk_retrieve.restype = ctypes.c_int
         lib.litetopk_retrieve.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_p, _c_i32, _c_p,
                                           _c_p, _c_p, _c_sz, _c_p, _c_p, _c_p]
+        lib.litetopk_unfused_retrieve.restype = ctypes.c_int
+        lib.litetopk_unfused_retrieve.argtypes = [_c_p, _c_p, _c_i32, _c_i32, _c_i64, _c_i32, _c_i32, _c_p, _c_p,
+                                                  _c_p, _c_sz, _c_p, _c_p]
         lib.litetopk_strerror.restype = ctypes.c_char_p
         lib.litetopk_strerror.argtypes = [ctypes.c_int]
         lib.litetopk_device_check.restype = ctypes.c_int
@@ -301,13 +304,43 @@ def unfused_score_select(q, k, w, pos, topk: int, q_scale=None, k_scale=None, re
     return (out, osc) if return_scores else out
 
 
+def _check_retrieve_args(q, db):
+    _expect(q.dim() == 2 and db.dim() == 2, f"q must be [T, D] and db [N, D], got {tuple(q.shape)}, {tuple(db.shape)}")
+    _expect(q.dtype == db.dtype, f"q ({q.dtype}) and db ({db.dtype}) must share one dtype")
+    _expect(db.shape[1] == q.shape[1], f"db rows have {db.shape[1]} elements, q rows {q.shape[1]}")
+
+
+def unfused_retrieve(q, db, topk: int, opts: Opts | None = None, return_scores: bool = False, workspace=None):
+    """Unfused retrieval comparison path (litetopk_unfused_retrieve): the full
+    T x N score matrix in the workspace, then a radix select per row."""
+    import torch
+    _check_retrieve_args(q, db)
+    _same_device(q, db=db)
+    _dev(q, "q"), _dev(db, "db")
+    T, D = q.shape
+    N = db.shape[0]
+    dt = _dtype_code(q)
+    lib = library()
+    o = opts.c() if opts is not None else None
+    nbytes = lib.litetopk_workspace_bytes(KIND_UNFUSED_RETRIEVE, T, 1, D, N, topk, 0, dt, None)
+    if nbytes == 0:
+        raise LtkError(-1, "litetopk_workspace_bytes")
+    ws = _workspace(nbytes, q.device, workspace)
+    out = torch.empty((T, topk), dtype=torch.int32, device=q.device)
+    osc = torch.empty((T, topk), dtype=torch.float32, device=q.device) if return_scores else None
+    rc = lib.litetopk_unfused_retrieve(_ptr(q), _ptr(db), T, D, N, dt, topk, _ptr(out), _ptr(osc), _ptr(ws),
+                                       ws.numel() * ws.element_size(),
+                                       ctypes.byref(o) if o is not None else None, _stream())
+    if rc != 0:
+        raise LtkError(rc, "litetopk_unfused_retrieve")
+    return (out, osc) if return_scores else out
+
+
 def retrieve(q, db, topk: int, sample=None, opts: Opts | None = None, return_scores: bool = False,
              return_stats: bool = False, workspace=None):
     """Fused inner-product retrieval top-k (litetopk_retrieve); q [T, D], db [N, D] bfloat16."""
     import torch
-    _expect(q.dim() == 2 and db.dim() == 2, f"q must be [T, D] and db [N, D], got {tuple(q.shape)}, {tuple(db.shape)}")
-    _expect(q.dtype == db.dtype, f"q ({q.dtype}) and db ({db.dtype}) must share one dtype")
-    _expect(db.shape[1] == q.shape[1], f"db rows have {db.shape[1]} elements, q rows {q.shape[1]}")
+    _check_retrieve_args(q, db)
     if sample is not None:
         _expect(sample.dtype == torch.int32, f"sample must be int32, got {sample.dtype}")
     _same_device(q, db=db, sample=sample)

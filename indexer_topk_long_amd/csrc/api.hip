@@ -205,6 +205,10 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
         if (T < 0 || L < 1) return 0;
         return unfused_ws_bytes(T, L, dtype == LTK_FP8_E4M3FN ? D : 0);
     }
+    if (kind == LTK_KIND_UNFUSED_RETRIEVE) {
+        if (T < 0 || L < 1) return 0;
+        return unfused_matrix_bytes(T, L);
+    }
     if (kind == LTK_KIND_NEXT_SAMPLE) {
         if (L < 1 || L > (int64_t)0x7fffff00) return 0;
         return ns_layout(L).words * 4;
@@ -383,6 +387,47 @@ int litetopk_next_sample(const int32_t* prev_idx, int32_t T, int32_t topk, int64
     if (launch_next_sample(prev_idx, (size_t)T * (size_t)topk, (int)L, n_sample, out_sample,
                            static_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream)) != hipSuccess)
         return LTK_EHIP;
+    return LTK_OK;
+}
+
+int litetopk_unfused_retrieve(const void* q, const void* db, int32_t T, int32_t D, int64_t N, int32_t dtype,
+                              int32_t topk, int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                              const ltk_opts* opts, void* stream) {
+    if (T < 0 || N < 1 || N > (int64_t)0x7fffff00 || topk < 1 || topk > 65536) return LTK_EINVAL;
+    if (dtype != LTK_BF16) return dtype < LTK_F32 || dtype > LTK_FP8_E4M3FN ? LTK_EINVAL : LTK_EUNSUPPORTED;
+    if (D != 64 && D != 128 && D != 256 && D != 512 && D != 768) return LTK_EUNSUPPORTED;
+    if (T > 0 && (!q || !db || !out_idx || !ws)) return LTK_EINVAL;
+    if (!aligned16(q) || !aligned16(db) || !aligned16(ws)) return LTK_EINVAL;
+    Opts o;
+    int st;
+    if ((st = resolve_opts(opts, retrieve_default_ccap(topk), o)) != LTK_OK) return st;
+    if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
+    const int ns = retr_splits(T, D, N, o.l_splits);
+    if ((N + ns - 1) / ns > kRetrMaxSplitRows) return LTK_EINVAL;
+    if (ws_bytes < unfused_matrix_bytes(T, N)) return LTK_EWORKSPACE;
+    if (T == 0) return LTK_OK;
+    if ((st = device_check()) != LTK_OK) return st;
+    RetrArgs r{};
+    r.q = static_cast<const uint8_t*>(q);
+    r.db = static_cast<const uint8_t*>(db);
+    r.T = T;
+    r.N = (int)N;
+    r.topk = topk;
+    r.n_splits = ns;
+    r.n_qgroups = (T + retr_group_queries(D) - 1) / retr_group_queries(D);
+    r.S = static_cast<float*>(ws);
+    r.ev_scan_start = o.ev0;
+    r.ev_scan_stop = o.ev1;
+    IdxArgs sel{};
+    sel.T = T;
+    sel.L = (int)N;
+    sel.topk = topk;
+    sel.sorted = o.sorted;
+    sel.pos = nullptr;
+    sel.S = r.S;
+    sel.out_idx = out_idx;
+    sel.out_score = out_score;
+    if (launch_retrieve_unfused(D, r, sel, static_cast<hipStream_t>(stream)) != hipSuccess) return LTK_EHIP;
     return LTK_OK;
 }
 

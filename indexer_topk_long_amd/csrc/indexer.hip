@@ -1442,7 +1442,7 @@ __global__ __launch_bounds__(256) void unfused_select_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];
     const int t = blockIdx.x;
     MemSource src{a.S + (size_t)t * a.L};
-    const int nvalid = max(min(a.pos[t], a.L - 1) + 1, 0);
+    const int nvalid = a.pos ? max(min(a.pos[t], a.L - 1) + 1, 0) : a.L;   // no positions: every key
     int32_t* out = a.out_idx + (size_t)t * a.topk;
     float* osc = row_select_scores(a, t, sh);
     select_row(src, nvalid, a.topk, out, osc, sh);
@@ -1755,6 +1755,13 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStre
         err = hipGetLastError();
     });
     return ok ? err : hipErrorInvalidValue;
+}
+
+hipError_t launch_unfused_select(const IdxArgs& a, hipStream_t st) {
+    const size_t lds = row_select_lds(a.topk, a.sorted, a.out_score != nullptr);
+    allow_lds(unfused_select_kernel, lds);
+    unfused_select_kernel<<<a.T, 256, lds, st>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st) {

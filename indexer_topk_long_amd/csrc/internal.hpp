@@ -172,6 +172,7 @@ struct RetrArgs {
     uint32_t* hist_c;        // [T][nsuper] shared super-bin histograms
     uint32_t* seg_cnt;       // [T][n_splits] candidates each split found (zeroed before the scan)
     int64_t cap_s;           // candidate slots per (query, split): ccap / n_splits
+    float* S;                // unfused: [T, N] score matrix
     int32_t* out_idx;
     float* out_score;
     hipEvent_t ev_scan_start, ev_scan_stop;   // optional, recorded around the scan launch
@@ -190,6 +191,10 @@ inline size_t unfused_ws_bytes(int32_t T, int64_t L, int lin_d) {
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st);
 hipError_t launch_finalize(const IdxArgs& a, hipStream_t st);
 hipError_t launch_retrieve(int D, const RetrArgs& a, const IdxArgs& fin, hipStream_t st);
+// Unfused retrieval: the full score matrix (a.S), then the row select of sel
+// (sel.S = a.S, sel.pos = null: every row is valid).
+hipError_t launch_retrieve_unfused(int D, const RetrArgs& a, const IdxArgs& sel, hipStream_t st);
+hipError_t launch_unfused_select(const IdxArgs& a, hipStream_t st);
 constexpr int kDsaMaxEntries = 32768;   // G x k selections packed by one workgroup (LDS)
 constexpr int64_t kDsaMaxKeys = (int64_t)1 << 26;   // key << 5 | row fits 31 bits
 hipError_t launch_dsa_pack(const int32_t* idx, int T, int k, int L, int G, int32_t* shared, uint32_t* masks,

@@ -149,7 +149,10 @@ __device__ __forceinline__ uint32_t load_shared_count(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int D>
+// FULL: the unfused comparison path -- every score goes to the T x N matrix
+// a.S, with no sample, gate or candidates (the same MFMA order, so the same
+// fp32 scores as the fused scan).
+template <int D, bool FULL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void retr_scan_kernel(RetrArgs a) {
     using G = RetrGeom<D>;
     constexpr int QW = kRetrQB * kRetrQ;                                  // queries per wave
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     Meta m_own{0.0f, 1.0f, 0, 0};
     const bool own_lane = lane < QW;
     const bool own_valid = own_lane && q0 + lane < a.T;
-    if (own_valid) {
+    if (!FULL && own_valid) {
         m_own = meta[q0 + lane];
         thr_own = m_own.thr0;
     }
@@ -310,6 +313,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (s + PF < G::KSTEPS) bq[s % PF] = rd(s + PF);
             if (s % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (FULL) {
+#pragma unroll
+            for (int R = 0; R < NR; ++R) {
+                const int q = q0 + rq(R);
+                if (row < r_hi && q < a.T) a.S[(size_t)q * (size_t)a.N + row] = acc[R >> 4][R & 15];
+            }
+            continue;
+        }
         // gate: one compare per register into a wave mask (scalar ORs); the
         // per-lane mask of passing registers (bit R of pm) only when some pass
         // (thresholds read from LDS: four queries' in one 16-byte read)
@@ -417,10 +428,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         vm_prev2 = vm_prev1;
         vm_prev1 = min(vm_now, 64);
     }
-    flush();
+    if constexpr (!FULL) flush();
     wait_vm<0>();   // loads issued past the last tile land before the workgroup ends
     // candidates this split found for each of the wave's queries (may exceed the slice)
-    if (own_valid) a.seg_cnt[(size_t)(q0 + lane) * a.n_splits + split] = my_cnt[lane];
+    if (!FULL && own_valid) a.seg_cnt[(size_t)(q0 + lane) * a.n_splits + split] = my_cnt[lane];
 }
 
 // ---------------------------------------------------------------------------
@@ -558,11 +569,11 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
     if (e != hipSuccess) return e;
     const size_t lds = G::LDS;
     if (lds > 65536)
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_scan_kernel<D>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_scan_kernel<D, false>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int nsplit_pad = (a.n_splits + 7) / 8 * 8;
     if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
-    retr_scan_kernel<D><<<nsplit_pad * a.n_qgroups, G::W * 64, lds, st>>>(a);
+    retr_scan_kernel<D, false><<<nsplit_pad * a.n_qgroups, G::W * 64, lds, st>>>(a);
     if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t compact_lds = (size_t)kCompactStage * 8 + ((size_t)a.n_splits + 1) * 4;
@@ -577,6 +588,33 @@ static hipError_t launch_retrieve_d(const RetrArgs& a, const IdxArgs& fin, hipSt
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)fb_lds);
     retr_fallback_kernel<D><<<a.T, 256, fb_lds, st>>>(a);
     return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_retrieve_unfused_d(const RetrArgs& a, const IdxArgs& sel, hipStream_t st) {
+    using G = RetrGeom<D>;
+    const size_t lds = G::LDS;
+    if (lds > 65536)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(retr_scan_kernel<D, true>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const int nsplit_pad = (a.n_splits + 7) / 8 * 8;
+    if (a.ev_scan_start) (void)hipEventRecord(a.ev_scan_start, st);
+    retr_scan_kernel<D, true><<<nsplit_pad * a.n_qgroups, G::W * 64, lds, st>>>(a);
+    if (a.ev_scan_stop) (void)hipEventRecord(a.ev_scan_stop, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_unfused_select(sel, st);
+}
+
+hipError_t launch_retrieve_unfused(int D, const RetrArgs& a, const IdxArgs& sel, hipStream_t st) {
+    switch (D) {
+        case 64: return launch_retrieve_unfused_d<64>(a, sel, st);
+        case 128: return launch_retrieve_unfused_d<128>(a, sel, st);
+        case 256: return launch_retrieve_unfused_d<256>(a, sel, st);
+        case 512: return launch_retrieve_unfused_d<512>(a, sel, st);
+        case 768: return launch_retrieve_unfused_d<768>(a, sel, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_retrieve(int D, const RetrArgs& a, const IdxArgs& fin, hipStream_t st) {

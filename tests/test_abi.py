@@ -26,7 +26,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = ltk.exported_symbols()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
 
@@ -130,6 +130,34 @@ def _rt(L, **kw):
 ])
 def test_retrieve_argument_errors(L, kw, code):
     assert _rt(L, **kw) == code
+
+
+def test_retrieve_split_size_limit(L):
+    """An explicit split count that leaves more than 2^26 rows in a split is
+    rejected (a queue entry of the scan packs the row's offset in its split
+    in 26 bits); the automatic count respects the limit.  No queries: nothing
+    is launched."""
+    o = ltk.Opts(l_splits=1).c()
+    big = (1 << 26) + 1
+    f = L.litetopk_retrieve
+    assert f(A16, A16, 0, 128, big, BF16, 8, None, 0, A16, None, A16, 1 << 40, ctypes.byref(o), None, None) == EINVAL
+    o2 = ltk.Opts(l_splits=2).c()
+    assert f(A16, A16, 0, 128, big, BF16, 8, None, 0, A16, None, A16, 1 << 40, ctypes.byref(o2), None, None) == OK
+    assert f(A16, A16, 0, 128, big, BF16, 8, None, 0, A16, None, A16, 1 << 40, None, None, None) == OK
+    u = L.litetopk_unfused_retrieve
+    assert u(A16, A16, 0, 128, big, BF16, 8, A16, None, A16, 1 << 40, ctypes.byref(o), None) == EINVAL
+
+
+def test_unfused_retrieve_argument_errors(L):
+    u = L.litetopk_unfused_retrieve
+    need = L.litetopk_workspace_bytes(4, 4, 1, 128, 1000, 8, 0, BF16, None)   # LTK_KIND_UNFUSED_RETRIEVE
+    assert 4 * 1000 * 4 <= need < 4 * 1000 * 4 + 256                          # the T x N fp32 matrix
+    assert u(A16, A16, 4, 128, 1000, BF16, 8, A16, None, A16, need - 1, None, None) == EWS
+    assert u(A16, A16, 4, 128, 1000, FP8, 8, A16, None, A16, need, None, None) == EUNSUP
+    assert u(A16, A16, 4, 100, 1000, BF16, 8, A16, None, A16, need, None, None) == EUNSUP
+    assert u(A16, MIS, 4, 128, 1000, BF16, 8, A16, None, A16, need, None, None) == EINVAL
+    assert u(A16, A16, 4, 128, 0, BF16, 8, A16, None, A16, need, None, None) == EINVAL
+    assert u(A16, A16, 0, 128, 1000, BF16, 8, None, None, None, 0, None, None) == OK
 
 
 def test_unfused_and_next_sample_argument_errors(L):

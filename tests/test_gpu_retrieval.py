@@ -139,3 +139,40 @@ def test_retrieval_earlier_batch_sample(lib):
     b, b_sc = canon(ref.cpu().numpy(), ref_sc.cpu().numpy())
     assert np.array_equal(a, b) and np.array_equal(a_sc.view(np.uint32), b_sc.view(np.uint32))
     _check(r, idx.cpu().numpy(), sc.cpu().numpy(), range(0, T, 5), "earlier-batch sample")
+
+
+UNFUSED = [(40, 5000, 64, 100), (33, 7001, 128, 64), (70, 4500, 256, 300), (20, 3000, 768, 50), (9, 2100, 512, 2000)]
+
+
+@pytest.mark.parametrize("shape", UNFUSED, ids=lambda s: f"T{s[0]}_N{s[1]}_D{s[2]}_k{s[3]}")
+def test_unfused_retrieval(lib, shape):
+    """The unfused path (full score matrix, radix select per row) returns the
+    fused path's sets and bit-identical scores, and the oracle's sets."""
+    import torch
+    T, N, D, k = shape
+    say("unfused retrieval", shape)
+    r = retrieval_inputs(T, N, D, k, n_centres=max(2, N // 400), sigma=0.3, n_sample=3 * k if 3 * k < N else N // 2,
+                         device="cuda", block=4096)
+    q = _q_dev(r)
+    idx, sc = lib.unfused_retrieve(q, r["db"], k, return_scores=True)
+    ref, ref_sc = lib.retrieve(q, r["db"], k, sample=torch.from_numpy(r["sample"]).cuda(), return_scores=True)
+    a, a_sc = canon(idx.cpu().numpy(), sc.cpu().numpy())
+    b, b_sc = canon(ref.cpu().numpy(), ref_sc.cpu().numpy())
+    assert np.array_equal(a, b) and np.array_equal(a_sc.view(np.uint32), b_sc.view(np.uint32))
+    _check(r, idx.cpu().numpy(), sc.cpu().numpy(), range(0, T, 3), f"unfused {shape}")
+
+
+def test_unfused_retrieval_large(lib):
+    """256 queries over 1M rows of 768 dimensions (a 1 GB score matrix): the
+    fused path's sets and scores, sorted output included."""
+    import torch
+    T, N, D, k = 256, 1 << 20, 768, 512
+    say("unfused retrieval large", (T, N, D, k))
+    r = retrieval_inputs(T, N, D, k, n_centres=500, sigma=0.3, n_sample=3 * k, device="cuda", block=1 << 16)
+    q = _q_dev(r)
+    opts = lib.Opts(sorted_output=1)
+    idx, sc = lib.unfused_retrieve(q, r["db"], k, opts=opts, return_scores=True)
+    ref, ref_sc = lib.retrieve(q, r["db"], k, sample=torch.from_numpy(r["sample"]).cuda(), opts=opts,
+                               return_scores=True)
+    assert torch.equal(idx, ref) and torch.equal(sc.view(torch.int32), ref_sc.view(torch.int32))
+    _check(r, idx.cpu().numpy(), sc.cpu().numpy(), [0, 127, 255], "unfused large")
