@@ -38,12 +38,12 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
 DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
-SCAN_TRAFFIC = {"digest": "619cf132cf20f51a", "workload": "prefill-1m-fp8",
-                "bytes": 2223725 * 1024 * 2.0 + 150376 * 1024 * 1.0}
-RETR_TRAFFIC = {"digest": "f856f9695cf01582", "workload": "retrieval-8m-d768-bf16",
-                "bytes": 10401972 * 1024 * 2.0 + 1295802 * 1024 * 1.0}
-DECODE_TRAFFIC = {"digest": "619cf132cf20f51a", "workload": "decode-1m-fp8",
-                  "bytes": 67641 * 1024 * 2.0 + 46 * 1024 * 1.0}
+SCAN_TRAFFIC = {"digest": "1d0876c304b33d72", "workload": "prefill-1m-fp8",
+                "bytes": 2228806 * 1024 * 2.0 + 151541 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "70f76ff064db45e9", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 10621385 * 1024 * 2.0 + 1366147 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "1d0876c304b33d72", "workload": "decode-1m-fp8",
+                  "bytes": 67663 * 1024 * 2.0 + 47 * 1024 * 1.0}
 DSA_TRAFFIC = {"digest": "295e9303474d2832", "workload": "dsa-1m-fp8",
                "pack_bytes": 33067 * 1024 * 2.0 + 134234 * 1024 * 1.0,
                "gather_bytes": 745525 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
