@@ -44,9 +44,9 @@ RETR_TRAFFIC = {"digest": "70f76ff064db45e9", "workload": "retrieval-8m-d768-bf1
                 "bytes": 10621385 * 1024 * 2.0 + 1366147 * 1024 * 1.0}
 DECODE_TRAFFIC = {"digest": "1d0876c304b33d72", "workload": "decode-1m-fp8",
                   "bytes": 67663 * 1024 * 2.0 + 47 * 1024 * 1.0}
-DSA_TRAFFIC = {"digest": "295e9303474d2832", "workload": "dsa-1m-fp8",
-               "pack_bytes": 33067 * 1024 * 2.0 + 134234 * 1024 * 1.0,
-               "gather_bytes": 745525 * 1024 * 2.0 + 2708536 * 1024 * 1.0}
+DSA_TRAFFIC = {"digest": "4384835ee6aafd1b", "workload": "dsa-1m-fp8",
+               "pack_bytes": 33066 * 1024 * 2.0 + 134413 * 1024 * 1.0,
+               "gather_bytes": 744615 * 1024 * 2.0 + 2708540 * 1024 * 1.0}
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
