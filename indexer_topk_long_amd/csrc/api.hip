@@ -215,16 +215,16 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     }
     if (kind != LTK_KIND_SCORE_SELECT && kind != LTK_KIND_RETRIEVE) return 0;
     if (T < 0 || L < 1 || topk < 1 || n_sample < 0) return 0;
-    (void)H;
     Opts o;
     if (resolve_opts(opts, kind == LTK_KIND_RETRIEVE ? retrieve_default_ccap(topk) : kDefaultCcap, o) != LTK_OK)
         return 0;
     if (kind == LTK_KIND_RETRIEVE)
         return ws_layout(T, L, sample_slots(n_sample, topk, L), o.ccap,
                          retr_hist_words(T, o.nbins, retr_splits(T, D, L, o.l_splits))).total;
+    (void)H;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
-    return ws_layout(T, L, sample_slots(n_sample, topk, L), p.ccap, p.shared ? (size_t)T * o.nbins : 0,
-                     dtype == LTK_FP8_E4M3FN ? D : 0).total;
+    const int32_t n_slots = sample_slots(n_sample, topk, L);
+    return ws_layout(T, L, n_slots, p.ccap, p.shared ? (size_t)T * o.nbins : 0, dtype == LTK_FP8_E4M3FN ? D : 0).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -244,6 +244,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     if (o.sorted && topk > kMaxSortedK) return LTK_EINVAL;
     const IdxPlan plan = indexer_plan(T, L, dtype, o);
     const int32_t n_slots = sample_slots(n_sample, topk, L);
+    // few queries and a small sample: the sample steps take one launch
+    const bool front = front_path(T, n_slots, dtype, D, H);
     const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0, fp8 ? D : 0);
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
@@ -282,6 +284,7 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.meta = wsb + lay.meta;
     a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
     a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
+    a.front_parts = front ? front_parts(n_slots) : 0;
     a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
     a.thr_fin = reinterpret_cast<int*>(wsb + lay.thrf);
     a.ovf_list = reinterpret_cast<int*>(wsb + lay.ovfl);
@@ -300,8 +303,16 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.ev_scan_stop = o.ev1;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_prepare_sample(a, sample, n_sample, lay, wsb, s) != hipSuccess) return LTK_EHIP;
-    if (launch_indexer_fused(dtype, D, head_blocks(H), a, s) != hipSuccess) return LTK_EHIP;
+    FrontArgs fr{};
+    if (front) {
+        fr.sample = sample;
+        fr.n = n_sample;
+        fr.zero = reinterpret_cast<uint32_t*>(wsb + lay.zero_begin);
+        fr.n_zero = (lay.bitmap - lay.zero_begin) / 4;   // the bitmap is not used
+    } else if (launch_prepare_sample(a, sample, n_sample, lay, wsb, s) != hipSuccess) {
+        return LTK_EHIP;
+    }
+    if (launch_indexer_fused(dtype, D, head_blocks(H), a, front ? &fr : nullptr, s) != hipSuccess) return LTK_EHIP;
     return LTK_OK;
 }
 

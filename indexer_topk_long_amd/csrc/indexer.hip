@@ -268,39 +268,72 @@ __device__ __forceinline__ int group_key_end(const IdxArgs& a, int t0) {
 // (q''/2) * S with S = 2^(8 - e) putting the largest magnitude in [128, 256),
 // each part taking the residue of the ones before it times 16.  Every fp8
 // pass reads these same bytes, so all of them get the same linear term.
+// The loads come first (qlin_load, every one issued before any is waited
+// for), then the sums (qlin_reduce), which every thread of a workgroup of at
+// least 256 threads calls (the first 256 do the work, so that every launch
+// adds in the same order).  lin, when given, receives a copy of the four
+// parts in LDS, and store = false leaves the workspace copy to another
+// workgroup.  qlin_reduce returns 1/S (to every thread).
 template <int D>
-__global__ __launch_bounds__(256) void qlin_kernel(IdxArgs a) {
-    constexpr int NQ = D / 4;          // 4-dimension groups
-    constexpr int HG = 256 / NQ;       // head groups
-    __shared__ float part[HG][D];
-    __shared__ float wmax[4];
-    const int t = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-    const int dq = tid % NQ, hg = tid / NQ;
-    const float sq = a.q_scale[t];
+struct QlinIn {
+    static constexpr int NQ = D / 4;          // 4-dimension groups
+    static constexpr int HG = 256 / NQ;       // head groups
+    static constexpr int NI = 64 / HG;        // heads per thread (at most 64 heads)
+    uint32_t v[NI];
+    float w[NI];
+    float sq;
+};
+
+template <int D>
+__device__ __forceinline__ void qlin_load(QlinIn<D>& in, const IdxArgs& a, int t) {
+    using Q = QlinIn<D>;
+    const int tid = threadIdx.x;
+    const int dq = tid % Q::NQ, hg = (tid / Q::NQ) % Q::HG;
+    in.sq = a.q_scale[t];
     const uint8_t* q = a.q + (size_t)t * a.H * D;
     const float* w = a.w + (size_t)t * a.H;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-    for (int h = hg; h < a.H; h += HG) {
-        const float c = (sq * w[h]) * 0.5f;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(q + (size_t)h * D + 4 * dq);
-        acc[0] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 0), acc[0]);
-        acc[1] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 1), acc[1]);
-        acc[2] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 2), acc[2]);
-        acc[3] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)v, 3), acc[3]);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[hg][4 * dq + i] = acc[i];
+    for (int i = 0; i < Q::NI; ++i) {
+        const int h = min(hg + i * Q::HG, a.H - 1);
+        in.v[i] = *reinterpret_cast<const uint32_t*>(q + (size_t)h * D + 4 * dq);
+        in.w[i] = w[h];
+    }
+}
+
+template <int D>
+__device__ float qlin_reduce(const QlinIn<D>& in, const IdxArgs& a, int t, uint8_t* lin, bool store = true) {
+    using Q = QlinIn<D>;
+    __shared__ float part[Q::HG][D];
+    __shared__ float wmax[4];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    if (tid < 256) {
+        const int dq = tid % Q::NQ, hg = tid / Q::NQ;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < Q::NI; ++i) {
+            if (hg + i * Q::HG < a.H) {
+                const float c = (in.sq * in.w[i]) * 0.5f;
+                acc[0] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)in.v[i], 0), acc[0]);
+                acc[1] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)in.v[i], 1), acc[1]);
+                acc[2] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)in.v[i], 2), acc[2]);
+                acc[3] = __builtin_fmaf(c, __builtin_amdgcn_cvt_f32_fp8((int)in.v[i], 3), acc[3]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[hg][4 * dq + i] = acc[i];
+    }
     __syncthreads();
     float x = 0.0f;
     if (tid < D) {
 #pragma unroll
-        for (int g = 0; g < HG; ++g) x += part[g][tid];
+        for (int g = 0; g < Q::HG; ++g) x += part[g][tid];
     }
-    float mx = wave_max_f32(tid < D ? fabsf(x) : 0.0f);
-    if (lane == 0) wmax[wave] = mx;
+    if (tid < 256) {
+        const float m = wave_max_f32(tid < D ? fabsf(x) : 0.0f);
+        if (lane == 0) wmax[wave] = m;
+    }
     __syncthreads();
-    mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     int e = 0;
     if (mx > 0.0f) frexpf(mx, &e);   // mx in [2^(e-1), 2^e)
     e = max(-100, min(e, 100));      // keeps S and 1/S finite and normal
@@ -310,11 +343,21 @@ __global__ __launch_bounds__(256) void qlin_kernel(IdxArgs a) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false) & 0xffu;
-            out[p * D + tid] = (uint8_t)code;
+            if (store) out[p * D + tid] = (uint8_t)code;
+            if (lin) lin[p * D + tid] = (uint8_t)code;
             r = (r - __builtin_amdgcn_cvt_f32_fp8((int)code, 0)) * 16.0f;   // exact residue, scaled
         }
     }
-    if (tid == 0) a.qinv[t] = ldexpf(1.0f, e - 8);
+    const float inv = ldexpf(1.0f, e - 8);
+    if (store && tid == 0) a.qinv[t] = inv;
+    return inv;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void qlin_kernel(IdxArgs a) {
+    QlinIn<D> in;
+    qlin_load<D>(in, a, blockIdx.x);
+    (void)qlin_reduce<D>(in, a, blockIdx.x, nullptr);
 }
 
 // 32 fp8 values of row `row` (D bytes), dimensions [32 ks, 32 ks + 32); zero
@@ -393,14 +436,64 @@ __device__ __forceinline__ float lin_one64_t(const LinFrag& aq, const uint8_t* k
 // Sample: score the de-duplicated sample keys
 // ---------------------------------------------------------------------------
 
+// Range, delta, histogram and initial threshold bin of query t (its Meta)
+// from each thread's count of valid sample scores and their extremes; add(smin,
+// delta) puts the thread's valid scores into the histogram sh (nbins words).
+// All NW * 64 threads of the workgroup call it together (it synchronises them).
+template <int NW, class Add>
+__device__ void sample_meta(const IdxArgs& a, int t, uint32_t c, float mn, float mx, uint32_t* sh, Add add) {
+    __shared__ float s_min[NW], s_max[NW];
+    __shared__ uint32_t s_nv[NW];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    c = wave_sum_u32(c);
+    for (int i = tid; i < a.nbins; i += NW * 64) sh[i] = 0u;
+    mn = wave_min_f32(mn);
+    mx = wave_max_f32(mx);
+    if (lane == 0) {
+        s_nv[wave] = c;
+        s_min[wave] = mn;
+        s_max[wave] = mx;
+    }
+    __syncthreads();
+    int nv = 0;
+    float smin = INFINITY, smax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        nv += (int)s_nv[w];
+        smin = fminf(smin, s_min[w]);
+        smax = fmaxf(smax, s_max[w]);
+    }
+    if (nv == 0) {
+        smin = 0.0f;
+        smax = 1.0f;
+    }
+    float width = smax - smin;
+    const float floor_w = 1e-6f * fmaxf(1.0f, fabsf(smax));
+    if (!(width >= floor_w)) width = floor_w;
+    const float delta = (float)a.nbins / width;
+    add(smin, delta);
+    __syncthreads();
+    if (wave == 0) {
+        int thr0 = 0;
+        if (nv >= a.topk) thr0 = max(0, suffix_pick(sh, a.nbins, (uint32_t)a.topk).bin);
+        if (lane == 0) {
+            Meta m;
+            m.smin = smin;
+            m.delta = delta;
+            m.thr0 = thr0;
+            m.nvalid = nv;
+            reinterpret_cast<Meta*>(a.meta)[t] = m;
+        }
+    }
+    __syncthreads();   // sh and the partials are free for the next query
+}
+
 // Sample statistics of query t: valid sample keys (<= pos), range, delta,
 // histogram and the initial threshold bin.  All 256 threads of the
 // workgroup call it together (it synchronises them); sh holds nbins words.
 __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
-    __shared__ float s_min[4], s_max[4];
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tid = threadIdx.x;
     const int nu = (int)*a.nu;
-    __shared__ uint32_t s_nv[4];
     const int pos_t = a.pos ? min(a.pos[t], a.L - 1) : a.L - 1;   // no positions: every key is valid
     const float* S = a.sscore + (size_t)t * a.n_sample;
     // one pass: valid sample keys (<= pos_t; the list may be in any order)
@@ -434,49 +527,16 @@ __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
             }
         }
     }
-    c = wave_sum_u32(c);
-    for (int i = tid; i < a.nbins; i += 256) sh[i] = 0u;
-    mn = wave_min_f32(mn);
-    mx = wave_max_f32(mx);
-    if (lane == 0) {
-        s_nv[wave] = c;
-        s_min[wave] = mn;
-        s_max[wave] = mx;
-    }
-    __syncthreads();
-    const int nv = (int)(s_nv[0] + s_nv[1] + s_nv[2] + s_nv[3]);
-    float smin = fminf(fminf(s_min[0], s_min[1]), fminf(s_min[2], s_min[3]));
-    float smax = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-    if (nv == 0) {
-        smin = 0.0f;
-        smax = 1.0f;
-    }
-    float width = smax - smin;
-    const float floor_w = 1e-6f * fmaxf(1.0f, fabsf(smax));
-    if (!(width >= floor_w)) width = floor_w;
-    const float delta = (float)a.nbins / width;
-    if (in_regs) {
+    sample_meta<4>(a, t, c, mn, mx, sh, [&](float smin, float delta) {
+        if (in_regs) {
 #pragma unroll
-        for (int i = 0; i < kStatsRegs; ++i)
-            if (!__builtin_isnan(v[i])) atomicAdd(&sh[bin_of(v[i], smin, delta, a.nbins)], 1u);
-    } else {
-        for (int j = tid; j < nu; j += 256)
-            if (a.sample_u[j] <= pos_t) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-        int thr0 = 0;
-        if (nv >= a.topk) thr0 = max(0, suffix_pick(sh, a.nbins, (uint32_t)a.topk).bin);
-        if (lane == 0) {
-            Meta m;
-            m.smin = smin;
-            m.delta = delta;
-            m.thr0 = thr0;
-            m.nvalid = nv;
-            reinterpret_cast<Meta*>(a.meta)[t] = m;
+            for (int i = 0; i < kStatsRegs; ++i)
+                if (!__builtin_isnan(v[i])) atomicAdd(&sh[bin_of(v[i], smin, delta, a.nbins)], 1u);
+        } else {
+            for (int j = tid; j < nu; j += 256)
+                if (a.sample_u[j] <= pos_t) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
         }
-    }
-    __syncthreads();   // sh and the partials are free for the next query
+    });
 }
 
 __global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
@@ -546,6 +606,186 @@ __device__ __forceinline__ void sample_score_part(const IdxArgs& a, int qg, int 
 template <int DT, int D, int HB>
 __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
     sample_score_part<DT, D, HB>(a, blockIdx.x / a.s_splits, blockIdx.x % a.s_splits);
+}
+
+// ---------------------------------------------------------------------------
+// Sample, decode shape: the sample steps in one launch
+// ---------------------------------------------------------------------------
+//
+// With few queries the steps above are each a launch of a few microseconds
+// that leaves most of the GPU idle.  Here `parts` workgroups per query do all
+// of them: workgroup (t, p) takes the sample keys of residue class p modulo
+// parts that query t can see and inserts them into its own LDS hash table.
+// The entry whose insertion finds its key new keeps the key's slot; the score
+// of the key -- the arithmetic of the sample pass, so the same value -- goes
+// to that slot of score row t.  The workgroup writes NaN to every other slot
+// it owns: the key's other entries, and the entries no class takes (empty,
+// outside the context or past the query's position) whose slot is p modulo
+// parts.  The classes partition the keys, so each distinct key the query sees
+// has exactly one score in the row.  Every workgroup of a query computes its
+// fp8 linear-term operands the same way (p = 0 stores them).  The launch's
+// other workgroups clear the workspace.
+
+constexpr int kFrontThreads = 512;
+constexpr int kFrontRegs = kFrontSampleMax / kFrontThreads;   // sample entries per thread
+
+template <int DT, int D, int HB>
+__global__ __launch_bounds__(kFrontThreads) void front_kernel(IdxArgs a, const int32_t* sample, int n, int parts,
+                                                              int log2_slots, uint32_t* zero, size_t n_zero) {
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int nq = a.T * parts;
+    if ((int)blockIdx.x >= nq) {
+        const size_t i0 = (size_t)(blockIdx.x - nq) * kFrontThreads + tid;
+        for (size_t i = i0; i < n_zero; i += (size_t)(gridDim.x - nq) * kFrontThreads) zero[i] = 0u;
+        if (a.stats && i0 == 0) {
+            a.stats->cand_written = 0;
+            a.stats->bytes_written = 0;
+            a.stats->max_cand_per_query = 0;
+            a.stats->overflow_rows = 0;
+        }
+        return;
+    }
+    const int t = blockIdx.x / parts, p = blockIdx.x % parts;
+    extern __shared__ unsigned long long fs[];
+    const int slots = 1 << log2_slots;
+    unsigned long long* list = fs;                              // key << 32 | its slot
+    uint32_t* tab = reinterpret_cast<uint32_t*>(fs + a.n_sample);   // hash table of keys
+    __shared__ uint32_t s_n;
+    __shared__ __attribute__((aligned(16))) uint8_t lin_l[DT == DT_FP8 ? 4 * D : 16];
+    const int pos_t = min(a.pos[t], a.L - 1);
+    const int ns = a.n_sample;                                  // slots of the score row
+    float* srow = a.sscore + (size_t)t * ns;
+    // every load that depends on nothing goes out before the first wait
+    int sv[kFrontRegs];
+    if (n > 0) {
+#pragma unroll
+        for (int r = 0; r < kFrontRegs; ++r) {
+            const int j = tid + kFrontThreads * r;
+            sv[r] = (j < n) ? sample[j] : -1;
+        }
+    }
+    QueryRegs<DT, D, HB> qr;
+    load_query<DT, D, HB>(qr, a, t);
+    QlinIn<D> qin;
+    if constexpr (DT == DT_FP8) qlin_load<D>(qin, a, t);
+    for (int i = tid; i < slots; i += kFrontThreads) tab[i] = kHashEmpty;
+    if (tid == 0) s_n = 0u;
+    __syncthreads();
+    if (n > 0) {
+        // keys of the class in [0, pos_t]: the entry that inserts a key lists
+        // it with its slot; the other slots this workgroup owns get NaN
+#pragma unroll
+        for (int r = 0; r < kFrontRegs; ++r) {
+            const int i = tid + kFrontThreads * r;
+            const int s = sv[r];
+            const bool vis = s >= 0 && s <= pos_t;
+            bool fresh = false;
+            if (vis && s % parts == p) {
+                const uint32_t key = (uint32_t)s;
+                uint32_t h = (key * 2654435761u) >> (32 - log2_slots);
+                while (true) {   // terminates: fewer entries than slots
+                    const uint32_t old = atomicCAS(&tab[h], kHashEmpty, key);
+                    if (old == kHashEmpty) { fresh = true; break; }
+                    if (old == key) break;
+                    h = (h + 1u) & (uint32_t)(slots - 1);
+                }
+                if (!fresh) srow[i] = NAN;
+            } else if (!vis && i < ns && i % parts == p) {
+                srow[i] = NAN;   // an entry no class takes
+            }
+            const uint64_t m = __ballot(fresh);
+            uint32_t base = 0u;
+            if (lane == 0 && m) base = atomicAdd(&s_n, (uint32_t)__popcll(m));
+            base = lane0_u32(base);
+            if (fresh) list[base + mbcnt(m)] = ((unsigned long long)s << 32) | (uint32_t)i;
+        }
+    } else {
+        // no sample given: ns evenly spaced keys below the largest causal
+        // bound of the call's queries (distinct and ascending), or fewer; this
+        // workgroup takes the slots p modulo parts
+        int kmax = 0;
+        for (int u = 0; u < a.T; ++u) kmax = max(kmax, min(a.pos[u], a.L - 1) + 1);
+        const int nw = min(ns, kmax);
+        for (int i = p + tid * parts; i < ns; i += kFrontThreads * parts) {
+            const int key = (i < nw) ? (int)(((int64_t)i * kmax) / nw) : -1;
+            if (key >= 0 && key <= pos_t) {
+                const uint32_t c = atomicAdd(&s_n, 1u);
+                list[c] = ((unsigned long long)key << 32) | (uint32_t)i;
+            } else {
+                srow[i] = NAN;
+            }
+        }
+    }
+    float inv = 0.0f;   // fp8: 1/S of the linear term
+    if constexpr (DT == DT_FP8) {
+        inv = qlin_reduce<D>(qin, a, t, lin_l, p == 0);   // synchronises the workgroup
+    }
+    __syncthreads();   // the list, and the linear-term parts
+    const int nu = (int)s_n;
+    // scores: wave w takes 64-key blocks w, w + 8, ... of the list as two
+    // 32-key slots of the query (lane l: list entry 64 b + l); every load of
+    // a block is issued before the first is waited for
+    LinFrag aq;
+    if constexpr (DT == DT_FP8) load_lin_frag<D>(aq, lin_l + (lane & 3) * D, lane >> 4);
+    const int nblk = (nu + 63) / 64;
+    auto key_at = [&](int j) { return (int)(list[min(j, nu - 1)] >> 32); };
+    for (int b = wave; b < nblk; b += kFrontThreads / 64) {
+        const int j = 64 * b + lane;
+        const unsigned long long own = list[min(j, nu - 1)];
+        HalfRow<DT, D> ka, kb;
+        load_key<DT, D>(ka, a.k, key_at(64 * b + (lane & 31)));
+        load_key<DT, D>(kb, a.k, key_at(64 * b + 32 + (lane & 31)));
+        float I;
+        if constexpr (DT == DT_FP8) {
+            // lane l's key is 64 b + 16 (l >> 4) + (l & 15): instruction i
+            // covers keys 16 i .. 16 i + 15 of the block
+            LinFrag kf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                load_lin_frag<D>(kf[i], a.k + (size_t)key_at(64 * b + 16 * i + (lane & 15)) * D, lane >> 4);
+            const float ks = a.k_scale[(int)(own >> 32)];
+            I = score_2slots<DT, D, HB>(qr, ka, qr, kb);
+            float tl = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ti = lin_combine(lin_mfma(aq, kf[i]));
+                tl = ((lane >> 4) == i) ? ti : tl;
+            }
+            I = lin_score(tl, inv, I, ks);
+        } else {
+            I = score_2slots<DT, D, HB>(qr, ka, qr, kb);
+        }
+        if (j < nu) srow[(uint32_t)own] = I;
+    }
+}
+
+// Statistics of query t from its score row of the one-launch sample steps
+// (NaN: no key at that slot).
+__global__ __launch_bounds__(kFrontThreads) void front_stats_kernel(IdxArgs a) {
+    __shared__ uint32_t sh[kMaxBins];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float* srow = a.sscore + (size_t)t * a.n_sample;
+    float v[kFrontRegs];
+#pragma unroll
+    for (int r = 0; r < kFrontRegs; ++r) {
+        const int i = tid + kFrontThreads * r;
+        v[r] = (i < a.n_sample) ? srow[i] : NAN;
+    }
+    uint32_t c = 0;
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kFrontRegs; ++r) {
+        if (!__builtin_isnan(v[r])) {
+            ++c;
+            mn = fminf(mn, v[r]);
+            mx = fmaxf(mx, v[r]);
+        }
+    }
+    sample_meta<kFrontThreads / 64>(a, t, c, mn, mx, sh, [&](float smin, float delta) {
+#pragma unroll
+        for (int r = 0; r < kFrontRegs; ++r)
+            if (!__builtin_isnan(v[r])) atomicAdd(&sh[bin_of(v[r], smin, delta, a.nbins)], 1u);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1199,7 +1439,10 @@ __device__ bool finalize_row(const IdxArgs& a, int t, uint32_t* sh) {
         // overflowed row is rescanned)
         const bool ovf = (int64_t)n > a.ccap;
         const uint64_t stored = ovf ? (uint64_t)a.ccap : (uint64_t)n;
-        const uint64_t b = 8ull * stored + (a.pass != 2 ? 4ull * (uint64_t)(*a.nu) : 0ull) +
+        // sample scores stored for this query: a whole row on the one-launch
+        // path, else one per distinct in-range sample key
+        const uint64_t nsc = a.front_parts ? (uint64_t)a.n_sample : (uint64_t)*a.nu;
+        const uint64_t b = 8ull * stored + (a.pass != 2 ? 4ull * nsc : 0ull) +
                            ((ovf && a.pass == 1) ? 0ull : 4ull * (uint64_t)k * (a.out_score ? 2u : 1u));
         atomicAdd((unsigned long long*)&a.stats->bytes_written, (unsigned long long)b);
     }
@@ -1728,14 +1971,30 @@ static bool run_scan_variant(const IdxArgs& args, hipStream_t st) {
     return false;
 }
 
-hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st) {
+hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, const FrontArgs* front, hipStream_t st) {
     const int nqg = (a.T + kQPG - 1) / kQPG;
     hipError_t err = hipSuccess;
     const bool ok = dispatch(dt, D, HB, [&](auto DTc, auto Dc, auto HBc) {
         constexpr int DT_ = decltype(DTc)::value, D_ = decltype(Dc)::value, HB_ = decltype(HBc)::value;
-        if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
-        sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
-        sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
+        if (front) {
+            // the caller checked front_fits for this combination
+            if constexpr (!(DT_ == DT_F32 && D_ == 128 && HB_ == 2)) {
+                const int parts = a.front_parts;
+                const size_t lds = front_lds_bytes(a.n_sample);
+                const int zb = (int)std::min<size_t>((front->n_zero + kFrontThreads - 1) / kFrontThreads, 512);
+                allow_lds(front_kernel<DT_, D_, HB_>, lds);
+                front_kernel<DT_, D_, HB_><<<a.T * parts + std::max(zb, 1), kFrontThreads, lds, st>>>(
+                    a, front->sample, front->n, parts, front_log2_slots(a.n_sample), front->zero, front->n_zero);
+                front_stats_kernel<<<a.T, kFrontThreads, 0, st>>>(a);
+            } else {
+                err = hipErrorInvalidValue;
+                return;
+            }
+        } else {
+            if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
+            sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
+            sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
+        }
         auto run_scan = [&](const IdxArgs& args) { return run_scan_variant<DT_, D_, HB_, false>(args, st); };
         if (!run_scan(a)) { err = hipErrorInvalidValue; return; }
         const size_t sel_lds = std::max(fin_lds_bytes(a), row_select_lds(a.topk, a.sorted, a.out_score != nullptr));

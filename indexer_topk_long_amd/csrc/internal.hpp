@@ -61,6 +61,33 @@ inline size_t qlin_bytes(int32_t T, int lin_d) { return (size_t)T * 4 * (size_t)
 // tail of the cleared range, then stay untouched).
 constexpr int kHashSampleMax = 16384;
 
+// Calls of at most kFrontMaxT queries whose sample has at most kFrontSampleMax
+// slots run the sample steps (de-duplication, linear-term operands, scores) as
+// one launch of front_parts workgroups per query, each taking the sample keys
+// of one residue class modulo front_parts; score row t of sscore then holds
+// one score per distinct key the query sees, at the slot of one of its
+// entries, and NaN at every other slot.  One more launch turns the rows into
+// statistics.  A workgroup's LDS holds the list of its keys (n_slots 64-bit
+// entries) and a hash table of 2^front_log2_slots keys (more than the sample,
+// as one class may hold every key).
+constexpr int kFrontMaxT = 8;
+constexpr int kFrontSampleMax = 6144;
+// (fp32 queries of 128 dimensions in two head blocks leave that kernel too
+// few registers: those calls keep the separate launches)
+inline bool front_fits(int dtype, int D, int HB) { return !(dtype == 0 && D == 128 && HB == 2); }
+inline bool front_path(int32_t T, int32_t n_slots, int dtype, int D, int H) {
+    return T <= kFrontMaxT && n_slots <= kFrontSampleMax && front_fits(dtype, D, (H + 31) / 32);
+}
+inline int front_parts(int32_t n_slots) { return n_slots > 512 ? (n_slots + 511) / 512 : 1; }
+inline int front_log2_slots(int32_t n_slots) {
+    int lg = 10;
+    while ((1 << lg) <= n_slots) ++lg;
+    return lg;
+}
+inline size_t front_lds_bytes(int32_t n_slots) {
+    return (size_t)n_slots * 8 + ((size_t)4 << front_log2_slots(n_slots));
+}
+
 // Sample slots of a call: the caller's sample size, or, with no sample,
 // min(3 k, L, 16384) evenly spaced causal keys drawn by the library (the
 // pages' sample is 3 k keys of the previous chunk's result).
@@ -123,6 +150,7 @@ struct IdxArgs {
                              // 1: first pass of two (overflowed rows are listed for a rescan);
                              // 2: the rescan of the listed rows
     int64_t ccap;
+    int front_parts;         // workgroups per query of the one-launch sample steps, or 0
     // workspace
     uint32_t* tail;
     uint32_t* flags;
@@ -181,7 +209,15 @@ struct RetrArgs {
 // Host launchers (return hipSuccess or the first launch error).
 hipError_t launch_prepare_sample(const IdxArgs& a, const int32_t* sample, int n_sample, const WsLayout& lay,
                                  uint8_t* ws, hipStream_t st);   // n_sample == 0: the library's own (a.n_sample keys)
-hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
+// The sample of a call that takes the one-launch sample steps, and the
+// workspace range its launch clears.
+struct FrontArgs {
+    const int32_t* sample;
+    int n;
+    uint32_t* zero;
+    size_t n_zero;
+};
+hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, const FrontArgs* front, hipStream_t st);
 hipError_t launch_indexer_unfused(int dt, int D, int HB, const IdxArgs& a, hipStream_t st);
 // Unfused workspace: the T x L fp32 score matrix, then (fp8) the linear-term parts.
 inline size_t unfused_matrix_bytes(int32_t T, int64_t L) { return align_up((size_t)T * (size_t)L * 4, 256); }

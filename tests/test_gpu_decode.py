@@ -115,6 +115,89 @@ def test_decode_waves_per_query_variants(lib, case):
     assert np.array_equal(canon(idx.cpu().numpy()), canon(uidx.cpu().numpy()))
 
 
+def _messy_sample(n, L, pos, seed):
+    """n sample entries with repeats, empty (-1) slots, keys past the context
+    and keys that only the later of the call's positions can see."""
+    g = np.random.default_rng(seed)
+    s = g.integers(0, L, size=n).astype(np.int32)
+    h = n // 4
+    s[:h] = s[h:2 * h]          # the second quarter's keys twice
+    s[3::37] = -1
+    s[5::41] = L + 3
+    p = np.clip(np.asarray(pos, np.int64), 0, L - 1)
+    m = len(s[7::43])
+    s[7::43] = p.max() - g.integers(0, p.max() - p.min() + 1, size=m)
+    return s
+
+
+FRONT = [
+    # (T, H, D, dtype, k, sample entries, positions): calls of at most 8
+    # queries with at most 6,144 sample slots take the sample steps in one
+    # launch; the neighbours keep the separate launches
+    (1, 64, 128, "fp8", 512, 0, None),          # no sample: the library's evenly spaced keys
+    (6, 64, 128, "fp8", 300, 6144, "mixed"),    # the largest such sample; unsorted, repeated, outside positions
+    (8, 20, 64, "bf16", 200, 3000, None),
+    (8, 20, 64, "bf16", 200, 6145, None),       # one slot more: separate launches
+    (9, 20, 64, "fp8", 200, 3000, None),        # nine queries: separate launches
+    (2, 64, 128, "f32", 128, 1000, None),       # fp32 rows of 128 in two head blocks: separate launches
+    (3, 20, 128, "f32", 64, 0, "mixed3"),
+]
+
+
+@pytest.mark.parametrize("case", FRONT, ids=lambda c: f"T{c[0]}_H{c[1]}_D{c[2]}_{c[3]}_k{c[4]}_s{c[5]}_{c[6]}")
+def test_sample_steps_in_one_launch(lib, case):
+    """Exact against the oracle, bit-identical to the unfused path, and the same
+    sets sorted through the overflow fallback, whichever sample path runs."""
+    import torch
+    T, H, D, dt, k, ns, pk = case
+    L = 30011
+    pos = {None: None,
+           "mixed": np.array([L - 1, 100, L - 1, L + 20000, 15000, -1], np.int32),
+           "mixed3": np.array([7, 29000, L + 9000], np.int32)}[pk]
+    say("sample steps", case)
+    inp = indexer_inputs(T, L, H, D, dt, k, 600, drift=True, tag=67, pos=pos)
+    d = to_dev(inp)
+    sample = torch.from_numpy(_messy_sample(ns, L, inp["pos"], 67)).cuda() if ns else None
+    # a workspace full of 0x7f bytes (floats of 3.4e38): a score slot left
+    # unwritten would raise the sample's threshold above the true one
+    code = {"f32": 0, "bf16": 1, "fp8": 2}[dt]
+    nb = lib.workspace_bytes(lib.KIND_SCORE_SELECT, T, H, D, L, k, ns, code)
+    ws = torch.full((nb,), 0x7f, dtype=torch.uint8, device="cuda")
+    idx, sc, st = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                   k_scale=d["k_scale"], return_scores=True, return_stats=True, workspace=ws)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    say("  candidates/query", st.cand_written / T, "overflow rows", st.overflow_rows)
+    check_rows(inp, idx, sc, range(T), f"sample steps {case}")
+    # bytes written: candidates, sample scores, indices and scores.  The one
+    # launch stores a whole score row per query (a score or NaN per sample
+    # slot); the separate launches store every distinct in-range key's score
+    # for every query.
+    one_launch = T <= 8 and (ns if ns else min(3 * k, L, 16384)) <= 6144 and not (dt == "f32" and D == 128 and H > 32)
+    if ns:
+        keys = np.unique(sample.cpu().numpy())
+        keys = keys[(keys >= 0) & (keys < L)]
+    else:
+        kmax = int(np.clip(inp["pos"], -1, L - 1).max()) + 1
+        nw = min(min(3 * k, L, 16384), kmax)
+        keys = (np.arange(nw, dtype=np.int64) * kmax) // nw
+    slots = ns if ns else min(3 * k, L, 16384)
+    n_scores = T * slots if one_launch else T * len(keys)
+    if st.overflow_rows == 0:
+        assert st.bytes_written == 8 * st.cand_written + 4 * n_scores + 8 * k * T
+    uidx, usc = lib.unfused_score_select(d["q"], d["k"], d["w"], d["pos"], k, q_scale=d["q_scale"],
+                                         k_scale=d["k_scale"], return_scores=True)
+    gi, gs = canon(idx, sc)
+    ui, us = canon(uidx.cpu().numpy(), usc.cpu().numpy())
+    assert np.array_equal(gi, ui)
+    assert np.array_equal(gs.view(np.uint32), us.view(np.uint32))
+    o = lib.Opts(sorted_output=True, cand_capacity=1)
+    sidx, ssc = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=sample, q_scale=d["q_scale"],
+                                 k_scale=d["k_scale"], opts=o, return_scores=True)
+    si, ss = canon(sidx.cpu().numpy(), ssc.cpu().numpy())
+    assert np.array_equal(si, gi)
+    assert np.array_equal(ss.view(np.uint32), gs.view(np.uint32))
+
+
 def test_decode_chain_of_steps(lib):
     """Four speculative-decode steps of T = 4: each step's sample is the previous step's result.
     The same chain again with the results kept in a ring that every step samples whole and
