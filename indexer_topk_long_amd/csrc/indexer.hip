@@ -269,11 +269,12 @@ __device__ __forceinline__ int group_key_end(const IdxArgs& a, int t0) {
 // each part taking the residue of the ones before it times 16.  Every fp8
 // pass reads these same bytes, so all of them get the same linear term.
 // The loads come first (qlin_load, every one issued before any is waited
-// for), then the sums (qlin_reduce), which every thread of a workgroup of at
-// least 256 threads calls (the first 256 do the work, so that every launch
-// adds in the same order).  lin, when given, receives a copy of the four
-// parts in LDS, and store = false leaves the workspace copy to another
-// workgroup.  qlin_reduce returns 1/S (to every thread).
+// for), then the sums (qlin_partial, a barrier, qlin_finish), which every
+// thread of a workgroup of at least 256 threads calls (the first 256 do the
+// work, so that every launch adds in the same order).  lin, when given,
+// receives a copy of the four parts in LDS, and store = false leaves the
+// workspace copy to another workgroup.  qlin_finish returns 1/S (to every
+// thread).
 template <int D>
 struct QlinIn {
     static constexpr int NQ = D / 4;          // 4-dimension groups
@@ -301,11 +302,16 @@ __device__ __forceinline__ void qlin_load(QlinIn<D>& in, const IdxArgs& a, int t
 }
 
 template <int D>
-__device__ float qlin_reduce(const QlinIn<D>& in, const IdxArgs& a, int t, uint8_t* lin, bool store = true) {
+struct QlinShared {
+    float part[QlinIn<D>::HG][D];
+    float wmax[4];
+};
+
+// Head-group partial sums into LDS (no barrier).
+template <int D>
+__device__ __forceinline__ void qlin_partial(const QlinIn<D>& in, const IdxArgs& a, QlinShared<D>& sh) {
     using Q = QlinIn<D>;
-    __shared__ float part[Q::HG][D];
-    __shared__ float wmax[4];
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int tid = threadIdx.x;
     if (tid < 256) {
         const int dq = tid % Q::NQ, hg = tid / Q::NQ;
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -320,20 +326,27 @@ __device__ float qlin_reduce(const QlinIn<D>& in, const IdxArgs& a, int t, uint8
             }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[hg][4 * dq + i] = acc[i];
+        for (int i = 0; i < 4; ++i) sh.part[hg][4 * dq + i] = acc[i];
     }
-    __syncthreads();
+}
+
+// The rest, after a barrier that follows qlin_partial: the head groups added,
+// the scale, the four parts.  Synchronises the workgroup once.
+template <int D>
+__device__ float qlin_finish(const IdxArgs& a, int t, uint8_t* lin, bool store, QlinShared<D>& sh) {
+    using Q = QlinIn<D>;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
     float x = 0.0f;
     if (tid < D) {
 #pragma unroll
-        for (int g = 0; g < Q::HG; ++g) x += part[g][tid];
+        for (int g = 0; g < Q::HG; ++g) x += sh.part[g][tid];
     }
     if (tid < 256) {
         const float m = wave_max_f32(tid < D ? fabsf(x) : 0.0f);
-        if (lane == 0) wmax[wave] = m;
+        if (lane == 0) sh.wmax[wave] = m;
     }
     __syncthreads();
-    const float mx = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float mx = fmaxf(fmaxf(sh.wmax[0], sh.wmax[1]), fmaxf(sh.wmax[2], sh.wmax[3]));
     int e = 0;
     if (mx > 0.0f) frexpf(mx, &e);   // mx in [2^(e-1), 2^e)
     e = max(-100, min(e, 100));      // keeps S and 1/S finite and normal
@@ -355,9 +368,12 @@ __device__ float qlin_reduce(const QlinIn<D>& in, const IdxArgs& a, int t, uint8
 
 template <int D>
 __global__ __launch_bounds__(256) void qlin_kernel(IdxArgs a) {
+    __shared__ QlinShared<D> sh;
     QlinIn<D> in;
     qlin_load<D>(in, a, blockIdx.x);
-    (void)qlin_reduce<D>(in, a, blockIdx.x, nullptr);
+    qlin_partial<D>(in, a, sh);
+    __syncthreads();
+    (void)qlin_finish<D>(a, blockIdx.x, nullptr, true, sh);
 }
 
 // 32 fp8 values of row `row` (D bytes), dimensions [32 ks, 32 ks + 32); zero
@@ -614,25 +630,33 @@ __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
 //
 // With few queries the steps above are each a launch of a few microseconds
 // that leaves most of the GPU idle.  Here `parts` workgroups per query do all
-// of them: workgroup (t, p) takes the sample keys of residue class p modulo
-// parts that query t can see and inserts them into its own LDS hash table.
-// The entry whose insertion finds its key new keeps the key's slot; the score
-// of the key -- the arithmetic of the sample pass, so the same value -- goes
-// to that slot of score row t.  The workgroup writes NaN to every other slot
-// it owns: the key's other entries, and the entries no class takes (empty,
-// outside the context or past the query's position) whose slot is p modulo
-// parts.  The classes partition the keys, so each distinct key the query sees
-// has exactly one score in the row.  Every workgroup of a query computes its
-// fp8 linear-term operands the same way (p = 0 stores them).  The launch's
-// other workgroups clear the workspace.
+// of them.  Workgroup (t, p) inserts the sample entries of class p
+// (front_class of the key) that query t can see into its LDS hash table; the
+// entry that inserts a key writes the key's score -- the arithmetic of the
+// sample pass, so the same value -- to its slot of score row t, every other
+// entry of the key writes NaN there.  The workgroup also writes NaN to the
+// slots of the entries no class takes (empty, outside the context or past the
+// query's position) that are p modulo parts.  The classes
+// partition the keys, so each distinct key the query sees has exactly one
+// score in the row.  Every workgroup of a query computes its fp8 linear-term
+// operands the same way (p = 0 stores them).  The launch's other workgroups
+// clear the workspace.
 
 constexpr int kFrontThreads = 512;
 constexpr int kFrontRegs = kFrontSampleMax / kFrontThreads;   // sample entries per thread
 
+// Class of a sample key: a hash of it, so that keys in arithmetic progression
+// spread over the classes (another multiplier than the hash table's, whose
+// slot bits it would otherwise fix).
+__device__ __forceinline__ int front_class(int key, int lgp) {
+    return lgp ? (int)(((uint32_t)key * 0x85EBCA77u) >> (32 - lgp)) : 0;
+}
+
 template <int DT, int D, int HB>
-__global__ __launch_bounds__(kFrontThreads) void front_kernel(IdxArgs a, const int32_t* sample, int n, int parts,
+__global__ __launch_bounds__(kFrontThreads) void front_kernel(IdxArgs a, const int32_t* sample, int n, int lgp,
                                                               int log2_slots, uint32_t* zero, size_t n_zero) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int parts = 1 << lgp;
     const int nq = a.T * parts;
     if ((int)blockIdx.x >= nq) {
         const size_t i0 = (size_t)(blockIdx.x - nq) * kFrontThreads + tid;
@@ -648,90 +672,106 @@ __global__ __launch_bounds__(kFrontThreads) void front_kernel(IdxArgs a, const i
     const int t = blockIdx.x / parts, p = blockIdx.x % parts;
     extern __shared__ unsigned long long fs[];
     const int slots = 1 << log2_slots;
-    unsigned long long* list = fs;                              // key << 32 | its slot
+    unsigned long long* list = fs;                                  // key << 32 | its slot
     uint32_t* tab = reinterpret_cast<uint32_t*>(fs + a.n_sample);   // hash table of keys
-    __shared__ uint32_t s_n;
+    __shared__ uint32_t s_wn[kFrontThreads / 64];
     __shared__ __attribute__((aligned(16))) uint8_t lin_l[DT == DT_FP8 ? 4 * D : 16];
+    __shared__ QlinShared<DT == DT_FP8 ? D : 64> qsh;
     const int pos_t = min(a.pos[t], a.L - 1);
-    const int ns = a.n_sample;                                  // slots of the score row
+    const int ns = a.n_sample;                                      // slots of the score row
     float* srow = a.sscore + (size_t)t * ns;
-    // every load that depends on nothing goes out before the first wait
+    // every load that depends on nothing goes out before the first wait (the
+    // query's first: the code between its loads has branches)
+    QlinIn<D> qin;
+    if constexpr (DT == DT_FP8) qlin_load<D>(qin, a, t);
+    QueryRegs<DT, D, HB> qr;
+    load_query<DT, D, HB>(qr, a, t);
     int sv[kFrontRegs];
+    int kmax = 0;   // no sample given: the largest causal bound of the call's queries
     if (n > 0) {
 #pragma unroll
         for (int r = 0; r < kFrontRegs; ++r) {
             const int j = tid + kFrontThreads * r;
             sv[r] = (j < n) ? sample[j] : -1;
         }
-    }
-    QueryRegs<DT, D, HB> qr;
-    load_query<DT, D, HB>(qr, a, t);
-    QlinIn<D> qin;
-    if constexpr (DT == DT_FP8) qlin_load<D>(qin, a, t);
-    for (int i = tid; i < slots; i += kFrontThreads) tab[i] = kHashEmpty;
-    if (tid == 0) s_n = 0u;
-    __syncthreads();
-    if (n > 0) {
-        // keys of the class in [0, pos_t]: the entry that inserts a key lists
-        // it with its slot; the other slots this workgroup owns get NaN
-#pragma unroll
-        for (int r = 0; r < kFrontRegs; ++r) {
-            const int i = tid + kFrontThreads * r;
-            const int s = sv[r];
-            const bool vis = s >= 0 && s <= pos_t;
-            bool fresh = false;
-            if (vis && s % parts == p) {
-                const uint32_t key = (uint32_t)s;
-                uint32_t h = (key * 2654435761u) >> (32 - log2_slots);
-                while (true) {   // terminates: fewer entries than slots
-                    const uint32_t old = atomicCAS(&tab[h], kHashEmpty, key);
-                    if (old == kHashEmpty) { fresh = true; break; }
-                    if (old == key) break;
-                    h = (h + 1u) & (uint32_t)(slots - 1);
-                }
-                if (!fresh) srow[i] = NAN;
-            } else if (!vis && i < ns && i % parts == p) {
-                srow[i] = NAN;   // an entry no class takes
-            }
-            const uint64_t m = __ballot(fresh);
-            uint32_t base = 0u;
-            if (lane == 0 && m) base = atomicAdd(&s_n, (uint32_t)__popcll(m));
-            base = lane0_u32(base);
-            if (fresh) list[base + mbcnt(m)] = ((unsigned long long)s << 32) | (uint32_t)i;
-        }
     } else {
-        // no sample given: ns evenly spaced keys below the largest causal
-        // bound of the call's queries (distinct and ascending), or fewer; this
-        // workgroup takes the slots p modulo parts
-        int kmax = 0;
         for (int u = 0; u < a.T; ++u) kmax = max(kmax, min(a.pos[u], a.L - 1) + 1);
-        const int nw = min(ns, kmax);
-        for (int i = p + tid * parts; i < ns; i += kFrontThreads * parts) {
-            const int key = (i < nw) ? (int)(((int64_t)i * kmax) / nw) : -1;
-            if (key >= 0 && key <= pos_t) {
-                const uint32_t c = atomicAdd(&s_n, 1u);
-                list[c] = ((unsigned long long)key << 32) | (uint32_t)i;
-            } else {
-                srow[i] = NAN;
+    }
+    for (int i = tid; i < slots; i += kFrontThreads) tab[i] = kHashEmpty;
+    __syncthreads();   // the empty table before any insertion
+    if constexpr (DT == DT_FP8) qlin_partial<D>(qin, a, qsh);
+    // entry r of this thread: slot i and key s.  With a sample: slot
+    // tid + 512 r.  Without: ns evenly spaced keys below kmax (distinct and
+    // ascending), or fewer, of which this workgroup takes the slots p modulo
+    // parts.
+    const int nw = min(ns, kmax);
+    auto entry = [&](int r, int& i, int& s) {
+        if (n > 0) {
+            i = tid + kFrontThreads * r;
+            s = sv[r];
+        } else {
+            i = p + parts * (tid + kFrontThreads * r);
+            s = (i < nw) ? (int)(((int64_t)i * kmax) / nw) : -1;
+        }
+    };
+    // the keys of the class in [0, pos_t]: the entry that inserts a key into
+    // the hash table lists it with its slot, the key's other entries write NaN
+    // there; so do the entries no class takes (empty, outside the context or
+    // past the query's position) whose slot is p modulo parts
+    uint32_t fresh = 0;   // bit r: entry r inserted its key
+#pragma unroll
+    for (int r = 0; r < kFrontRegs; ++r) {
+        int i, s;
+        entry(r, i, s);
+        const bool vis = i < ns && s >= 0 && s <= pos_t;
+        if (vis && (n == 0 || front_class(s, lgp) == p)) {
+            const uint32_t key = (uint32_t)s;
+            uint32_t h = (key * 2654435761u) >> (32 - log2_slots);
+            bool ins = false;
+            while (true) {   // terminates: fewer entries than slots
+                const uint32_t old = atomicCAS(&tab[h], kHashEmpty, key);
+                if (old == kHashEmpty) { ins = true; break; }
+                if (old == key) break;
+                h = (h + 1u) & (uint32_t)(slots - 1);
             }
+            if (ins) fresh |= 1u << r;
+            else srow[i] = NAN;
+        } else if (i < ns && !vis && (i & (parts - 1)) == p) {
+            srow[i] = NAN;
+        }
+    }
+    const uint32_t c = (uint32_t)__builtin_popcount(fresh);
+    const uint32_t incl = wave_scan_add_u32(c);
+    if (lane == 63) s_wn[wave] = incl;
+    __syncthreads();
+    uint32_t o = incl - c, nu = 0;
+#pragma unroll
+    for (int w = 0; w < kFrontThreads / 64; ++w) {
+        const uint32_t x = s_wn[w];
+        o += (w < wave) ? x : 0u;
+        nu += x;
+    }
+#pragma unroll
+    for (int r = 0; r < kFrontRegs; ++r) {
+        if (fresh & (1u << r)) {
+            int i, s;
+            entry(r, i, s);
+            list[o++] = ((unsigned long long)s << 32) | (uint32_t)i;
         }
     }
     float inv = 0.0f;   // fp8: 1/S of the linear term
-    if constexpr (DT == DT_FP8) {
-        inv = qlin_reduce<D>(qin, a, t, lin_l, p == 0);   // synchronises the workgroup
-    }
-    __syncthreads();   // the list, and the linear-term parts
-    const int nu = (int)s_n;
+    if constexpr (DT == DT_FP8) inv = qlin_finish<D>(a, t, lin_l, p == 0, qsh);   // synchronises
+    __syncthreads();   // the list and the linear-term parts
     // scores: wave w takes 64-key blocks w, w + 8, ... of the list as two
     // 32-key slots of the query (lane l: list entry 64 b + l); every load of
     // a block is issued before the first is waited for
     LinFrag aq;
     if constexpr (DT == DT_FP8) load_lin_frag<D>(aq, lin_l + (lane & 3) * D, lane >> 4);
-    const int nblk = (nu + 63) / 64;
-    auto key_at = [&](int j) { return (int)(list[min(j, nu - 1)] >> 32); };
+    const int nblk = ((int)nu + 63) / 64;
+    auto key_at = [&](int j) { return (int)(list[min(j, (int)nu - 1)] >> 32); };
     for (int b = wave; b < nblk; b += kFrontThreads / 64) {
         const int j = 64 * b + lane;
-        const unsigned long long own = list[min(j, nu - 1)];
+        const unsigned long long own = list[min(j, (int)nu - 1)];
         HalfRow<DT, D> ka, kb;
         load_key<DT, D>(ka, a.k, key_at(64 * b + (lane & 31)));
         load_key<DT, D>(kb, a.k, key_at(64 * b + 32 + (lane & 31)));
@@ -755,7 +795,7 @@ __global__ __launch_bounds__(kFrontThreads) void front_kernel(IdxArgs a, const i
         } else {
             I = score_2slots<DT, D, HB>(qr, ka, qr, kb);
         }
-        if (j < nu) srow[(uint32_t)own] = I;
+        if (j < (int)nu) srow[(uint32_t)own] = I;
     }
 }
 
@@ -1984,7 +2024,8 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, const F
                 const int zb = (int)std::min<size_t>((front->n_zero + kFrontThreads - 1) / kFrontThreads, 512);
                 allow_lds(front_kernel<DT_, D_, HB_>, lds);
                 front_kernel<DT_, D_, HB_><<<a.T * parts + std::max(zb, 1), kFrontThreads, lds, st>>>(
-                    a, front->sample, front->n, parts, front_log2_slots(a.n_sample), front->zero, front->n_zero);
+                    a, front->sample, front->n, front_log2_parts(a.n_sample), front_log2_slots(a.n_sample),
+                    front->zero, front->n_zero);
                 front_stats_kernel<<<a.T, kFrontThreads, 0, st>>>(a);
             } else {
                 err = hipErrorInvalidValue;

@@ -64,7 +64,7 @@ constexpr int kHashSampleMax = 16384;
 // Calls of at most kFrontMaxT queries whose sample has at most kFrontSampleMax
 // slots run the sample steps (de-duplication, linear-term operands, scores) as
 // one launch of front_parts workgroups per query, each taking the sample keys
-// of one residue class modulo front_parts; score row t of sscore then holds
+// of one class (a hash of the key); score row t of sscore then holds
 // one score per distinct key the query sees, at the slot of one of its
 // entries, and NaN at every other slot.  One more launch turns the rows into
 // statistics.  A workgroup's LDS holds the list of its keys (n_slots 64-bit
@@ -78,7 +78,12 @@ inline bool front_fits(int dtype, int D, int HB) { return !(dtype == 0 && D == 1
 inline bool front_path(int32_t T, int32_t n_slots, int dtype, int D, int H) {
     return T <= kFrontMaxT && n_slots <= kFrontSampleMax && front_fits(dtype, D, (H + 31) / 32);
 }
-inline int front_parts(int32_t n_slots) { return n_slots > 512 ? (n_slots + 511) / 512 : 1; }
+inline int front_log2_parts(int32_t n_slots) {   // about 512 sample entries per workgroup, at most 16
+    int lg = 0;
+    while (lg < 4 && ((int64_t)512 << lg) < n_slots) ++lg;
+    return lg;
+}
+inline int front_parts(int32_t n_slots) { return 1 << front_log2_parts(n_slots); }
 inline int front_log2_slots(int32_t n_slots) {
     int lg = 10;
     while ((1 << lg) <= n_slots) ++lg;
