@@ -33,7 +33,7 @@ namespace ltk {
 constexpr int kRetrQ = 32;                // queries per wave (one MFMA M block)
 constexpr int kRetrQB = 1;                // query blocks per wave
 constexpr int kRetrRows = 32;             // database rows per LDS tile
-constexpr int kRetrRefreshCands = 64;     // candidates a wave adds before it refreshes
+constexpr int kRetrRefreshCands = 128;    // candidates a wave adds before it refreshes
 constexpr int kSuperBins = 16;            // fine bins per super-bin of the shared histogram
 
 constexpr int kRetrStashRegs = 8;         // accumulator registers staged per rare-path round
