@@ -505,8 +505,9 @@ __device__ void sample_meta(const IdxArgs& a, int t, uint32_t c, float mn, float
 }
 
 // Sample statistics of query t: valid sample keys (<= pos), range, delta,
-// histogram and the initial threshold bin.  All 256 threads of the
-// workgroup call it together (it synchronises them); sh holds nbins words.
+// histogram and the initial threshold bin.  All NT threads of the workgroup
+// call it together (it synchronises them); sh holds nbins words.
+template <int NT>
 __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
     const int tid = threadIdx.x;
     const int nu = (int)*a.nu;
@@ -516,7 +517,7 @@ __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
     // and their score range; up to kStatsRegs scores per thread stay in
     // registers (NaN when invalid) for the histogram
     constexpr int kStatsRegs = 16;
-    const bool in_regs = nu <= 256 * kStatsRegs;
+    const bool in_regs = nu <= NT * kStatsRegs;
     float v[kStatsRegs];
     uint32_t c = 0;
     float mn = INFINITY, mx = -INFINITY;
@@ -524,7 +525,7 @@ __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
 #pragma unroll
         for (int i = 0; i < kStatsRegs; ++i) {
             // the score loads do not wait for the key loads (one round trip)
-            const int j = tid + 256 * i;
+            const int j = tid + NT * i;
             const float sj = (j < nu) ? S[j] : NAN;
             const bool ok = j < nu && a.sample_u[j] <= pos_t;
             v[i] = ok ? sj : NAN;
@@ -535,7 +536,7 @@ __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
             }
         }
     } else {
-        for (int j = tid; j < nu; j += 256) {
+        for (int j = tid; j < nu; j += NT) {
             if (a.sample_u[j] <= pos_t) {
                 ++c;
                 mn = fminf(mn, S[j]);
@@ -543,21 +544,29 @@ __device__ void sample_stats_query(const IdxArgs& a, int t, uint32_t* sh) {
             }
         }
     }
-    sample_meta<4>(a, t, c, mn, mx, sh, [&](float smin, float delta) {
+    sample_meta<NT / 64>(a, t, c, mn, mx, sh, [&](float smin, float delta) {
         if (in_regs) {
 #pragma unroll
             for (int i = 0; i < kStatsRegs; ++i)
                 if (!__builtin_isnan(v[i])) atomicAdd(&sh[bin_of(v[i], smin, delta, a.nbins)], 1u);
         } else {
-            for (int j = tid; j < nu; j += 256)
+            for (int j = tid; j < nu; j += NT)
                 if (a.sample_u[j] <= pos_t) atomicAdd(&sh[bin_of(S[j], smin, delta, a.nbins)], 1u);
         }
     });
 }
 
-__global__ __launch_bounds__(256) void sample_stats_kernel(IdxArgs a) {
+// One workgroup per query; 1,024 threads when the sample has more slots than
+// 256 threads hold in registers.
+template <int NT>
+__global__ __launch_bounds__(NT) void sample_stats_kernel(IdxArgs a) {
     extern __shared__ uint32_t sh[];  // [nbins]
-    sample_stats_query(a, blockIdx.x, sh);
+    sample_stats_query<NT>(a, blockIdx.x, sh);
+}
+
+static void launch_stats_kernel(const IdxArgs& a, hipStream_t st) {
+    if (a.n_sample > 256 * 16) sample_stats_kernel<1024><<<a.T, 1024, (size_t)a.nbins * 4, st>>>(a);
+    else sample_stats_kernel<256><<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
 }
 
 template <int DT, int D, int HB>
@@ -2034,7 +2043,7 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, const F
         } else {
             if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
             sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
-            sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
+            launch_stats_kernel(a, st);
         }
         auto run_scan = [&](const IdxArgs& args) { return run_scan_variant<DT_, D_, HB_, false>(args, st); };
         if (!run_scan(a)) { err = hipErrorInvalidValue; return; }
@@ -2065,7 +2074,7 @@ hipError_t launch_unfused_select(const IdxArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_sample_stats(const IdxArgs& a, hipStream_t st) {
-    sample_stats_kernel<<<a.T, 256, (size_t)a.nbins * 4, st>>>(a);
+    launch_stats_kernel(a, st);
     return hipGetLastError();
 }
 
