@@ -110,6 +110,26 @@ def _variants(inp):
     }
 
 
+def test_sample_with_many_distinct_keys(lib):
+    """More distinct sample keys than the statistics hold in registers (16 per
+    thread of 1,024): the statistics loop over the sample, and the result is
+    exact and equal to the unfused path's."""
+    import torch
+    T, L, k = 12, 40000, 300
+    inp = indexer_inputs(T, L, 64, 128, "fp8", k, 600, drift=True, tag=82)
+    d = to_dev(inp)
+    smp = np.concatenate([random_sample(20000, L, tag=83), random_sample(5000, L, tag=84)]).astype(np.int32)
+    say("distinct sample keys", len(np.unique(smp)))
+    idx, sc = lib.score_select(d["q"], d["k"], d["w"], d["pos"], k, sample=torch.from_numpy(smp).cuda(),
+                               q_scale=d["q_scale"], k_scale=d["k_scale"], return_scores=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    check_rows(inp, idx, sc, range(T), "many distinct sample keys")
+    uidx, usc = _run_unfused(lib, d, k)
+    a, asc = canon(idx, sc)
+    b, bsc = canon(uidx, usc)
+    assert np.array_equal(a, b) and np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
 def test_sample_bins_refresh_capacity_independence(lib, dt):
     """The result does not depend on the sample, the bin count, the refresh
