@@ -864,6 +864,16 @@ constexpr int kScanStages = 3;             // 32 KB tiles, one wave per query: o
 constexpr int kScanStagesFew = 4;          // at decode shape (R > 1), where the key stream bounds the scan
 constexpr int kLinPad = 16;                // floats of padding per linear-term row (spreads LDS banks)
 constexpr int kSlotValuPerMfma = 8;        // fp8 prefill slots: head-sum VALU instructions issued behind each MFMA
+constexpr int kLinLead = 2;                // fp8 prefill: the next tile's linear-term rows, this many slots before the tile's end
+
+// Issue priority of the calling wave (s_setprio takes an immediate; in an
+// unrolled loop the level folds to one instruction).
+__device__ __forceinline__ void set_wave_prio(int level) {
+    if (level >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (level == 2) __builtin_amdgcn_s_setprio(2);
+    else if (level == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
 
 template <int DT, int D, int TB = kTileBytes>
 struct TileGeom {
@@ -1198,29 +1208,70 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j)
         if (j < ntiles) load_tile<DT, D, SS::TB, ASYNC>(a, toff, k_lo + j * G::TK, tiles + j * G::STAGE_BYTES, wave, lane);
-    int sbuf = 0;   // stage holding tile `it`
-    for (int it = 0; it < ntiles; ++it) {
-        // tile `it` has landed once at most the loads of the later tiles in
-        // flight remain (vector-memory operations complete in issue order)
-        const int later = min(NST - 2, ntiles - 1 - it);
+    // The wave's own loads of tile i have landed once at most the loads of
+    // the later tiles issued so far remain (vector-memory operations complete
+    // in issue order; the candidate flushes drain their own).
+    auto wait_tile = [&](int i) {
+        const int later = min(NST - 2, ntiles - 1 - i);
         if (wave < G::SCALE_INST) {
             if (NST == 4 && later >= 2) wait_vm<2 * LPW_HI>(); else if (later >= 1) wait_vm<LPW_HI>(); else wait_vm<0>();
         } else {
             if (NST == 4 && later >= 2) wait_vm<2 * LPW_LO>(); else if (later >= 1) wait_vm<LPW_LO>(); else wait_vm<0>();
         }
+    };
+    // fp8 at prefill shape: the slot pipeline runs on across tiles.  A wave
+    // computes the next tile's linear-term rows of its own key blocks during
+    // its last slot of the current tile (they go to the other row buffer,
+    // which nobody reads after the barrier that starts the current tile), and
+    // the gate of a tile's last pair waits for the next tile's first MFMAs.
+    // The per-tile barrier is then the only point where the waves of a SIMD
+    // leave the matrix core idle together.
+    constexpr bool CONT = G::LIN && R == 1 && HalfRow<DT, D>::NV <= 4;   // the fp8 branch of the slot loop below
+    auto lin_rows = [&](int i) { return lbuf + (size_t)(i & 1) * QPG * G::LROW; };
+    float ga = 0.0f, gb = 0.0f, glin = 0.0f, gsk = 0.0f;   // the pair waiting for its gate
+    int gkey = 0;                                          // and its first key
+    bool gpend = false;
+    if constexpr (CONT) {
+        if (ntiles > 0) {
+            wait_tile(0);
+            lin_phase<DT, D, SS::TB, QPG>(tiles, apart, lin_rows(0), wave, lane);
+        }
+    }
+    int sbuf = 0;   // stage holding tile `it`
+    for (int it = 0; it < ntiles; ++it) {
         const uint8_t* st = tiles + sbuf * G::STAGE_BYTES;
-        float* lrow = lbuf + (size_t)(it & 1) * QPG * G::LROW;   // this tile's linear-term rows
-        if constexpr (G::LIN) lin_phase<DT, D, SS::TB, QPG>(st, apart, lrow, wave, lane);
+        float* lrow = lin_rows(it);   // this tile's linear-term rows
+        if constexpr (!CONT) {
+            wait_tile(it);
+            if constexpr (G::LIN) lin_phase<DT, D, SS::TB, QPG>(st, apart, lrow, wave, lane);
+        }
         __syncthreads();
+        const int key0 = k_lo + it * G::TK;
+        const bool act = tv && key0 < wave_end;   // some key of this tile is visible to the wave's query
         if (it + NST - 1 < ntiles) {   // into the stage every wave finished scoring before the barrier
             const int nb = (sbuf + NST - 1) % NST;
             load_tile<DT, D, SS::TB, ASYNC>(a, toff, k_lo + (it + NST - 1) * G::TK, tiles + nb * G::STAGE_BYTES, wave, lane);
         }
-        const int key0 = k_lo + it * G::TK;
         sbuf = (sbuf + 1) % NST;
         const float* sks = reinterpret_cast<const float*>(st + SS::TB);
         const float* lq = lrow + (wave / R) * G::LROW;                  // the wave's query's linear terms
-        if (!tv || key0 >= wave_end) continue;   // nothing of this tile is visible to the wave's query
+        // the next tile's linear-term rows of this wave's own key blocks
+        auto next_lin = [&]() {
+            if (it + 1 < ntiles) {
+                wait_tile(it + 1);
+                lin_phase<DT, D, SS::TB, QPG>(tiles + sbuf * G::STAGE_BYTES, apart, lin_rows(it + 1), wave, lane);
+            }
+        };
+        if (!act) {   // nothing of this tile is visible to the wave's query
+            if constexpr (CONT) {
+                if (gpend) {
+                    process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), gkey);
+                    gpend = false;
+                }
+                next_lin();
+            }
+            continue;
+        }
         if constexpr (DT == DT_F32) {
             // fp32: a whole fragment is 16 registers per 16 dimensions and
             // the query's head blocks as many again per block, so the slots
@@ -1289,13 +1340,14 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         } else if constexpr (DT == DT_FP8 && R == 1) {
             // fp8 at prefill shape: the pipeline below, with each pair's gate
             // deferred into the next slot, just behind that slot's first
-            // MFMA.  The gate's dependent chain (half exchange, linear term,
-            // key scale, compare, ballot, branch) then runs while the matrix
-            // core works, instead of leaving it idle at the end of every
-            // other slot (which a wave running alone, after its SIMD
-            // partner reached the tile's barrier, otherwise exposes).  A
-            // gate one slot later sees a threshold at most one refresh
-            // staler: still safe.
+            // MFMA (for a tile's last pair: the next tile's).  The gate's
+            // dependent chain (half exchange, linear term, key scale,
+            // compare, ballot, branch) then runs while the matrix core
+            // works, instead of leaving it idle at the end of every other
+            // slot (which a wave running alone, after its SIMD partner
+            // reached the tile's barrier, otherwise exposes).  A gate one
+            // slot later sees a threshold at most one refresh staler: still
+            // safe.
             constexpr int NS = G::TK / 32;
             constexpr int KS = HalfRow<DT, D>::KSTEPS;
             constexpr int VPM = kSlotValuPerMfma;
@@ -1306,11 +1358,17 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
             mfma_1slot<DT, D, HB>(ra.q, kf[0], accC);
             if (NS > 1) read_frag<DT, D>(kf[1], st, row0(1), lane);
             float pprev = 0.0f;
-            float ga = 0.0f, gb = 0.0f, glin = 0.0f, gsk = 0.0f;   // the pair waiting for its gate
-            int gr0 = 0;
-            bool gpend = false;
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl) {
+                // A wave's priority falls as it works through the tile, so
+                // that of the two waves sharing a SIMD the one behind issues
+                // first.  Left to the oldest-first arbitration, one wave ran
+                // ahead and then waited at the barrier for a quarter of the
+                // tile while its partner finished alone.
+                if (sl == 0) set_wave_prio(3);
+                else if (sl == NS / 2) set_wave_prio(2);
+                else if (sl == 3 * NS / 4) set_wave_prio(1);
+                else if (sl == NS - 1) set_wave_prio(0);
                 const HalfRow<DT, D>& kn = kf[(sl + 1) & 1];
                 if (sl + 1 < NS) {
                     accN[0] = v16f{};
@@ -1322,11 +1380,15 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                     // empty asm that the chain's inputs pass through
                     __builtin_amdgcn_sched_barrier(0);
                     asm volatile("" : "+v"(ga), "+v"(gb), "+v"(glin), "+v"(gsk));
-                    process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), key0 + gr0);
+                    process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), gkey);
                     gpend = false;
                 }
+                // the last slots' MFMAs are in flight: the next tile's
+                // linear-term rows now, the head sums behind them
+                if (sl == NS - kLinLead) next_lin();
                 if (sl & 1) {   // this pair's linear terms and key scales, read early
-                    gr0 = row0(sl - 1);
+                    const int gr0 = row0(sl - 1);
+                    gkey = key0 + gr0;
                     glin = lq[gr0 + lane];
                     gsk = sks[gr0 + lane];
                 }
@@ -1369,7 +1431,6 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);   // each slot its own scheduling region
             }
-            if (gpend) process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), key0 + gr0);
         } else {
             // 32-key slots, software-pipelined: the MFMAs of slot s+1 are issued
             // before the head sum of slot s, so the matrix core and the VALU of
@@ -1432,6 +1493,9 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
                 if constexpr (DT == DT_FP8 && R == 1) __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
+    if constexpr (CONT) {   // the last tile's last pair
+        if (gpend) process(lin_score(glin, inv_own, combine_halves(ga, gb), gsk), gkey);
     }
     // final partial batch
     if (cnt > 0) {
