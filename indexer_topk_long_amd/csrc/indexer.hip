@@ -866,15 +866,6 @@ constexpr int kLinPad = 16;                // floats of padding per linear-term 
 constexpr int kSlotValuPerMfma = 8;        // fp8 prefill slots: head-sum VALU instructions issued behind each MFMA
 constexpr int kLinLead = 2;                // fp8 prefill: the next tile's linear-term rows, this many slots before the tile's end
 
-// Issue priority of the calling wave (s_setprio takes an immediate; in an
-// unrolled loop the level folds to one instruction).
-__device__ __forceinline__ void set_wave_prio(int level) {
-    if (level >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (level == 2) __builtin_amdgcn_s_setprio(2);
-    else if (level == 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-}
-
 template <int DT, int D, int TB = kTileBytes>
 struct TileGeom {
     static constexpr int RB = D * DTraits<DT>::ESZ;        // bytes per key row

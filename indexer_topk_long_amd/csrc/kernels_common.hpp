@@ -45,6 +45,17 @@ __device__ __forceinline__ void wait_vm_plus(int extra) {
 // every iteration, waits that then also stall on the tile loads in flight.
 __device__ __forceinline__ void drain_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Issue priority of the calling wave (s_setprio takes an immediate; with a
+// constant level, as in an unrolled loop, this folds to one instruction).
+// The scans lower a wave's priority as it works through a tile, so that of
+// the two waves sharing a SIMD the one behind issues first.
+__device__ __forceinline__ void set_wave_prio(int level) {
+    if (level >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (level == 2) __builtin_amdgcn_s_setprio(2);
+    else if (level == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // XOR swizzle of the 16-byte chunks of a row.  LDS has 64 four-byte banks (a
 // 256-byte bank line).  The MFMA fragment read of the scans is the half-row
 // read: lane l takes row (l & 31), and the two 32-lane halves take different

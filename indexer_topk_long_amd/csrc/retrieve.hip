@@ -297,9 +297,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         v16f acc[kRetrQB];
 #pragma unroll
         for (int b = 0; b < kRetrQB; ++b) acc[b] = v16f{};
+        // issue priority falls through the tile (3, 2 over the MFMAs, 1 for the
+        // gate and the candidates, 0 in a refresh): of the two waves of a
+        // SIMD the one behind issues first
 #pragma unroll
         for (int s = 0; s < G::KSTEPS; ++s) {
             constexpr int LSTEP = G::KSTEPS / G::LPW;   // MFMA steps between this wave's tile loads
+            if (s == 0) set_wave_prio(3);
+            else if (s == G::KSTEPS / 2) set_wave_prio(2);
             if (s % LSTEP == 0 && s / LSTEP < G::LPW)
             {
                 int ln;
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (s + PF < G::KSTEPS) bq[s % PF] = rd(s + PF);
             if (s % PF == PF - 1) __builtin_amdgcn_sched_barrier(0);
         }
+        set_wave_prio(1);
         if constexpr (FULL) {
 #pragma unroll
             for (int R = 0; R < NR; ++R) {
@@ -380,6 +386,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (qn >= 64 || (qn > 0 && added >= kRetrRefreshCands)) flush();
         if (added >= kRetrRefreshCands) {
             added = 0;
+            set_wave_prio(0);
             int nt = thr_own;
             if (own_valid) {
                 const uint32_t kk = (uint32_t)a.topk;
