@@ -1211,12 +1211,11 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
         }
     };
     // fp8 at prefill shape: the slot pipeline runs on across tiles.  A wave
-    // computes the next tile's linear-term rows of its own key blocks during
-    // its last slot of the current tile (they go to the other row buffer,
-    // which nobody reads after the barrier that starts the current tile), and
-    // the gate of a tile's last pair waits for the next tile's first MFMAs.
-    // The per-tile barrier is then the only point where the waves of a SIMD
-    // leave the matrix core idle together.
+    // computes the next tile's linear-term rows of its own key blocks
+    // kLinLead slots before the end of the current tile, behind MFMAs in
+    // flight (they go to the other row buffer, which nobody reads after the
+    // barrier that starts the current tile), and the gate of a tile's last
+    // pair waits for the next tile's first MFMAs.
     constexpr bool CONT = G::LIN && R == 1 && HalfRow<DT, D>::NV <= 4;   // the fp8 branch of the slot loop below
     auto lin_rows = [&](int i) { return lbuf + (size_t)(i & 1) * QPG * G::LROW; };
     float ga = 0.0f, gb = 0.0f, glin = 0.0f, gsk = 0.0f;   // the pair waiting for its gate
