@@ -1311,6 +1311,12 @@ __global__ __launch_bounds__(512) void scan_kernel(IdxArgs a) {
             float pprev = 0.0f;
 #pragma unroll
             for (int sl = 0; sl < NS; ++sl) {
+                if constexpr (R == 1) {   // priority falling through the tile, as in the fp8 loop
+                    if (sl == 0) set_wave_prio(3);
+                    else if (sl == NS / 2) set_wave_prio(2);
+                    else if (sl == 3 * NS / 4) set_wave_prio(1);
+                    else if (sl == NS - 1) set_wave_prio(0);
+                }
                 if (sl + 1 < NS) {
                     read_frag<DT, D>(kf, st, row0(sl + 1), lane);
                     mfma_1slot<DT, D, HB>(ra.q, kf, accN);
