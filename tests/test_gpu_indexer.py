@@ -145,7 +145,9 @@ def test_sample_bins_refresh_capacity_independence(lib, dt):
     cases = []
     for name, smp in _variants(inp).items():
         cases.append((name, torch.from_numpy(smp).cuda(), None))
-    for nb in (1, 2, 7, 1024):
+    # 800 bins: the wide tiles no longer fit the LDS, three 32 KB stages do
+    # (1,024 bins: two); each bin count below takes its own scan variant
+    for nb in (1, 2, 7, 800, 1024):
         cases.append((f"nbins{nb}", d["sample"], ltk.Opts(nbins=nb)))
     for r in (3, -1):
         cases.append((f"refresh{r}", d["sample"], ltk.Opts(refresh_every=r)))
