@@ -38,12 +38,12 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
 DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
-SCAN_TRAFFIC = {"digest": "d336789c88258447", "workload": "prefill-1m-fp8",
-                "bytes": 2228850 * 1024 * 2.0 + 152866 * 1024 * 1.0}
+SCAN_TRAFFIC = {"digest": "614a10a459a71e55", "workload": "prefill-1m-fp8",
+                "bytes": 2228848 * 1024 * 2.0 + 151736 * 1024 * 1.0}
 RETR_TRAFFIC = {"digest": "e5237b561c434b2c", "workload": "retrieval-8m-d768-bf16",
                 "bytes": 8806249 * 1024 * 2.0 + 1730021 * 1024 * 1.0}
-DECODE_TRAFFIC = {"digest": "d336789c88258447", "workload": "decode-1m-fp8",
-                  "bytes": 67674 * 1024 * 2.0 + 46 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "614a10a459a71e55", "workload": "decode-1m-fp8",
+                  "bytes": 67675 * 1024 * 2.0 + 47 * 1024 * 1.0}
 DSA_TRAFFIC = {"digest": "28551f069d2e071c", "workload": "dsa-1m-fp8",
                "pack_bytes": 33067 * 1024 * 2.0 + 134093 * 1024 * 1.0,
                "gather_bytes": 744583 * 1024 * 2.0 + 2708540 * 1024 * 1.0}

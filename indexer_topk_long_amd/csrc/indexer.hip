@@ -891,8 +891,8 @@ struct TileGeom {
 
 // Tile size of a scan with R waves per query.  At one wave per query
 // (prefill shape) the MFMA/VALU work bounds the scan, and each tile ends in a
-// workgroup barrier that drains the wave's software pipeline, so the tiles
-// are as large as two stages allow (64 KB, measured 1.5 % faster than 32 KB
+// workgroup barrier at which every wave stops issuing, so the tiles are as
+// large as two stages allow (64 KB, measured 1.5 % faster than 32 KB
 // tiles with three stages; 48 KB for fp8, whose linear-term rows take LDS
 // too).  WIDE needs rows of at least 128 bytes (at most 512 keys, whose
 // scales take one wave load each) and LDS for two such stages, which the
