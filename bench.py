@@ -38,15 +38,15 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "indexer.hip"]
 RETR_SOURCES = ["device.hpp", "kernels_common.hpp", "internal.hpp", "retrieve.hip"]
 DSA_SOURCES = ["device.hpp", "internal.hpp", "dsa.hip"]
-SCAN_TRAFFIC = {"digest": "614a10a459a71e55", "workload": "prefill-1m-fp8",
-                "bytes": 2228848 * 1024 * 2.0 + 151736 * 1024 * 1.0}
-RETR_TRAFFIC = {"digest": "e5237b561c434b2c", "workload": "retrieval-8m-d768-bf16",
-                "bytes": 8806249 * 1024 * 2.0 + 1730021 * 1024 * 1.0}
-DECODE_TRAFFIC = {"digest": "614a10a459a71e55", "workload": "decode-1m-fp8",
-                  "bytes": 67675 * 1024 * 2.0 + 47 * 1024 * 1.0}
-DSA_TRAFFIC = {"digest": "28551f069d2e071c", "workload": "dsa-1m-fp8",
-               "pack_bytes": 33067 * 1024 * 2.0 + 134093 * 1024 * 1.0,
-               "gather_bytes": 744583 * 1024 * 2.0 + 2708540 * 1024 * 1.0}
+SCAN_TRAFFIC = {"digest": "a2b5049f774f6b45", "workload": "prefill-1m-fp8",
+                "bytes": 2228843 * 1024 * 2.0 + 152471 * 1024 * 1.0}
+RETR_TRAFFIC = {"digest": "ddb385e3e0aa1fa1", "workload": "retrieval-8m-d768-bf16",
+                "bytes": 8615774 * 1024 * 2.0 + 1730362 * 1024 * 1.0}
+DECODE_TRAFFIC = {"digest": "a2b5049f774f6b45", "workload": "decode-1m-fp8",
+                  "bytes": 67674 * 1024 * 2.0 + 46 * 1024 * 1.0}
+DSA_TRAFFIC = {"digest": "712d6bd147e58a78", "workload": "dsa-1m-fp8",
+               "pack_bytes": 33067 * 1024 * 2.0 + 134174 * 1024 * 1.0,
+               "gather_bytes": 744743 * 1024 * 2.0 + 2708540 * 1024 * 1.0}
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA

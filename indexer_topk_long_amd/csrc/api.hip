@@ -224,7 +224,8 @@ size_t litetopk_workspace_bytes(int32_t kind, int32_t T, int32_t H, int32_t D, i
     (void)H;
     const IdxPlan p = indexer_plan(T, L, dtype, o);
     const int32_t n_slots = sample_slots(n_sample, topk, L);
-    return ws_layout(T, L, n_slots, p.ccap, p.shared ? (size_t)T * o.nbins : 0, dtype == LTK_FP8_E4M3FN ? D : 0).total;
+    const size_t grb = sample_by_scan(T, n_slots) && !front_path(T, n_slots, dtype, D, H) ? (size_t)D * dtype_bytes(dtype) : 0;
+    return ws_layout(T, L, n_slots, p.ccap, p.shared ? (size_t)T * o.nbins : 0, dtype == LTK_FP8_E4M3FN ? D : 0, grb).total;
 }
 
 int litetopk_score_select(const void* q, const float* q_scale, const void* k, const float* k_scale, const float* w,
@@ -246,7 +247,8 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     const int32_t n_slots = sample_slots(n_sample, topk, L);
     // few queries and a small sample: the sample steps take one launch
     const bool front = front_path(T, n_slots, dtype, D, H);
-    const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0, fp8 ? D : 0);
+    const size_t grb = sample_by_scan(T, n_slots) && !front_path(T, n_slots, dtype, D, H) ? (size_t)D * dtype_bytes(dtype) : 0;
+    const WsLayout lay = ws_layout(T, L, n_slots, plan.ccap, plan.shared ? (size_t)T * o.nbins : 0, fp8 ? D : 0, grb);
     if (ws_bytes < lay.total) return LTK_EWORKSPACE;
     if (T == 0) return LTK_OK;
     if ((st = device_check()) != LTK_OK) return st;
@@ -285,6 +287,9 @@ int litetopk_score_select(const void* q, const float* q_scale, const void* k, co
     a.sample_u = reinterpret_cast<int32_t*>(wsb + lay.sample_u);
     a.sscore = reinterpret_cast<float*>(wsb + lay.sscore);
     a.front_parts = front ? front_parts(n_slots) : 0;
+    a.sg_k = grb ? wsb + lay.sgk : nullptr;
+    a.sg_scale = grb ? reinterpret_cast<float*>(wsb + lay.sgs) : nullptr;
+    a.sg_pos = grb ? reinterpret_cast<int32_t*>(wsb + lay.sgp) : nullptr;
     a.cand = reinterpret_cast<uint2*>(wsb + lay.cand);
     a.thr_fin = reinterpret_cast<int*>(wsb + lay.thrf);
     a.ovf_list = reinterpret_cast<int*>(wsb + lay.ovfl);

@@ -627,6 +627,29 @@ __device__ __forceinline__ void sample_score_part(const IdxArgs& a, int qg, int 
     }
 }
 
+// Sample pass at prefill shape: the de-duplicated sample keys' rows (and
+// fp8 scales) copied into one contiguous array, row j from sample_u[j] (rows
+// past the nu distinct keys repeat the last; their scores are never read),
+// and a causal bound past every row for each query.  The scan's full-score
+// form then scores every query against the array into the sample-score rows
+// (launch_indexer_fused), with the scan's own arithmetic and tiles.
+__global__ __launch_bounds__(256) void sample_gather_kernel(IdxArgs a, int rb) {
+    const int nu = (int)*a.nu;
+    const int chunks = rb / 16;
+    const size_t total = (size_t)a.n_sample * chunks;
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t u = (size_t)blockIdx.x * 256 + threadIdx.x; u < total; u += stride) {
+        const int j = (int)(u / chunks), c = (int)(u % chunks);
+        const int key = nu > 0 ? a.sample_u[min(j, nu - 1)] : 0;
+        reinterpret_cast<u32x4*>(a.sg_k + (size_t)j * rb)[c] = reinterpret_cast<const u32x4*>(a.k + (size_t)key * rb)[c];
+    }
+    for (size_t j = (size_t)blockIdx.x * 256 + threadIdx.x; j < (size_t)a.n_sample; j += stride) {
+        const int key = nu > 0 ? a.sample_u[min((int)j, nu - 1)] : 0;
+        if (a.k_scale) a.sg_scale[j] = a.k_scale[key];
+    }
+    for (size_t t = (size_t)blockIdx.x * 256 + threadIdx.x; t < (size_t)a.T; t += stride) a.sg_pos[t] = a.n_sample - 1;
+}
+
 // Sample scores of a query group's queries, split over s_splits workgroups.
 template <int DT, int D, int HB>
 __global__ __launch_bounds__(256) void sample_score_kernel(IdxArgs a) {
@@ -2102,7 +2125,25 @@ hipError_t launch_indexer_fused(int dt, int D, int HB, const IdxArgs& a, const F
             }
         } else {
             if constexpr (DT_ == DT_FP8) qlin_kernel<D_><<<a.T, 256, 0, st>>>(a);
-            sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
+            if (a.sg_k != nullptr) {
+                // prefill shape: the sample's rows gathered, then scored by
+                // the scan's full-score form into the sample-score rows
+                constexpr int RB = D_ * DTraits<DT_>::ESZ;
+                sample_gather_kernel<<<256, 256, 0, st>>>(a, RB);
+                IdxArgs b = a;
+                b.k = a.sg_k;
+                b.k_scale = (DT_ == DT_FP8) ? a.sg_scale : nullptr;
+                b.L = a.n_sample;
+                b.pos = a.sg_pos;
+                b.S = a.sscore;          // row stride b.L = n_sample: the sample-score rows
+                b.n_splits = 1;
+                b.pass = 0;
+                b.hist_g = nullptr;
+                b.ev_scan_start = b.ev_scan_stop = nullptr;
+                if (!run_scan_variant<DT_, D_, HB_, true>(b, st)) { err = hipErrorInvalidValue; return; }
+            } else {
+                sample_score_kernel<DT_, D_, HB_><<<nqg * a.s_splits, 256, 0, st>>>(a);
+            }
             launch_stats_kernel(a, st);
         }
         auto run_scan = [&](const IdxArgs& args) { return run_scan_variant<DT_, D_, HB_, false>(args, st); };

@@ -49,7 +49,7 @@ inline int sample_chunks(int64_t L) {
 // by the first kernel of every call.
 struct WsLayout {
     size_t tail, flags, thrf, ovfc, hist, bitmap, ccount, zero_begin, zero_end;
-    size_t nu, meta, sample_u, sscore, qlin, qinv, ovfl, cand, total;
+    size_t nu, meta, sample_u, sscore, qlin, qinv, ovfl, sgk, sgs, sgp, cand, total;
 };
 
 // Per-query linear-term operands of the fp8 score (four fp8 parts of D bytes
@@ -71,6 +71,12 @@ constexpr int kHashSampleMax = 16384;
 // entries) and a hash table of 2^front_log2_slots keys (more than the sample,
 // as one class may hold every key).
 constexpr int kFrontMaxT = 8;
+// Calls of at least this many queries (prefill chunks) score their sample
+// with the scan itself: the distinct sample keys' rows are copied into a
+// contiguous array, which the scan's full-score form then covers.
+constexpr int kSampleScanMinT = 2048;
+inline bool sample_by_scan(int32_t T, int32_t n_slots) { return T >= kSampleScanMinT && n_slots > 0; }
+inline size_t dtype_bytes(int dtype) { return dtype == 0 ? 4 : dtype == 1 ? 2 : 1; }   // fp32, bf16, fp8
 constexpr int kFrontSampleMax = 6144;
 // (fp32 queries of 128 dimensions in two head blocks leave that kernel too
 // few registers: those calls keep the separate launches)
@@ -108,7 +114,7 @@ inline int32_t sample_slots(int32_t n_sample, int32_t topk, int64_t L) {
 // (retrieval: T x (nbins + super-bins) + T x splits; indexer: T x nbins when
 // its splits share thresholds, else 0).
 inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, size_t hist_words = 0,
-                          int lin_d = 0) {
+                          int lin_d = 0, size_t gather_row_bytes = 0) {
     WsLayout w{};
     size_t o = 0;
     // cleared by the sample preparation of every call
@@ -131,6 +137,12 @@ inline WsLayout ws_layout(int32_t T, int64_t L, int32_t n_sample, int64_t ccap, 
     w.qlin = o;     o = align_up(o + qlin_bytes(T, lin_d), 256);
     w.qinv = o;     o = align_up(o + (lin_d ? (size_t)T * 4 : 0), 256);
     w.ovfl = o;     o = align_up(o + (size_t)T * 4, 256);
+    // the sample pass at prefill shape: the sample's key rows, their scales
+    // and one causal bound per query, for the scan (gather_row_bytes = 0: none)
+    const size_t ng = gather_row_bytes ? (size_t)(n_sample > 0 ? n_sample : 1) : 0;
+    w.sgk = o;      o = align_up(o + ng * gather_row_bytes, 256);
+    w.sgs = o;      o = align_up(o + ng * 4, 256);
+    w.sgp = o;      o = align_up(o + (gather_row_bytes ? (size_t)T * 4 : 0), 256);
     w.cand = o;     o = align_up(o + (size_t)T * (size_t)ccap * 8, 256);
     w.total = o;
     return w;
@@ -171,6 +183,9 @@ struct IdxArgs {
     uint32_t* ovf_count;     // number of them
     uint8_t* qlin;           // fp8: [T][4][D] parts of each query's q''/2 (linear term), else null
     float* qinv;             // fp8: [T] 1/S of those parts
+    uint8_t* sg_k;           // sample pass by the scan: [n_sample][D] the sample's key rows, else null
+    float* sg_scale;         // and their scales (fp8)
+    int32_t* sg_pos;         // [T] n_sample - 1 (every row visible to every query)
     // outputs
     int32_t* out_idx;
     float* out_score;

@@ -131,6 +131,30 @@ def test_sample_with_many_distinct_keys(lib):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_sample_scored_by_the_scan(lib, dt):
+    """Calls of 2,048 queries or more score their sample with the scan's
+    full-score form over the gathered sample rows.  Samples whose distinct
+    count is not a multiple of the tile, with duplicates and invalid entries,
+    none, and 16,384 entries: exact on sampled rows, and every row equal to
+    the unfused path's, scores bit for bit."""
+    import torch
+    T, L, k = 2048, 6000, 200
+    inp = indexer_inputs(T, L, 64, 128, dt, k, 400, drift=True, tag=86, n_sample=3 * k)
+    d = to_dev(inp)
+    uidx, usc = canon(*_run_unfused(lib, d, k))
+    rows = list(range(0, T, 128)) + [T - 2, T - 1]
+    for name, smp in _variants(inp).items():
+        if name not in ("random", "empty", "dups_invalid", "hash_table_full"):
+            continue
+        say("sample", name, len(smp))
+        idx, sc = _run_fused(lib, d, k, sample=torch.from_numpy(np.asarray(smp, np.int32)).cuda())
+        check_rows(inp, idx, sc, rows, f"{dt} sample {name}")
+        a, asc = canon(idx, sc)
+        assert np.array_equal(a, uidx), name
+        assert np.array_equal(asc.view(np.uint32), usc.view(np.uint32)), name
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
 def test_sample_bins_refresh_capacity_independence(lib, dt):
     """The result does not depend on the sample, the bin count, the refresh
     period, the key split or the buffer capacity (forced overflow included):
