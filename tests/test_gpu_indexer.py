@@ -130,25 +130,28 @@ def test_sample_with_many_distinct_keys(lib):
     assert np.array_equal(a, b) and np.array_equal(asc.view(np.uint32), bsc.view(np.uint32))
 
 
-@pytest.mark.parametrize("dt", ["bf16", "fp8"])
-def test_sample_scored_by_the_scan(lib, dt):
+@pytest.mark.parametrize("dt,H,D", [("bf16", 64, 128), ("fp8", 64, 128), ("fp8", 20, 64), ("f32", 20, 64)])
+def test_sample_scored_by_the_scan(lib, dt, H, D):
     """Calls of 2,048 queries or more score their sample with the scan's
     full-score form over the gathered sample rows.  Samples whose distinct
     count is not a multiple of the tile, with duplicates and invalid entries,
-    none, and 16,384 entries: exact on sampled rows, and every row equal to
-    the unfused path's, scores bit for bit."""
+    none, and 16,384 entries, and bin counts that select the scan's other
+    tile variants: exact on sampled rows, and every row equal to the unfused
+    path's, scores bit for bit."""
     import torch
+    import indexer_topk_long_amd as ltk
     T, L, k = 2048, 6000, 200
-    inp = indexer_inputs(T, L, 64, 128, dt, k, 400, drift=True, tag=86, n_sample=3 * k)
+    inp = indexer_inputs(T, L, H, D, dt, k, 400, drift=True, tag=86, n_sample=3 * k)
     d = to_dev(inp)
     uidx, usc = canon(*_run_unfused(lib, d, k))
     rows = list(range(0, T, 128)) + [T - 2, T - 1]
-    for name, smp in _variants(inp).items():
-        if name not in ("random", "empty", "dups_invalid", "hash_table_full"):
-            continue
+    cases = [(name, smp, None) for name, smp in _variants(inp).items()
+             if name in ("random", "empty", "dups_invalid", "hash_table_full")]
+    cases += [(f"random_nbins{nb}", _variants(inp)["random"], ltk.Opts(nbins=nb)) for nb in (800, 1024)]
+    for name, smp, o in cases:
         say("sample", name, len(smp))
-        idx, sc = _run_fused(lib, d, k, sample=torch.from_numpy(np.asarray(smp, np.int32)).cuda())
-        check_rows(inp, idx, sc, rows, f"{dt} sample {name}")
+        idx, sc = _run_fused(lib, d, k, opts=o, sample=torch.from_numpy(np.asarray(smp, np.int32)).cuda())
+        check_rows(inp, idx, sc, rows, f"{dt} H{H} D{D} sample {name}")
         a, asc = canon(idx, sc)
         assert np.array_equal(a, uidx), name
         assert np.array_equal(asc.view(np.uint32), usc.view(np.uint32)), name
